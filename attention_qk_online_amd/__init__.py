@@ -1,0 +1,276 @@
+"""Fused attention forward for AMD MI355X (gfx950): Python binding of libattn.so.
+
+Every function here only checks arguments, allocates outputs with torch and
+passes raw device pointers plus the current HIP stream to the C ABI declared
+in ``include/attn.h``; all arithmetic runs in the library's HIP kernels.  If
+the library has not been built the import still succeeds, but every call
+raises ``RuntimeError`` -- there is no fallback path.
+
+Entry points (names follow the C ABI):
+
+* :func:`decode_paged` -- batched decode over a paged KV cache (split-KV +
+  log-sum-exp merge), the analogue of FlashInfer's single/batch decode calls
+  described in "FlashInfer内核库深度解析".
+* :func:`prefill_varlen` -- ragged (causal) prefill addressed by cu_seqlens,
+  with the argument list of ``varlen_fwd`` in "FlashAttention-3 内核在最新大模型
+  推理中的集成实践" section 二.
+* :func:`prefill_paged` -- chunked prefill over a paged KV cache (same page).
+
+The softmax scale defaults to 1/sqrt(head_dim) (same page, section 二).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["decode_paged", "decode_paged_workspace_size", "prefill_varlen", "prefill_paged",
+           "timing_begin", "timing_end", "library_path", "load_library", "AttnError",
+           "KERNEL_KINDS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libattn.so")
+_lib = None
+
+ATTN_F32, ATTN_BF16 = 0, 1
+KERNEL_KINDS = ("decode_split", "decode_combine", "prefill", "prefill_paged")
+_STATUS = {0: "ok", 1: "null", 2: "shape", 3: "dtype", 4: "unsupported", 5: "value",
+           6: "workspace", 7: "hip"}
+
+
+class AttnError(RuntimeError):
+    """A call into libattn.so returned a non-zero status."""
+
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"libattn: {_STATUS.get(status, status)} error: {detail}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libattn.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m attention_qk_online_amd.build` "
+                           "(hipcc, gfx950); there is no fallback implementation")
+    lib = ctypes.CDLL(p)
+    c_int, c_float, c_size, vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+    lib.attn_decode_paged_workspace_size.restype = c_size
+    lib.attn_decode_paged_workspace_size.argtypes = [c_int] * 7
+    lib.attn_decode_paged.restype = c_int
+    lib.attn_decode_paged.argtypes = [c_int, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int,
+                                      c_int, c_int, c_int, c_int, c_float, vp, vp, vp, c_size, vp]
+    lib.attn_prefill_varlen.restype = c_int
+    lib.attn_prefill_varlen.argtypes = [c_int, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int,
+                                        c_int, c_int, c_int, c_int, c_float, vp, vp, vp]
+    lib.attn_prefill_paged.restype = c_int
+    lib.attn_prefill_paged.argtypes = [c_int, vp, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int,
+                                       c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_float,
+                                       vp, vp, vp]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [c_int]
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_timing_begin.restype = c_int
+    lib.attn_timing_begin.argtypes = [c_int]
+    lib.attn_timing_end.restype = c_int
+    lib.attn_timing_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int)]
+    lib.attn_kernel_name.restype = ctypes.c_char_p
+    lib.attn_kernel_name.argtypes = [c_int]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        raise AttnError(status, lib.attn_last_error().decode() or
+                        lib.attn_status_string(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, dim=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (no silent copies are made)")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got shape {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _scale(scale: Optional[float], D: int) -> float:
+    s = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if not math.isfinite(s):
+        raise ValueError("scale must be finite")
+    return s
+
+
+def decode_paged_workspace_size(B: int, Hq: int, Hkv: int, D: int, page_size: int,
+                                max_kv_len: int, split_pages: int = 0) -> int:
+    return int(load_library().attn_decode_paged_workspace_size(B, Hq, Hkv, D, page_size,
+                                                               max_kv_len, split_pages))
+
+
+def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                 page_table: torch.Tensor, kv_lens: torch.Tensor, scale: Optional[float] = None,
+                 max_kv_len: Optional[int] = None, split_pages: int = 0,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Batched decode over a paged KV cache.
+
+    q [B, Hq, D]; k_pages, v_pages [num_pages, page_size, Hkv, D] (NHD);
+    page_table [B, max_pages] int32; kv_lens [B] int32.  ``max_kv_len`` is a
+    host bound on every kv_len; when omitted it is read from ``kv_lens`` with
+    one device-to-host copy.  Returns (out [B, Hq, D], lse [B, Hq] float32).
+    """
+    lib = load_library()
+    dt = _dtype_code(q)
+    pq = _dev(q, "q", dim=3)
+    pk = _dev(k_pages, "k_pages", q.dtype, 4)
+    pv = _dev(v_pages, "v_pages", q.dtype, 4)
+    pt = _dev(page_table, "page_table", torch.int32, 2)
+    pl = _dev(kv_lens, "kv_lens", torch.int32, 1)
+    B, Hq, D = q.shape
+    num_pages, page_size, Hkv, Dk = k_pages.shape
+    if tuple(v_pages.shape) != tuple(k_pages.shape) or Dk != D:
+        raise ValueError(f"k_pages {tuple(k_pages.shape)} / v_pages {tuple(v_pages.shape)} do not "
+                         f"match q {tuple(q.shape)}")
+    if page_table.shape[0] != B or kv_lens.shape[0] != B:
+        raise ValueError("page_table and kv_lens need one row per request")
+    if max_kv_len is None:
+        max_kv_len = int(kv_lens.max().item()) if B > 0 else 0
+    s = _scale(scale, D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _dev(out, "out", q.dtype, 3)
+    _dev(lse, "lse", torch.float32, 2)
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq):
+        raise ValueError("out/lse have the wrong shape")
+    ws_bytes = int(lib.attn_decode_paged_workspace_size(B, Hq, Hkv, D, page_size, max_kv_len,
+                                                        split_pages))
+    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    pw = _dev(workspace, "workspace")
+    _check(lib.attn_decode_paged(dt, pq, pk, pv, pt, pl, B, Hq, Hkv, D, page_size, num_pages,
+                                 page_table.shape[1], max_kv_len, split_pages, s, out.data_ptr(),
+                                 lse.data_ptr(), pw, workspace.numel() * workspace.element_size(),
+                                 _stream(q.device)))
+    return out, lse
+
+
+def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                   cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                   causal: bool = True, scale: Optional[float] = None,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None
+                   ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Ragged prefill: q [Tq, Hq, D], k/v [Tk, Hkv, D] packed by cu_seqlens [B+1].
+
+    Returns (out [Tq, Hq, D], lse [Tq, Hq] float32).
+    """
+    lib = load_library()
+    dt = _dtype_code(q)
+    pq = _dev(q, "q", dim=3)
+    pk = _dev(k, "k", q.dtype, 3)
+    pv = _dev(v, "v", q.dtype, 3)
+    pcq = _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    pck = _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    Tq, Hq, D = q.shape
+    Tk, Hkv, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Dk != D:
+        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} do not match q {tuple(q.shape)}")
+    B = cu_seqlens_q.shape[0] - 1
+    if B < 0 or cu_seqlens_k.shape[0] != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have B+1 entries")
+    s = _scale(scale, D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Tq, Hq), dtype=torch.float32, device=q.device)
+    _dev(out, "out", q.dtype, 3)
+    _dev(lse, "lse", torch.float32, 2)
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (Tq, Hq):
+        raise ValueError("out/lse have the wrong shape")
+    _check(lib.attn_prefill_varlen(dt, pq, pk, pv, pcq, pck, B, Hq, Hkv, D, Tq, Tk,
+                                   int(max_seqlen_q), int(max_seqlen_k), int(bool(causal)), s,
+                                   out.data_ptr(), lse.data_ptr(), _stream(q.device)))
+    return out, lse
+
+
+def prefill_paged(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_pages: torch.Tensor,
+                  v_pages: torch.Tensor, page_table: torch.Tensor, kv_lens: torch.Tensor,
+                  max_seqlen_q: int, max_kv_len: int, causal: bool = True,
+                  scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunked prefill over a paged KV cache: request b's queries are the last
+    Lq_b of its kv_lens[b] cached tokens.  Returns (out, lse)."""
+    lib = load_library()
+    dt = _dtype_code(q)
+    pq = _dev(q, "q", dim=3)
+    pcq = _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    pk = _dev(k_pages, "k_pages", q.dtype, 4)
+    pv = _dev(v_pages, "v_pages", q.dtype, 4)
+    pt = _dev(page_table, "page_table", torch.int32, 2)
+    pl = _dev(kv_lens, "kv_lens", torch.int32, 1)
+    Tq, Hq, D = q.shape
+    num_pages, page_size, Hkv, Dk = k_pages.shape
+    if tuple(v_pages.shape) != tuple(k_pages.shape) or Dk != D:
+        raise ValueError("k_pages / v_pages do not match q")
+    B = cu_seqlens_q.shape[0] - 1
+    if page_table.shape[0] != B or kv_lens.shape[0] != B:
+        raise ValueError("page_table and kv_lens need one row per request")
+    s = _scale(scale, D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Tq, Hq), dtype=torch.float32, device=q.device)
+    _dev(out, "out", q.dtype, 3)
+    _dev(lse, "lse", torch.float32, 2)
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (Tq, Hq):
+        raise ValueError("out/lse have the wrong shape")
+    _check(lib.attn_prefill_paged(dt, pq, pcq, pk, pv, pt, pl, B, Hq, Hkv, D, Tq, page_size,
+                                  num_pages, page_table.shape[1], int(max_seqlen_q),
+                                  int(max_kv_len), int(bool(causal)), s, out.data_ptr(),
+                                  lse.data_ptr(), _stream(q.device)))
+    return out, lse
+
+
+def timing_begin(capacity: int = 4096) -> None:
+    """Start recording per-kernel HIP-event timings inside the library."""
+    _check(load_library().attn_timing_begin(int(capacity)))
+
+
+def timing_end() -> dict:
+    """Stop recording; returns {kernel_kind: (total_ms, launches)}."""
+    n = len(KERNEL_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int * n)()
+    _check(load_library().attn_timing_end(ms, cnt))
+    return {KERNEL_KINDS[i]: (ms[i], cnt[i]) for i in range(n)}

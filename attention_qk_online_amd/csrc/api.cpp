@@ -1,0 +1,320 @@
+// C ABI entry points: argument checks, the split plan for decode, launches
+// and the optional kernel-timing facility.  Declarations and the contract of
+// every entry point are in include/attn.h.
+#include "attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+attn_status fail(attn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- timing ---
+struct TimingRecord {
+  hipEvent_t start, stop;
+  int kind;
+};
+struct Timing {
+  bool on = false;
+  int capacity = 0;
+  int used = 0;
+  std::vector<TimingRecord> recs;
+} g_timing;
+
+// Launch `fn` (returns hipError_t) bracketed by timing events when enabled.
+template <typename F>
+hipError_t timed(int kind, hipStream_t s, F&& fn) {
+  TimingRecord* rec = nullptr;
+  if (g_timing.on && g_timing.used < g_timing.capacity) {
+    rec = &g_timing.recs[g_timing.used++];
+    rec->kind = kind;
+    (void)hipEventRecord(rec->start, s);
+  }
+  hipError_t e = fn();
+  if (rec) (void)hipEventRecord(rec->stop, s);
+  return e;
+}
+
+// ------------------------------------------------------------ decode plan ---
+// Pages per split when the caller passes 0: aim for about kUnitsTarget work
+// items over the whole batch (B * Hkv * splits of the longest request), with
+// splits of at least kMinSplitPages pages so partial states stay a small
+// fraction of the KV bytes.
+constexpr int kUnitsTarget = 2048;
+constexpr int kMinSplitPages = 8;
+
+int auto_split_pages(int B, int Hkv, int max_pages) {
+  if (max_pages <= 0) return kMinSplitPages;
+  long pairs = (long)B * Hkv;
+  long want = (kUnitsTarget + pairs - 1) / (pairs > 0 ? pairs : 1);
+  if (want < 1) want = 1;
+  long sp = (max_pages + want - 1) / want;
+  if (sp < kMinSplitPages) sp = kMinSplitPages;
+  return (int)sp;
+}
+
+struct DecodePlan {
+  int split_pages, n_splits;
+  size_t part_o_elems, part_lse_elems;
+  size_t bytes;  // 0 when no request can have more than one split
+};
+
+DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int page_size, int max_kv_len,
+                       int split_pages) {
+  DecodePlan pl{};
+  const int max_pages = page_size > 0 ? (max_kv_len + page_size - 1) / page_size : 0;
+  pl.split_pages = split_pages > 0 ? split_pages : auto_split_pages(B, Hkv, max_pages);
+  pl.n_splits = max_pages > 0 ? (max_pages + pl.split_pages - 1) / pl.split_pages : 1;
+  if (pl.n_splits < 1) pl.n_splits = 1;
+  if (pl.n_splits == 1) return pl;
+  pl.part_o_elems = (size_t)B * pl.n_splits * Hq * D;
+  pl.part_lse_elems = (size_t)B * pl.n_splits * Hq;
+  // part_o first, then part_lse, each 256-byte aligned
+  size_t o_bytes = (pl.part_o_elems * sizeof(float) + 255) & ~(size_t)255;
+  size_t l_bytes = (pl.part_lse_elems * sizeof(float) + 255) & ~(size_t)255;
+  pl.bytes = o_bytes + l_bytes;
+  return pl;
+}
+
+bool dtype_ok(attn_dtype d) { return d == ATTN_F32 || d == ATTN_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_NULL: return "null pointer argument";
+    case ATTN_E_SHAPE: return "invalid or inconsistent sizes";
+    case ATTN_E_DTYPE: return "unknown element type";
+    case ATTN_E_UNSUPPORTED: return "configuration not supported by this build";
+    case ATTN_E_VALUE: return "invalid value (non-finite scale)";
+    case ATTN_E_WORKSPACE: return "workspace missing or too small";
+    case ATTN_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+const char* attn_kernel_name(attn_kernel_kind kind) {
+  switch (kind) {
+    case ATTN_KERNEL_DECODE_SPLIT: return "decode_split";
+    case ATTN_KERNEL_DECODE_COMBINE: return "decode_combine";
+    case ATTN_KERNEL_PREFILL: return "prefill";
+    case ATTN_KERNEL_PREFILL_PAGED: return "prefill_paged";
+    default: return "unknown";
+  }
+}
+
+size_t attn_decode_paged_workspace_size(int B, int Hq, int Hkv, int D, int page_size,
+                                        int max_kv_len, int split_pages) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || max_kv_len < 0 ||
+      split_pages < 0)
+    return 0;
+  return plan_decode(B, Hq, Hkv, D, page_size, max_kv_len, split_pages).bytes;
+}
+
+attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pages,
+                              const void* v_pages, const int32_t* page_table,
+                              const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                              int page_size, int num_pages, int max_pages_per_req,
+                              int max_kv_len, int split_pages, float scale, void* out,
+                              float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  g_last_error[0] = 0;
+  if (!dtype_ok(dtype)) return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32/ATTN_BF16", dtype);
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || num_pages < 0 ||
+      max_pages_per_req < 0 || max_kv_len < 0 || split_pages < 0)
+    return fail(ATTN_E_SHAPE,
+                "negative or zero size (B=%d Hq=%d Hkv=%d D=%d page_size=%d num_pages=%d "
+                "max_pages_per_req=%d max_kv_len=%d split_pages=%d)",
+                B, Hq, Hkv, D, page_size, num_pages, max_pages_per_req, max_kv_len, split_pages);
+  if (Hq % Hkv != 0) return fail(ATTN_E_SHAPE, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if ((long)max_kv_len > (long)max_pages_per_req * page_size)
+    return fail(ATTN_E_SHAPE, "max_kv_len=%d exceeds max_pages_per_req*page_size=%ld", max_kv_len,
+                (long)max_pages_per_req * page_size);
+  if (!std::isfinite(scale)) return fail(ATTN_E_VALUE, "scale is not finite");
+  const int G = Hq / Hkv;
+  if (!attn::decode_supported((int)dtype, D, G, page_size))
+    return fail(ATTN_E_UNSUPPORTED, "decode: dtype=%d D=%d G=%d page_size=%d not built "
+                "(bf16: D in {64,128,256}; f32: D in {64,128}; G in {1,2,4,8}; page_size 16)", dtype, D, G, page_size);
+  if (B == 0) return ATTN_OK;
+  if (!q || !k_pages || !v_pages || !page_table || !kv_lens || !out || !lse)
+    return fail(ATTN_E_NULL, "a required pointer is NULL");
+  if (num_pages == 0 && max_kv_len > 0)
+    return fail(ATTN_E_SHAPE, "num_pages is 0 but max_kv_len=%d", max_kv_len);
+  const DecodePlan pl = plan_decode(B, Hq, Hkv, D, page_size, max_kv_len, split_pages);
+  if (pl.bytes > 0 && (!workspace || workspace_bytes < pl.bytes))
+    return fail(ATTN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (((uintptr_t)q | (uintptr_t)k_pages | (uintptr_t)v_pages | (uintptr_t)out) % 16 != 0)
+    return fail(ATTN_E_UNSUPPORTED, "q, k_pages, v_pages and out must be 16-byte aligned");
+
+  attn::DecodeParams p{};
+  p.q = q; p.k_pages = k_pages; p.v_pages = v_pages;
+  p.page_table = page_table; p.kv_lens = kv_lens;
+  p.out = out; p.lse = lse;
+  if (pl.bytes > 0) {
+    p.part_o = reinterpret_cast<float*>(workspace);
+    size_t o_bytes = (pl.part_o_elems * sizeof(float) + 255) & ~(size_t)255;
+    p.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + o_bytes);
+  }
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.num_pages = num_pages; p.max_pages = max_pages_per_req;
+  p.max_kv_len = max_kv_len; p.split_pages = pl.split_pages; p.n_splits = pl.n_splits;
+  p.scale_log2 = scale * kLog2e;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = timed(ATTN_KERNEL_DECODE_SPLIT, s,
+                       [&] { return attn::launch_decode_split(p, (int)dtype, D, G, s); });
+  if (e != hipSuccess)
+    return fail(ATTN_E_HIP, "decode_split launch: %s", hipGetErrorString(e));
+  if (pl.n_splits > 1) {
+    e = timed(ATTN_KERNEL_DECODE_COMBINE, s,
+              [&] { return attn::launch_decode_combine(p, (int)dtype, D, s); });
+    if (e != hipSuccess)
+      return fail(ATTN_E_HIP, "decode_combine launch: %s", hipGetErrorString(e));
+  }
+  return ATTN_OK;
+}
+
+static attn_status check_prefill_common(attn_dtype dtype, int B, int Hq, int Hkv, int D,
+                                        int total_q, int max_seqlen_q, int causal, float scale) {
+  if (!dtype_ok(dtype)) return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32/ATTN_BF16", dtype);
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || total_q < 0 || max_seqlen_q < 0)
+    return fail(ATTN_E_SHAPE, "negative or zero size (B=%d Hq=%d Hkv=%d D=%d total_q=%d "
+                "max_seqlen_q=%d)", B, Hq, Hkv, D, total_q, max_seqlen_q);
+  if (Hq % Hkv != 0) return fail(ATTN_E_SHAPE, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (causal != 0 && causal != 1) return fail(ATTN_E_VALUE, "causal must be 0 or 1");
+  if (!std::isfinite(scale)) return fail(ATTN_E_VALUE, "scale is not finite");
+  if (!attn::prefill_supported((int)dtype, D))
+    return fail(ATTN_E_UNSUPPORTED, "prefill: dtype=%d D=%d not built (bf16, D in {128,256})",
+                dtype, D);
+  return ATTN_OK;
+}
+
+attn_status attn_prefill_varlen(attn_dtype dtype, const void* q, const void* k, const void* v,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int B, int Hq, int Hkv, int D, int total_q, int total_k,
+                                int max_seqlen_q, int max_seqlen_k, int causal, float scale,
+                                void* out, float* lse, void* stream) {
+  g_last_error[0] = 0;
+  attn_status st = check_prefill_common(dtype, B, Hq, Hkv, D, total_q, max_seqlen_q, causal, scale);
+  if (st != ATTN_OK) return st;
+  if (total_k < 0 || max_seqlen_k < 0)
+    return fail(ATTN_E_SHAPE, "negative total_k=%d or max_seqlen_k=%d", total_k, max_seqlen_k);
+  if (B == 0 || max_seqlen_q == 0 || total_q == 0) return ATTN_OK;
+  if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !out || !lse)
+    return fail(ATTN_E_NULL, "a required pointer is NULL");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16 != 0)
+    return fail(ATTN_E_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
+  attn::PrefillParams p{};
+  p.q = q; p.k = k; p.v = v; p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
+  p.out = out; p.lse = lse;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.total_q = total_q; p.total_k = total_k;
+  p.max_seqlen_q = max_seqlen_q; p.max_seqlen_k = max_seqlen_k; p.causal = causal;
+  p.q_tiles = (max_seqlen_q + attn::kPrefillBM - 1) / attn::kPrefillBM;
+  p.scale_log2 = scale * kLog2e;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = timed(ATTN_KERNEL_PREFILL, s, [&] { return attn::launch_prefill(p, D, false, s); });
+  if (e != hipSuccess) return fail(ATTN_E_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+attn_status attn_prefill_paged(attn_dtype dtype, const void* q, const int32_t* cu_seqlens_q,
+                               const void* k_pages, const void* v_pages,
+                               const int32_t* page_table, const int32_t* kv_lens, int B, int Hq,
+                               int Hkv, int D, int total_q, int page_size, int num_pages,
+                               int max_pages_per_req, int max_seqlen_q, int max_kv_len,
+                               int causal, float scale, void* out, float* lse, void* stream) {
+  g_last_error[0] = 0;
+  attn_status st = check_prefill_common(dtype, B, Hq, Hkv, D, total_q, max_seqlen_q, causal, scale);
+  if (st != ATTN_OK) return st;
+  if (page_size <= 0 || num_pages < 0 || max_pages_per_req < 0 || max_kv_len < 0)
+    return fail(ATTN_E_SHAPE, "negative or zero size (page_size=%d num_pages=%d "
+                "max_pages_per_req=%d max_kv_len=%d)", page_size, num_pages, max_pages_per_req,
+                max_kv_len);
+  if (page_size != 16)
+    return fail(ATTN_E_UNSUPPORTED, "prefill_paged: page_size=%d not built (16)", page_size);
+  if ((long)max_kv_len > (long)max_pages_per_req * page_size)
+    return fail(ATTN_E_SHAPE, "max_kv_len=%d exceeds max_pages_per_req*page_size=%ld", max_kv_len,
+                (long)max_pages_per_req * page_size);
+  if (B == 0 || max_seqlen_q == 0 || total_q == 0) return ATTN_OK;
+  if (!q || !k_pages || !v_pages || !cu_seqlens_q || !page_table || !kv_lens || !out || !lse)
+    return fail(ATTN_E_NULL, "a required pointer is NULL");
+  if (num_pages == 0 && max_kv_len > 0)
+    return fail(ATTN_E_SHAPE, "num_pages is 0 but max_kv_len=%d", max_kv_len);
+  if (((uintptr_t)q | (uintptr_t)k_pages | (uintptr_t)v_pages | (uintptr_t)out) % 16 != 0)
+    return fail(ATTN_E_UNSUPPORTED, "q, k_pages, v_pages and out must be 16-byte aligned");
+  attn::PrefillParams p{};
+  p.q = q; p.k = k_pages; p.v = v_pages; p.cu_q = cu_seqlens_q;
+  p.page_table = page_table; p.kv_lens = kv_lens;
+  p.out = out; p.lse = lse;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.total_q = total_q; p.total_k = 0;
+  p.max_seqlen_q = max_seqlen_q; p.max_seqlen_k = max_kv_len;
+  p.num_pages = num_pages; p.max_pages = max_pages_per_req; p.causal = causal;
+  p.q_tiles = (max_seqlen_q + attn::kPrefillBM - 1) / attn::kPrefillBM;
+  p.scale_log2 = scale * kLog2e;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e =
+      timed(ATTN_KERNEL_PREFILL_PAGED, s, [&] { return attn::launch_prefill(p, D, true, s); });
+  if (e != hipSuccess) return fail(ATTN_E_HIP, "prefill_paged launch: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+attn_status attn_timing_begin(int capacity) {
+  g_last_error[0] = 0;
+  if (capacity <= 0) return fail(ATTN_E_SHAPE, "capacity must be positive");
+  while ((int)g_timing.recs.size() < capacity) {
+    TimingRecord r{};
+    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess)
+      return fail(ATTN_E_HIP, "hipEventCreate failed");
+    g_timing.recs.push_back(r);
+  }
+  g_timing.capacity = capacity;
+  g_timing.used = 0;
+  g_timing.on = true;
+  return ATTN_OK;
+}
+
+attn_status attn_timing_end(double* ms_per_kind, int* launches_per_kind) {
+  g_last_error[0] = 0;
+  g_timing.on = false;
+  for (int k = 0; k < ATTN_KERNEL_KINDS; ++k) {
+    if (ms_per_kind) ms_per_kind[k] = 0.0;
+    if (launches_per_kind) launches_per_kind[k] = 0;
+  }
+  for (int i = 0; i < g_timing.used; ++i) {
+    TimingRecord& r = g_timing.recs[i];
+    if (hipEventSynchronize(r.stop) != hipSuccess)
+      return fail(ATTN_E_HIP, "hipEventSynchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+      return fail(ATTN_E_HIP, "hipEventElapsedTime failed");
+    if (ms_per_kind) ms_per_kind[r.kind] += ms;
+    if (launches_per_kind) launches_per_kind[r.kind] += 1;
+  }
+  g_timing.used = 0;
+  return ATTN_OK;
+}
+
+}  // extern "C"

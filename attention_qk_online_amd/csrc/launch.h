@@ -1,0 +1,52 @@
+// Internal host-side interface between the C ABI (api.cpp) and the kernel
+// translation units.  Each launcher enqueues exactly one kernel on `stream`
+// and returns the launch status; argument checks happen before, in api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct DecodeParams {
+  const void* q;           // [B, Hq, D]
+  const void* k_pages;     // [num_pages, P, Hkv, D]
+  const void* v_pages;
+  const int32_t* page_table;  // [B, max_pages]
+  const int32_t* kv_lens;     // [B]
+  void* out;               // [B, Hq, D]
+  float* lse;              // [B, Hq]
+  float* part_o;           // [B, n_splits, Hq, D]   (workspace)
+  float* part_lse;         // [B, n_splits, Hq]      (workspace)
+  int B, Hq, Hkv, num_pages, max_pages, max_kv_len, split_pages, n_splits;
+  float scale_log2;        // softmax scale * log2(e)
+};
+
+struct PrefillParams {
+  const void* q;           // [total_q, Hq, D]
+  const void* k;           // contiguous: [total_k, Hkv, D]; paged: pool [num_pages, P, Hkv, D]
+  const void* v;
+  const int32_t* cu_q;     // [B+1]
+  const int32_t* cu_k;     // [B+1] (contiguous only)
+  const int32_t* page_table;  // [B, max_pages] (paged only)
+  const int32_t* kv_lens;     // [B]            (paged only)
+  void* out;               // [total_q, Hq, D]
+  float* lse;              // [total_q, Hq]
+  int B, Hq, Hkv, total_q, total_k, max_seqlen_q, max_seqlen_k;
+  int num_pages, max_pages;
+  int causal;
+  int q_tiles;             // ceil(max_seqlen_q / BM)
+  float scale_log2;
+};
+
+// dtype: 0 = f32, 1 = bf16 (values of attn_dtype).
+bool decode_supported(int dtype, int D, int G, int page_size);
+hipError_t launch_decode_split(const DecodeParams& p, int dtype, int D, int G, hipStream_t s);
+hipError_t launch_decode_combine(const DecodeParams& p, int dtype, int D, hipStream_t s);
+
+// Query rows per workgroup of the prefill kernels (grid sizing on the host).
+constexpr int kPrefillBM = 128;
+bool prefill_supported(int dtype, int D);
+hipError_t launch_prefill(const PrefillParams& p, int D, bool paged, hipStream_t s);
+
+}  // namespace attn

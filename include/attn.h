@@ -1,0 +1,192 @@
+/*
+ * attn.h -- C ABI of the fused attention forward for AMD MI355X (gfx950).
+ *
+ * One pass computes, per query row and query head,
+ *
+ *     s_j   = scale * <q, k_j>            over the visible keys j
+ *     lse   = log(sum_j exp(s_j))          (natural log, fp32)
+ *     out   = sum_j exp(s_j - lse) * v_j
+ *
+ * without writing the score matrix to memory: scores live in registers and an
+ * online softmax (running maximum and running sum, rescaled whenever the
+ * maximum grows) folds each block of keys into the output.  This is the
+ * fused scheme of "FlashAttention-3 内核在最新大模型推理中的集成实践"
+ * (section 一: tiles in on-chip memory, online softmax accumulated in place;
+ * section 四: the rescaling must never be dropped) and of "FlashInfer
+ * Attention Kernel技术解析" (section 1.3: QK^T, softmax with wave-level
+ * reductions, and PV as one pipeline).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensors are dense, row-major, and live in device memory unless the
+ *    argument says "host".  Element types: ATTN_F32 (float) or ATTN_BF16
+ *    (bfloat16 bits).  `out` has the input element type; `lse` is float.
+ *  - Grouped heads: query head h reads KV head h / (Hq / Hkv); Hq must be a
+ *    multiple of Hkv ("FlashAttention-3 ..." section 二: queries carry
+ *    num_heads, keys/values num_kv_heads).
+ *  - Causal masking is aligned to the bottom right: query i of a sequence with
+ *    Lq queries and Lk keys sees key j iff j <= i + (Lk - Lq).  A query row
+ *    that sees no key gets out = 0 and lse = -inf.
+ *  - Paged KV pools use the NHD layout [num_pages, page_size, Hkv, D]
+ *    ("FlashInfer内核库深度解析", KV-cache layout: NHD suits multi-head
+ *    parallelism); logical token t of request b is at
+ *    pool[page_table[b * max_pages_per_req + t / page_size]][t % page_size].
+ *    Table entries past ceil(kv_len / page_size) are never read.
+ *  - Ownership: the caller owns every buffer.  These entry points allocate no
+ *    device memory, keep no state between calls (apart from the optional
+ *    timing facility below), enqueue all work asynchronously on `stream`
+ *    (a hipStream_t; NULL means the default stream) and never synchronise
+ *    the device.  Host arrays are read only during the call.  `out`, `lse`
+ *    and `workspace` must not alias any input.
+ *  - Errors: every argument check runs before anything is enqueued; a
+ *    failing call returns a status, writes nothing and launches nothing.
+ *    attn_last_error() then describes the failure (thread-local text).
+ *    Device-resident index data (page tables, lengths, cu_seqlens) cannot be
+ *    checked on the host without a sync, so the kernels clamp it instead:
+ *    every memory access stays inside the sizes passed here, and a request
+ *    whose device data are inconsistent (a page id outside [0, num_pages), a
+ *    kv_len above max_kv_len or max_pages_per_req * page_size, a length
+ *    above max_seqlen_*) gets NaN in its out and lse rows.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_E_NULL = 1,        /* a required pointer is NULL                          */
+  ATTN_E_SHAPE = 2,       /* a size is negative or sizes are inconsistent         */
+  ATTN_E_DTYPE = 3,       /* unknown element type                                 */
+  ATTN_E_UNSUPPORTED = 4, /* valid request that this build has no kernel for     */
+  ATTN_E_VALUE = 5,       /* a non-finite scale                                   */
+  ATTN_E_WORKSPACE = 6,   /* workspace missing or smaller than the size query     */
+  ATTN_E_HIP = 7          /* the HIP runtime rejected a launch                    */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* ------------------------------------------------------------------------ */
+/* Batched decode over a paged KV cache.
+ *
+ * One query token per request attends to that request's kv_len cached tokens
+ * (no mask).  The keys of a request are cut into splits of `split_pages`
+ * pages; each (request, KV head, split) is one work item that streams its
+ * K/V pages with 128-bit loads and keeps G = Hq/Hkv query heads in registers.
+ * Splits are merged by their log-sum-exp in a second kernel (only requests
+ * with more than one split touch the workspace).  Pages, page tables and
+ * per-request lengths follow "FlashInfer内核库深度解析" (PageAttention:
+ * fixed-size pages addressed through a table) and "FlashAttention-3 ..."
+ * section 二 (physical block addressing in continuous batching).
+ *
+ *  q           [B, Hq, D]                   dtype
+ *  k_pages     [num_pages, page_size, Hkv, D] dtype
+ *  v_pages     [num_pages, page_size, Hkv, D] dtype
+ *  page_table  [B, max_pages_per_req]       int32
+ *  kv_lens     [B]                          int32, 0 <= kv_len <= max_kv_len
+ *  max_kv_len  host int: an upper bound of every kv_len (sizes the grid)
+ *  split_pages host int: pages per split; 0 picks a default from the sizes
+ *  scale       finite float (the caller's softmax scale, usually 1/sqrt(D))
+ *  out         [B, Hq, D]                   dtype
+ *  lse         [B, Hq]                      float
+ *  workspace   device scratch of at least attn_decode_paged_workspace_size()
+ *              bytes (may be NULL when that size is 0); contents on entry
+ *              do not matter and are clobbered.
+ *
+ * Supported: dtype BF16 with D in {64, 128, 256}, or F32 with D in {64, 128};
+ * Hq/Hkv in {1, 2, 4, 8}; page_size 16.  Anything else returns
+ * ATTN_E_UNSUPPORTED.
+ */
+size_t attn_decode_paged_workspace_size(int B, int Hq, int Hkv, int D, int page_size,
+                                        int max_kv_len, int split_pages);
+
+attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pages,
+                              const void* v_pages, const int32_t* page_table,
+                              const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                              int page_size, int num_pages, int max_pages_per_req,
+                              int max_kv_len, int split_pages, float scale, void* out,
+                              float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Ragged prefill addressed by cu_seqlens ("FlashAttention-3 ..." section 二:
+ * packed [total_tokens, heads, head_dim] tensors, prefix offsets of length
+ * batch+1, max_seqlen_q / max_seqlen_k, softmax_scale and causal).
+ *
+ *  q            [total_q, Hq, D]   bf16
+ *  k, v         [total_k, Hkv, D]  bf16
+ *  cu_seqlens_q [B+1] int32, nondecreasing, cu[0] = 0, cu[B] <= total_q
+ *  cu_seqlens_k [B+1] int32, same rules against total_k
+ *  max_seqlen_q, max_seqlen_k  host ints bounding every per-sequence length
+ *  causal       0 or 1 (bottom-right aligned)
+ *  out          [total_q, Hq, D] bf16;  lse [total_q, Hq] float
+ *
+ * Query tiles of 128 rows run on bf16 MFMA with fp32 accumulation; K/V tiles
+ * are staged through LDS; tiles wholly above the causal diagonal are never
+ * loaded.  Supported: dtype BF16; D in {128, 256}; any Hq multiple of Hkv.
+ * Rows of out/lse outside every [cu_seqlens_q[b], cu_seqlens_q[b+1]) are
+ * not written.
+ */
+attn_status attn_prefill_varlen(attn_dtype dtype, const void* q, const void* k, const void* v,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int B, int Hq, int Hkv, int D, int total_q, int total_k,
+                                int max_seqlen_q, int max_seqlen_k, int causal, float scale,
+                                void* out, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Chunked prefill over a paged KV cache ("FlashAttention-3 ..." section 二:
+ * chunked prefill and PagedAttention block addressing).  Request b's
+ * queries are the last Lq_b = cu_seqlens_q[b+1] - cu_seqlens_q[b] of its
+ * kv_lens[b] cached tokens (their own K/V already written to the cache), so
+ * the causal mask is bottom-right aligned.  Pages may be shared between
+ * requests (a common prefix).
+ *
+ *  q            [total_q, Hq, D] bf16;   cu_seqlens_q [B+1] int32
+ *  k_pages, v_pages [num_pages, page_size, Hkv, D] bf16
+ *  page_table   [B, max_pages_per_req] int32;  kv_lens [B] int32
+ *  max_seqlen_q, max_kv_len  host bounds
+ *  out [total_q, Hq, D] bf16;  lse [total_q, Hq] float
+ *
+ * Supported: dtype BF16; D in {128, 256}; page_size 16.
+ */
+attn_status attn_prefill_paged(attn_dtype dtype, const void* q, const int32_t* cu_seqlens_q,
+                               const void* k_pages, const void* v_pages,
+                               const int32_t* page_table, const int32_t* kv_lens, int B, int Hq,
+                               int Hkv, int D, int total_q, int page_size, int num_pages,
+                               int max_pages_per_req, int max_seqlen_q, int max_kv_len,
+                               int causal, float scale, void* out, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Status text (static strings) and the detail of the calling thread's last
+ * failing call (valid until that thread's next call into the library). */
+const char* attn_status_string(attn_status s);
+const char* attn_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Optional kernel timing for benchmarks.  Between attn_timing_begin() and
+ * attn_timing_end(), every kernel the library launches is bracketed by a
+ * pair of hipEvents recorded on its launch stream.  attn_timing_end() waits
+ * for those events and returns, per kernel kind, the summed milliseconds and
+ * the number of launches.  Process-wide, not thread-safe; it creates HIP
+ * events (no device memory).  At most `capacity` launches are recorded. */
+typedef enum {
+  ATTN_KERNEL_DECODE_SPLIT = 0,
+  ATTN_KERNEL_DECODE_COMBINE = 1,
+  ATTN_KERNEL_PREFILL = 2,
+  ATTN_KERNEL_PREFILL_PAGED = 3,
+  ATTN_KERNEL_KINDS = 4
+} attn_kernel_kind;
+
+attn_status attn_timing_begin(int capacity);
+attn_status attn_timing_end(double* ms_per_kind, int* launches_per_kind);
+const char* attn_kernel_name(attn_kernel_kind kind);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ATTN_H */

@@ -1,0 +1,155 @@
+"""C-ABI library checks that need no GPU: it loads, exports every function
+declared in include/attn.h, and rejects bad arguments with the documented
+status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_VALUE, E_WS, E_HIP = range(8)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import attention_qk_online_amd as A
+    if not os.path.exists(A.library_path()):
+        pytest.fail("libattn.so is not built (run __graft_entry__.build())")
+    return A.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert len(names) >= 9, names
+    raw = ctypes.CDLL(os.path.join(ROOT, "attention_qk_online_amd", "libattn.so"))
+    for n in names:
+        assert hasattr(raw, n), f"{n} is declared in attn.h but not exported"
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert lib.attn_status_string(s)
+    assert lib.attn_status_string(99) == b"unknown status"
+    for k in range(4):
+        assert lib.attn_kernel_name(k) != b"unknown"
+
+
+def _decode(lib, **kw):
+    a = dict(dtype=1, q=16, k=16, v=16, table=16, lens=16, B=2, Hq=8, Hkv=2, D=128, P=16,
+             num_pages=100, max_pages=8, max_kv_len=128, split=0, scale=0.1, out=16, lse=16,
+             ws=16, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.attn_decode_paged(a["dtype"], a["q"], a["k"], a["v"], a["table"], a["lens"], a["B"],
+                                 a["Hq"], a["Hkv"], a["D"], a["P"], a["num_pages"], a["max_pages"],
+                                 a["max_kv_len"], a["split"], a["scale"], a["out"], a["lse"], a["ws"],
+                                 a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), E_DTYPE),
+    (dict(B=-1), E_SHAPE),
+    (dict(Hq=6, Hkv=4), E_SHAPE),
+    (dict(max_kv_len=129), E_SHAPE),          # above max_pages * page_size
+    (dict(scale=float("inf")), E_VALUE),
+    (dict(scale=float("nan")), E_VALUE),
+    (dict(D=96), E_UNSUP),
+    (dict(P=32, max_pages=4), E_UNSUP),
+    (dict(Hq=32, Hkv=2), E_UNSUP),            # group of 16
+    (dict(dtype=0, D=256), E_UNSUP),
+    (dict(q=None), E_NULL),
+    (dict(table=None), E_NULL),
+    (dict(ws=None, split=2), E_WS),
+    (dict(ws_bytes=8, split=2), E_WS),
+    (dict(q=8), E_UNSUP),                     # misaligned
+    (dict(num_pages=0), E_SHAPE),
+])
+def test_decode_rejects(lib, kw, status):
+    assert _decode(lib, **kw) == status
+    assert lib.attn_last_error()
+
+
+def test_decode_empty_batch_is_noop(lib):
+    assert _decode(lib, B=0, q=None, k=None) == OK
+
+
+def test_workspace_size(lib):
+    # one split -> no workspace; forced small splits -> B*splits*Hq*(D+1) floats (256-aligned parts)
+    assert lib.attn_decode_paged_workspace_size(4, 8, 2, 128, 16, 100, 0) == 0
+    n = lib.attn_decode_paged_workspace_size(4, 8, 2, 128, 16, 160, 2)   # 10 pages -> 5 splits
+    o = 4 * 5 * 8 * 128 * 4
+    lse = 4 * 5 * 8 * 4
+    assert n == ((o + 255) // 256 + (lse + 255) // 256) * 256
+    assert lib.attn_decode_paged_workspace_size(-1, 8, 2, 128, 16, 160, 2) == 0
+
+
+def _prefill(lib, **kw):
+    a = dict(dtype=1, q=16, k=16, v=16, cq=16, ck=16, B=2, Hq=8, Hkv=2, D=128, Tq=100, Tk=100,
+             mq=64, mk=64, causal=1, scale=0.1, out=16, lse=16, stream=None)
+    a.update(kw)
+    return lib.attn_prefill_varlen(a["dtype"], a["q"], a["k"], a["v"], a["cq"], a["ck"], a["B"],
+                                   a["Hq"], a["Hkv"], a["D"], a["Tq"], a["Tk"], a["mq"], a["mk"],
+                                   a["causal"], a["scale"], a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3), E_DTYPE),
+    (dict(dtype=0), E_UNSUP),                 # fp32 prefill is not built
+    (dict(D=64), E_UNSUP),
+    (dict(Hq=8, Hkv=3), E_SHAPE),
+    (dict(causal=2), E_VALUE),
+    (dict(scale=float("-inf")), E_VALUE),
+    (dict(Tk=-1), E_SHAPE),
+    (dict(cq=None), E_NULL),
+    (dict(out=None), E_NULL),
+    (dict(k=24), E_UNSUP),
+])
+def test_prefill_rejects(lib, kw, status):
+    assert _prefill(lib, **kw) == status
+
+
+def test_prefill_empty_is_noop(lib):
+    assert _prefill(lib, B=0, q=None) == OK
+    assert _prefill(lib, mq=0, q=None) == OK
+
+
+def test_prefill_paged_rejects(lib):
+    def call(**kw):
+        a = dict(dtype=1, q=16, cq=16, k=16, v=16, t=16, lens=16, B=2, Hq=4, Hkv=4, D=256, Tq=10,
+                 P=16, num_pages=10, max_pages=4, mq=5, mkv=64, causal=1, scale=0.1, out=16, lse=16)
+        a.update(kw)
+        return lib.attn_prefill_paged(a["dtype"], a["q"], a["cq"], a["k"], a["v"], a["t"], a["lens"],
+                                      a["B"], a["Hq"], a["Hkv"], a["D"], a["Tq"], a["P"],
+                                      a["num_pages"], a["max_pages"], a["mq"], a["mkv"], a["causal"],
+                                      a["scale"], a["out"], a["lse"], None)
+    assert call(P=8) == E_UNSUP
+    assert call(mkv=65) == E_SHAPE
+    assert call(t=None) == E_NULL
+    assert call(D=100) == E_UNSUP
+    assert call(B=0, q=None) == OK
+
+
+def test_binding_rejects_host_tensors():
+    import attention_qk_online_amd as A
+    q = torch.zeros(2, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        A.decode_paged(q, q, q, torch.zeros(2, 1, dtype=torch.int32), torch.zeros(2, dtype=torch.int32))
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import attention_qk_online_amd as A
+    with pytest.raises(RuntimeError):
+        A.load_library(str(tmp_path / "missing.so"))
+
+
+def test_timing_api_without_gpu(lib):
+    assert lib.attn_timing_begin(0) == E_SHAPE

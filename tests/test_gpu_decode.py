@@ -1,0 +1,137 @@
+"""GPU parity of attn_decode_paged (split-KV decode + LSE combine) against the oracle."""
+import math
+
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(case, gpu, split_pages=0, pools=None, table=None):
+    import attention_qk_online_amd as A
+    kp, vp = pools if pools is not None else case.pools(gpu)
+    t = (case.page_table if table is None else table).to(gpu)
+    out, lse = A.decode_paged(case.q.to(gpu), kp, vp, t, case.kv_lens.to(gpu), scale=case.scale,
+                              max_kv_len=case.max_kv_len, split_pages=split_pages)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _oracle(case):
+    kp, vp = case.pools("cpu")
+    return oracle.ref_decode_paged(case.q, kp, vp, case.page_table, case.kv_lens, case.scale)
+
+
+def test_single_sequence_fp32(gpu):
+    """fp32 decode, 1 token, 4 heads (MHA), head_dim 64, contiguous KV of 256 as pages."""
+    case = workloads.make_config(1)
+    out, lse = _run(case, gpu)
+    ro, rl = _oracle(case)
+    assert_parity(out, lse, ro, rl, torch.float32, case.name)
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 8, 2), (128, 32, 8), (64, 8, 8), (256, 16, 2),
+                                      (128, 8, 1)])
+@pytest.mark.parametrize("split_pages", [0, 1, 2, 7])
+def test_small_paged_bf16(gpu, D, Hq, Hkv, split_pages):
+    lens = [1, 15, 16, 17, 300, 64, 1000, 3]
+    case = workloads.make_decode(B=len(lens), Hq=Hq, Hkv=Hkv, D=D, page_size=16, kv_lens=lens,
+                                 dtype=torch.bfloat16, seed=100 + D + Hq, extra_pages=9)
+    out, lse = _run(case, gpu, split_pages)
+    ro, rl = _oracle(case)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, f"D{D} Hq{Hq} Hkv{Hkv} split{split_pages}")
+
+
+def test_small_fp32_groups(gpu):
+    for G in (1, 2, 4, 8):
+        case = workloads.make_decode(B=3, Hq=8, Hkv=8 // G, D=128, page_size=16, kv_lens=[5, 77, 200],
+                                     dtype=torch.float32, seed=7 + G)
+        out, lse = _run(case, gpu, split_pages=3)
+        ro, rl = _oracle(case)
+        assert_parity(out, lse, ro, rl, torch.float32, f"fp32 G{G}")
+
+
+def test_split_counts_agree(gpu):
+    """Forced split counts (1 page .. whole request) agree with each other and the oracle."""
+    case = workloads.make_decode(B=4, Hq=16, Hkv=4, D=128, page_size=16, kv_lens=[2000, 1, 513, 4096],
+                                 dtype=torch.bfloat16, seed=9)
+    ro, rl = _oracle(case)
+    pools = case.pools(gpu)
+    results = []
+    for sp in (1, 2, 7, 64, 256):
+        out, lse = _run(case, gpu, sp, pools=pools)
+        assert_parity(out, lse, ro, rl, torch.bfloat16, f"split_pages={sp}")
+        results.append(out.float())
+    for r in results[1:]:
+        assert (r - results[0]).abs().max().item() <= 2e-2
+
+
+def test_page_permutation_bitwise(gpu):
+    """Moving physical pages (and remapping the table) changes nothing, bit for bit."""
+    case = workloads.make_decode(B=5, Hq=8, Hkv=2, D=128, page_size=16, kv_lens=[33, 400, 16, 1, 250],
+                                 dtype=torch.bfloat16, seed=11, extra_pages=20)
+    kp, vp = case.pools(gpu)
+    out1, lse1 = _run(case, gpu, pools=(kp, vp))
+    perm = torch.randperm(case.num_pages, generator=torch.Generator().manual_seed(5))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(case.num_pages)
+    pg = perm.to(gpu)
+    out2, lse2 = _run(case, gpu, pools=(kp[pg].contiguous(), vp[pg].contiguous()),
+                      table=inv[case.page_table.long()].to(torch.int32))
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_deterministic(gpu):
+    case = workloads.make_decode(B=6, Hq=32, Hkv=8, D=128, page_size=16, len_range=(1, 3000),
+                                 dtype=torch.bfloat16, seed=12)
+    pools = case.pools(gpu)
+    a = _run(case, gpu, pools=pools)
+    b = _run(case, gpu, pools=pools)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_empty_and_bad_requests(gpu):
+    """kv_len 0 -> out 0, lse -inf; an out-of-range page id or an oversize kv_len
+    poisons only that request with NaN; neighbours are unaffected."""
+    import attention_qk_online_amd as A
+    case = workloads.make_decode(B=4, Hq=8, Hkv=2, D=128, page_size=16, kv_lens=[0, 40, 40, 40],
+                                 dtype=torch.bfloat16, seed=13, extra_pages=2)
+    ro, rl = _oracle(case)
+    kp, vp = case.pools(gpu)
+    table = case.page_table.clone()
+    table[2, 1] = case.num_pages + 5           # out of range
+    lens = case.kv_lens.clone()
+    lens[3] = 10 ** 6                          # above max_kv_len
+    out, lse = A.decode_paged(case.q.to(gpu), kp, vp, table.to(gpu), lens.to(gpu), scale=case.scale,
+                              max_kv_len=48, split_pages=1)
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu()
+    assert torch.equal(out[0].float(), torch.zeros_like(out[0].float()))
+    assert torch.isneginf(lse[0]).all()
+    assert_parity(out[1:2], lse[1:2], ro[1:2], rl[1:2], torch.bfloat16, "neighbour")
+    assert torch.isnan(out[2].float()).all() and torch.isnan(lse[2]).all()
+    assert torch.isnan(out[3].float()).all() and torch.isnan(lse[3]).all()
+
+
+def test_large_logits(gpu):
+    """Logits around 1000 (scale x q.k): the online rescaling keeps the result finite."""
+    case = workloads.make_decode(B=2, Hq=4, Hkv=1, D=128, page_size=16, kv_lens=[700, 33],
+                                 dtype=torch.bfloat16, seed=14, scale=40.0)
+    out, lse = _run(case, gpu, split_pages=3)
+    ro, rl = _oracle(case)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    assert rl.abs().max() > 500
+    assert_parity(out, lse, ro, rl, torch.bfloat16, "large logits")
+
+
+def test_paged_config_full(gpu):
+    """Batched paged GQA decode at full size: B 64, Hq 32, Hkv 8, D 128, page 16,
+    kv_len in [512, 4096], pages scattered over a 300k-page pool."""
+    case = workloads.make_config(2)
+    out, lse = _run(case, gpu)
+    ro, rl = _oracle(case)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, case.name)

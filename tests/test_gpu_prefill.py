@@ -1,0 +1,176 @@
+"""GPU parity of attn_prefill_varlen / attn_prefill_paged against the oracle."""
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _varlen(case, gpu, causal=None):
+    import attention_qk_online_amd as A
+    causal = case.causal if causal is None else causal
+    out, lse = A.prefill_varlen(case.q.to(gpu), case.k.to(gpu), case.v.to(gpu),
+                                case.cu_seqlens_q.to(gpu), case.cu_seqlens_k.to(gpu),
+                                case.max_seqlen_q, case.max_seqlen_k, causal=causal,
+                                scale=case.scale)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _paged(case, gpu, pools=None, table=None):
+    import attention_qk_online_amd as A
+    kp, vp = pools if pools is not None else case.pools(gpu)
+    t = case.page_table if table is None else table
+    out, lse = A.prefill_paged(case.q.to(gpu), case.cu_seqlens_q.to(gpu), kp, vp, t.to(gpu),
+                               case.kv_lens.to(gpu), case.max_seqlen_q, case.max_kv_len,
+                               causal=case.causal, scale=case.scale)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _ref(case, causal=None, rows=None):
+    causal = case.causal if causal is None else causal
+    return oracle.ref_prefill_varlen(case.q, case.k, case.v, case.cu_seqlens_q, case.cu_seqlens_k,
+                                     causal, case.scale, rows=rows)
+
+
+def _sample_rows(cu, n, seed):
+    """Rows to check at full size: first/last two rows of every sequence, the
+    rows around each 128-row tile edge of the first sequence, plus random rows."""
+    cu = [int(x) for x in cu]
+    rows = set()
+    for a, b in zip(cu[:-1], cu[1:]):
+        rows.update(r for r in (a, a + 1, b - 2, b - 1) if a <= r < b)
+    for t in range(cu[0] + 127, min(cu[1], cu[0] + 1024), 128):
+        rows.update((t, t + 1))
+    g = torch.Generator().manual_seed(seed)
+    rows.update(torch.randint(0, cu[-1], (n,), generator=g).tolist())
+    return torch.tensor(sorted(r for r in rows if r < cu[-1]))
+
+
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("causal", [True, False])
+def test_small_varlen(gpu, D, causal):
+    lens = [1, 17, 128, 129, 300, 64, 255]
+    case = workloads.make_prefill(B=len(lens), Hq=8, Hkv=2, D=D, lens_q=lens, dtype=torch.bfloat16,
+                                  seed=200 + D, causal=causal)
+    out, lse = _varlen(case, gpu)
+    ro, rl = _ref(case)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, f"D{D} causal{causal}")
+
+
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_group_sizes(gpu, G):
+    case = workloads.make_prefill(B=2, Hq=8, Hkv=8 // G, D=128, lens_q=[200, 77], dtype=torch.bfloat16,
+                                  seed=210 + G, causal=True)
+    out, lse = _varlen(case, gpu)
+    ro, rl = _ref(case)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, f"G{G}")
+
+
+def test_bottom_right_causal(gpu):
+    """Lq != Lk: queries are the last Lq positions; Lq > Lk leaves leading rows empty."""
+    case = workloads.make_prefill(B=4, Hq=4, Hkv=4, D=128, lens_q=[100, 5, 300, 40],
+                                  lens_k=[500, 5, 130, 0], dtype=torch.bfloat16, seed=220, causal=True)
+    out, lse = _varlen(case, gpu)
+    ro, rl = _ref(case)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, "bottom-right")
+
+
+def test_causal_row0_and_gqa_bitwise(gpu):
+    """Causal row 0 is exactly v[0]; GQA equals MHA with repeated K/V, bit for bit."""
+    case = workloads.make_prefill(B=1, Hq=8, Hkv=2, D=128, lens_q=[333], dtype=torch.bfloat16,
+                                  seed=230, causal=True)
+    out, lse = _varlen(case, gpu)
+    v0 = case.v[0].repeat_interleave(4, dim=0)
+    assert torch.equal(out[0].cpu(), v0)
+    rep = workloads.PrefillCase(**{**case.__dict__, "Hkv": 8,
+                                   "k": case.k.repeat_interleave(4, dim=1).contiguous(),
+                                   "v": case.v.repeat_interleave(4, dim=1).contiguous()})
+    out2, lse2 = _varlen(rep, gpu)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+def test_large_logits(gpu):
+    case = workloads.make_prefill(B=1, Hq=2, Hkv=1, D=128, lens_q=[400], dtype=torch.bfloat16,
+                                  seed=240, causal=True, scale=40.0)
+    out, lse = _varlen(case, gpu)
+    ro, rl = _ref(case)
+    assert torch.isfinite(out.float()).all()
+    assert rl.abs().max() > 500
+    assert_parity(out, lse, ro, rl, torch.bfloat16, "large logits")
+
+
+def test_deterministic(gpu):
+    case = workloads.make_prefill(B=3, Hq=8, Hkv=1, D=128, len_range=(100, 700), dtype=torch.bfloat16,
+                                  seed=250, causal=True)
+    a = _varlen(case, gpu)
+    b = _varlen(case, gpu)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_small_paged(gpu, D):
+    case = workloads.make_paged_prefill(B=3, Hq=4, Hkv=2, D=D, page_size=16, chunk=70, cached=200,
+                                        shared_prefix=64, dtype=torch.bfloat16, seed=260 + D)
+    out, lse = _paged(case, gpu)
+    ro, rl = oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, case.pool_k, case.pool_v,
+                                      case.page_table, case.kv_lens, True, case.scale)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, f"paged D{D}")
+
+
+def test_paged_equals_contiguous_bitwise(gpu):
+    """The paged loader and the contiguous loader give identical bits."""
+    case = workloads.make_paged_prefill(B=2, Hq=4, Hkv=4, D=128, page_size=16, chunk=150, cached=333,
+                                        shared_prefix=32, dtype=torch.bfloat16, seed=270)
+    out, lse = _paged(case, gpu)
+    ks, vs, ck = [], [], [0]
+    for b in range(case.B):
+        L = int(case.kv_lens[b])
+        ks.append(oracle.gather_pages(case.pool_k, case.page_table[b], L))
+        vs.append(oracle.gather_pages(case.pool_v, case.page_table[b], L))
+        ck.append(ck[-1] + L)
+    contig = workloads.PrefillCase(name="contig", seed=0, B=case.B, Hq=4, Hkv=4, D=128,
+                                   dtype=torch.bfloat16, causal=True, scale=case.scale, q=case.q,
+                                   k=torch.cat(ks), v=torch.cat(vs), cu_seqlens_q=case.cu_seqlens_q,
+                                   cu_seqlens_k=torch.tensor(ck, dtype=torch.int32))
+    out2, lse2 = _varlen(contig, gpu)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+def test_ragged_config_sampled(gpu):
+    """Ragged causal prefill at full size: B 8, L in [1024, 4096], Hq 64, Hkv 8, D 128."""
+    case = workloads.make_config(3)
+    out, lse = _varlen(case, gpu)
+    rows = _sample_rows(case.cu_seqlens_q, 96, 3)
+    ro, rl = _ref(case, rows=rows)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, case.name + " (sampled rows)", rows=rows)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+def test_long_config_sampled(gpu):
+    """Single 32768-token causal prefill (Hq 64, Hkv 8, D 128), plus the 1K/4K/16K prefixes."""
+    case = workloads.make_config(4)
+    for L in (1024, 4096, 16384, 32768):
+        sub = case.prefix(L) if L < 32768 else case
+        out, lse = _varlen(sub, gpu)
+        rows = _sample_rows(sub.cu_seqlens_q, 24, L)
+        ro, rl = _ref(sub, rows=rows)
+        assert_parity(out, lse, ro, rl, torch.bfloat16, f"{sub.name} (sampled rows)", rows=rows)
+        assert torch.isfinite(out.float()).all()
+        del out, lse
+
+
+def test_chunked_paged_config_sampled(gpu):
+    """Chunked prefill on a paged cache: 16 requests x 512-token chunks over 8192 cached
+    tokens, the first 4096 on shared pages; Hq = Hkv = 16, D 256, page 16."""
+    case = workloads.make_config(5)
+    out, lse = _paged(case, gpu)
+    rows = _sample_rows(case.cu_seqlens_q, 48, 5)
+    ro, rl = oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, case.pool_k, case.pool_v,
+                                      case.page_table, case.kv_lens, True, case.scale, rows=rows)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, case.name + " (sampled rows)", rows=rows)
+    assert torch.isfinite(out.float()).all()
