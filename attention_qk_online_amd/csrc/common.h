@@ -63,11 +63,24 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-// Exchange with the lane 32 positions away (lane i <-> i^32), one instruction on gfx950.
+// v_permlane32_swap with the same register as both operands returns
+// r[0] = (x[0..31], x[0..31]) and r[1] = (x[32..63], x[32..63]), so each lane
+// sees its own value and its partner's (lane ^ 32) in r[0], r[1].
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                            false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                            false, false);
+  return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
+// Value of lane ^ 32.
 __device__ __forceinline__ float swap_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
                                             false, false);
-  return __builtin_bit_cast(float, (int)r[0]);
+  return __builtin_bit_cast(float, (int)(__lane_id() < 32 ? r[1] : r[0]));
 }
 
 __device__ __forceinline__ float shfl_xor_f32(float x, int mask) {

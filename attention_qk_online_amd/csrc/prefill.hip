@@ -234,7 +234,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
         mt = fmaxf(mt, v);
       }
     }
-    mt = fmaxf(mt, swap_halves(mt));
+    mt = max_halves(mt);
     const float mn = fmaxf(m, mt);
     const float mu = mn == kNegInf ? 0.f : mn;
     const float alpha = exp2_fast(m - mu);
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   const bool any_bad = __syncthreads_or(bad);
 
   // ---- epilogue: O / l, LSE in natural log
-  const float ltot = lsum + swap_halves(lsum);
+  const float ltot = sum_halves(lsum);
   float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   float lse_v = ltot > 0.f ? (m + log2_fast(ltot)) * kLn2 : kNegInf;
   if (any_bad) {
