@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM:
+  1. batched paged GQA decode (bf16, B 64, Hq 32, Hkv 8, D 128, page 16,
+     kv_len uniform in [512, 4096], pages scattered over a 300k-page pool):
+     split-KV kernel + log-sum-exp combine;
+  2. ragged causal prefill (bf16, B 8, L uniform in [1024, 4096], Hq 64,
+     Hkv 8, D 128) packed by cu_seqlens;
+  3. chunked prefill over a paged cache with a shared prefix (bf16, 16
+     requests x 512-token chunks on 8192 cached tokens, Hq = Hkv = 16, D 256).
+
+The headline value is decode KV throughput (algorithmic K+V bytes / decode
+call time, GB/s); prefill TFLOPS (algorithmic causal flops / call time) is
+reported beside it.  Per-kernel durations come from HIP events that the
+library records around each of its launches on the launch stream.  The CPU
+oracle is timed on the host cores over the whole decode workload (repeated
+to at least ~10 s), as a reported baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--no-cpu-baseline]
+Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+METRIC = "decode KV GB/s (% HBM peak); causal prefill TFLOPS (% bf16 MFMA peak)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sweep", action="store_true", help="also time the 1K-32K single-sequence sweep")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the kernels shard by request/head with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_qk_online_amd as A
+    import workloads
+
+    dev = torch.device("cuda:0")
+    A.load_library()
+
+    # ---------------------------------------------------------------- inputs
+    log("bench: generating inputs")
+    dec = workloads.make_config(2)
+    d_kp, d_vp = dec.pools(dev)
+    d_q, d_table, d_lens = dec.q.to(dev), dec.page_table.to(dev), dec.kv_lens.to(dev)
+    d_out = torch.empty_like(d_q)
+    d_lse = torch.empty((dec.B, dec.Hq), dtype=torch.float32, device=dev)
+    ws_bytes = A.decode_paged_workspace_size(dec.B, dec.Hq, dec.Hkv, dec.D, dec.page_size,
+                                             dec.max_kv_len, 0)
+    d_ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    pre = workloads.make_config(3)
+    p_q, p_k, p_v = pre.q.to(dev), pre.k.to(dev), pre.v.to(dev)
+    p_cq, p_ck = pre.cu_seqlens_q.to(dev), pre.cu_seqlens_k.to(dev)
+    p_out = torch.empty_like(p_q)
+    p_lse = torch.empty(p_q.shape[:2], dtype=torch.float32, device=dev)
+
+    pg = workloads.make_config(5)
+    g_q, g_cq = pg.q.to(dev), pg.cu_seqlens_q.to(dev)
+    g_kp, g_vp = pg.pools(dev)
+    g_table, g_lens = pg.page_table.to(dev), pg.kv_lens.to(dev)
+    g_out = torch.empty_like(g_q)
+    g_lse = torch.empty(g_q.shape[:2], dtype=torch.float32, device=dev)
+
+    def decode():
+        A.decode_paged(d_q, d_kp, d_vp, d_table, d_lens, scale=dec.scale, max_kv_len=dec.max_kv_len,
+                       out=d_out, lse=d_lse, workspace=d_ws)
+
+    def prefill():
+        A.prefill_varlen(p_q, p_k, p_v, p_cq, p_ck, pre.max_seqlen_q, pre.max_seqlen_k, causal=True,
+                         scale=pre.scale, out=p_out, lse=p_lse)
+
+    def paged():
+        A.prefill_paged(g_q, g_cq, g_kp, g_vp, g_table, g_lens, pg.max_seqlen_q, pg.max_kv_len,
+                        causal=True, scale=pg.scale, out=g_out, lse=g_lse)
+
+    stream = torch.cuda.current_stream(dev)
+    log("bench: warmup")
+    for _ in range(args.warmup):
+        decode(); prefill(); paged()
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------------ timed steps
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    A.timing_begin(8 * K + 16)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        decode()
+        ev[i][1].record(stream)
+        prefill()
+        ev[i][2].record(stream)
+        paged()
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kt = A.timing_end()
+    log("bench: timed", K, "steps in", t1 - t0, "s")
+
+    seg = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K for j in range(3)]
+    ms_decode, ms_prefill, ms_paged = seg
+
+    def avg(kind):
+        ms, n = kt[kind]
+        return ms / n if n else float("nan")
+
+    kv_bytes = dec.kv_bytes()
+    pre_flops = pre.flops()
+    pg_flops = pg.flops()
+    split_ms = avg("decode_split")
+    prefill_ms = avg("prefill")
+    paged_ms = avg("prefill_paged")
+    decode_gbs = kv_bytes / (ms_decode * 1e-3) / 1e9
+
+    def roofline_hbm(nbytes, ms):
+        a = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None}
+
+    def roofline_mfma(flops, ms):
+        a = flops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(a, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(a / BF16_PEAK_TFLOPS, 4), "traffic": None}
+
+    res = {
+        "metric": METRIC,
+        "value": round(decode_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workloads.CONFIG_NAMES[2], "B": dec.B, "Hq": dec.Hq, "Hkv": dec.Hkv,
+                   "D": dec.D, "page_size": dec.page_size, "pool_pages": dec.num_pages,
+                   "sum_kv_len": int(dec.kv_lens.sum()), "kv_bytes": kv_bytes,
+                   "step": "paged decode + ragged causal prefill + chunked paged prefill"},
+        "decode": {"call_ms": round(ms_decode, 5), "split_kernel_ms": round(split_ms, 5),
+                   "combine_kernel_ms": round(avg("decode_combine"), 5),
+                   "frac_of_hbm_peak": round(decode_gbs / HBM_PEAK_GBS, 4)},
+        "roofline": roofline_hbm(kv_bytes, split_ms),
+        "prefill": {
+            "metric": "causal prefill TFLOPS", "unit": "TFLOP/s",
+            "value": round(pre_flops / (ms_prefill * 1e-3) / 1e12, 2),
+            "workload": workloads.CONFIG_NAMES[3], "flops": pre_flops,
+            "call_ms": round(ms_prefill, 4), "kernel_ms": round(prefill_ms, 4),
+            "roofline": roofline_mfma(pre_flops, prefill_ms),
+        },
+        "prefill_paged": {
+            "metric": "chunked paged prefill TFLOPS", "unit": "TFLOP/s",
+            "value": round(pg_flops / (ms_paged * 1e-3) / 1e12, 2),
+            "workload": workloads.CONFIG_NAMES[5], "flops": pg_flops,
+            "call_ms": round(ms_paged, 4), "kernel_ms": round(paged_ms, 4),
+            "roofline": roofline_mfma(pg_flops, paged_ms),
+        },
+    }
+
+    if args.sweep:
+        del p_q, p_k, p_v, p_out, p_lse
+        long = workloads.make_config(4)
+        q, k, v = long.q.to(dev), long.k.to(dev), long.v.to(dev)
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        sweep = {}
+        for L in (1024, 4096, 16384, 32768):
+            cu = torch.tensor([0, L], dtype=torch.int32, device=dev)
+            fl = workloads.prefill_flops([L], [L], long.Hq, long.D, True)
+            reps = max(3, min(50, int(2e12 / fl * 20)))
+
+            def call():
+                A.prefill_varlen(q[:L], k[:L], v[:L], cu, cu, L, L, causal=True, scale=long.scale,
+                                 out=out[:L], lse=lse[:L])
+            for _ in range(2):
+                call()
+            torch.cuda.synchronize()
+            A.timing_begin(reps + 4)
+            for _ in range(reps):
+                call()
+            kk = A.timing_end()
+            ms = kk["prefill"][0] / kk["prefill"][1]
+            sweep[str(L)] = {"kernel_ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                             "frac": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            log("bench: sweep", L, sweep[str(L)])
+        res["prefill_sweep"] = {"workload": workloads.CONFIG_NAMES[4], "by_length": sweep}
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(dec, args.cpu_seconds)
+
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(dec, seconds):
+    """The float64 oracle over the whole decode workload on the host cores,
+    repeated until at least ``seconds`` have passed; GB/s of algorithmic KV bytes."""
+    import torch
+    import oracle
+    torch.set_num_threads(os.cpu_count() or 1)
+    log("bench: cpu baseline (oracle)")
+    # The oracle only reads referenced pages, so the pool is left unfilled elsewhere.
+    shape = (dec.num_pages, dec.page_size, dec.Hkv, dec.D)
+    kp = torch.empty(shape, dtype=dec.dtype)
+    vp = torch.empty(shape, dtype=dec.dtype)
+    kp.view(-1, dec.Hkv, dec.D).index_copy_(0, dec.slot_index, dec.k_tok)
+    vp.view(-1, dec.Hkv, dec.D).index_copy_(0, dec.slot_index, dec.v_tok)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.ref_decode_paged(dec.q, kp, vp, dec.page_table, dec.kv_lens, dec.scale)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(dec.kv_bytes() * reps / dt / 1e9, 3), "unit": "GB/s",
+            "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": f"whole decode workload ({dec.B} requests) x {reps} repetitions, "
+                      f"{dt:.1f} s, float64 torch on CPU; os.cpu_count()={os.cpu_count()}",
+            "cpu_model": cpu_model}
+
+
+if __name__ == "__main__":
+    main()
