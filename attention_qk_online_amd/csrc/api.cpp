@@ -60,6 +60,9 @@ hipError_t timed(int kind, hipStream_t s, F&& fn) {
 // fraction of the KV bytes.
 constexpr int kUnitsTarget = 2048;
 constexpr int kMinSplitPages = 8;
+// The decode kernel keeps one wave's page ids in a single VGPR: 64 per wave,
+// 4 waves per workgroup.
+constexpr int kMaxSplitPages = 256;
 
 int auto_split_pages(int B, int Hkv, int max_pages) {
   if (max_pages <= 0) return kMinSplitPages;
@@ -82,6 +85,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int page_size, int max_kv_
   DecodePlan pl{};
   const int max_pages = page_size > 0 ? (max_kv_len + page_size - 1) / page_size : 0;
   pl.split_pages = split_pages > 0 ? split_pages : auto_split_pages(B, Hkv, max_pages);
+  if (pl.split_pages > kMaxSplitPages) pl.split_pages = kMaxSplitPages;
   pl.n_splits = max_pages > 0 ? (max_pages + pl.split_pages - 1) / pl.split_pages : 1;
   if (pl.n_splits < 1) pl.n_splits = 1;
   if (pl.n_splits == 1) return pl;

@@ -27,6 +27,10 @@ namespace {
 
 constexpr int kPage = 16;   // tokens per page handled by this kernel
 constexpr int kNW = 4;      // waves per workgroup
+#ifndef ATTN_DECODE_BATCH
+#define ATTN_DECODE_BATCH 2
+#endif
+constexpr int kBatch = ATTN_DECODE_BATCH;  // pages whose loads are issued together
 
 template <typename T, int D>
 struct Slice {
@@ -99,7 +103,7 @@ __device__ __forceinline__ int splits_of(int len, int split_pages) {
   return ns < 1 ? 1 : ns;
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, int NB>
 __global__ __launch_bounds__(kNW * 64) void decode_split_kernel(DecodeParams p) {
   using S = Slice<T, D>;
   constexpr int VPL = S::VPL;
@@ -135,63 +139,82 @@ __global__ __launch_bounds__(kNW * 64) void decode_split_kernel(DecodeParams p) 
   const size_t lane_off = (size_t)kvh * D + gl * VPL;
   const int32_t* table = p.page_table + (size_t)b * p.max_pages;
 
-  S kc[4], vc[4], kn[4], vn[4];
-  auto fetch = [&](int pg, S (&kk)[4], S (&vv)[4]) -> bool {
-    const int pid = table[pg];
-    if ((unsigned)pid >= (unsigned)p.num_pages) return false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t off = ((size_t)pid * kPage + grp * 4 + i) * row_stride + lane_off;
-      kk[i].load(kbase + off);
-      vv[i].load(vbase + off);
-    }
-    return true;
-  };
+  // Pages of this wave: first, first + NW, first + 2 NW, ...  A split holds
+  // at most 64 * NW pages, so all of this wave's page ids fit in one VGPR
+  // (lane j holds the j-th id) and are read before the loop; each page then
+  // takes its id with readlane, with no scalar load in front of its K/V loads.
+  const int first = pg_begin + wave;
+  const int n_w = first < pg_end ? (pg_end - first + kNW - 1) / kNW : 0;
+  const int ids = lane < n_w ? table[first + kNW * lane] : 0;
 
-  int pg = pg_begin + wave;
-  bool ok_cur = pg < pg_end ? fetch(pg, kc, vc) : true;
-  for (; pg < pg_end; pg += kNW) {
-    const int nxt = pg + kNW;
-    bool ok_nxt = true;
-    if (nxt < pg_end) ok_nxt = fetch(nxt, kn, vn);
-    if (!ok_cur) {
+  struct Buf {
+    S k[4], v[4];
+    bool ok;
+  };
+  // Loads are issued unconditionally (an id outside the pool is replaced by
+  // page 0 and the page is flagged) so that no branch separates a load from
+  // its use and the load counters stay exact across the rotation below.
+  auto fetch = [&](int i, Buf& bf) {
+    int pid = __builtin_amdgcn_readlane(ids, i);
+    bf.ok = (unsigned)pid < (unsigned)p.num_pages;
+    pid = bf.ok ? pid : 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const size_t off = ((size_t)pid * kPage + grp * 4 + t) * row_stride + lane_off;
+      bf.k[t].load(kbase + off);
+      bf.v[t].load(vbase + off);
+    }
+  };
+  auto compute = [&](int i, Buf& bf) {
+    if (!bf.ok) {
       bad = true;
-    } else {
-      const int tok0 = pg * kPage + grp * 4;
-      float s[4][G];
+      return;
+    }
+    const int tok0 = (first + kNW * i) * kPage + grp * 4;
+    float s[4][G];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool valid = tok0 + i < len;
-        if (!valid) vc[i].zero();   // poisoned tail slots must not reach o (0 * NaN)
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float d = row16_sum(kc[i].dot(qs[g])) * p.scale_log2;
-          s[i][g] = valid ? d : kNegInf;
-        }
-      }
+    for (int t = 0; t < 4; ++t) {
+      const bool valid = tok0 + t < len;
+      if (!valid) bf.v[t].zero();   // poisoned tail slots must not reach o (0 * NaN)
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float mb = fmaxf(fmaxf(s[0][g], s[1][g]), fmaxf(s[2][g], s[3][g]));
-        float mn = fmaxf(m[g], mb);
-        float mu = mn == kNegInf ? 0.f : mn;
-        float alpha = exp2_fast(m[g] - mu);
-        float pr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(s[i][g] - mu);
-        l[g] = l[g] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-#pragma unroll
-        for (int e = 0; e < VPL; ++e) {
-          float acc = o[g][e] * alpha;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc = __builtin_fmaf(pr[i], vc[i].elem(e), acc);
-          o[g][e] = acc;
-        }
-        m[g] = mn;
+        const float d = row16_sum(bf.k[t].dot(qs[g])) * p.scale_log2;
+        s[t][g] = valid ? d : kNegInf;
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { kc[i] = kn[i]; vc[i] = vn[i]; }
-    ok_cur = ok_nxt;
+    for (int g = 0; g < G; ++g) {
+      const float mb = fmaxf(fmaxf(s[0][g], s[1][g]), fmaxf(s[2][g], s[3][g]));
+      const float mn = fmaxf(m[g], mb);
+      const float mu = mn == kNegInf ? 0.f : mn;
+      const float alpha = exp2_fast(m[g] - mu);
+      float pr[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) pr[t] = exp2_fast(s[t][g] - mu);
+      l[g] = l[g] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) {
+        float acc = o[g][e] * alpha;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc = __builtin_fmaf(pr[t], bf.v[t].elem(e), acc);
+        o[g][e] = acc;
+      }
+      m[g] = mn;
+    }
+  };
+
+  // Pages go in batches of NB: all loads of a batch are issued first, then its
+  // pages are folded in order, so the next page's loads stay in flight while
+  // one page is computed.  Inside a batch the fetch index is clamped to the
+  // wave's last page (duplicate loads hit in cache and are never used).
+  Buf bufs[NB];
+  const int last = n_w - 1;
+  for (int i = 0; i < n_w; i += NB) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) fetch(min(i + j, last), bufs[j]);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (j == 0 || i + j < n_w) compute(i + j, bufs[j]);
   }
 
   // Merge the four 16-lane groups of the wave (lane ^ 16, then lane ^ 32).
@@ -289,7 +312,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
 template <typename T, int D, int G>
 hipError_t launch_split_t(const DecodeParams& p, hipStream_t s) {
   dim3 grid(p.n_splits, p.Hkv, p.B);
-  hipLaunchKernelGGL((decode_split_kernel<T, D, G>), grid, dim3(kNW * 64), 0, s, p);
+  hipLaunchKernelGGL((decode_split_kernel<T, D, G, kBatch>), grid, dim3(kNW * 64), 0, s, p);
   return hipGetLastError();
 }
 

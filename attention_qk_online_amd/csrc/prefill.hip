@@ -1,11 +1,14 @@
 // Ragged causal prefill for gfx950 on bf16 MFMA with fp32 accumulation.
 //
 // One workgroup = one (query tile of BM = 128 rows, query head) of one
-// sequence; four waves own 32 query rows each.  Per key tile of BN = 64:
-//   1. K[BN, D] and V^T[D, BN] are staged in LDS (V is transposed on the way
-//      in so both MFMA operands read contiguous k-slices); the next tile's
-//      global loads are issued into registers before the current tile is
-//      computed, so HBM latency hides behind MFMA work.
+// sequence; four waves own 32 query rows each, and two workgroups share a CU
+// so that one wave's matrix work overlaps another's softmax.  Per key tile
+// of BN keys (64 for head_dim 128, 32 for head_dim 256):
+//   1. The tile's K and V rows were fetched into registers during the
+//      previous tile and are written to one of two LDS stages (row-major,
+//      XOR-swizzled so the reads below hit every bank once); the next tile's
+//      global loads are issued right after, so HBM latency hides behind a
+//      whole tile of MFMA work.  One barrier per tile.
 //   2. S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: Q stays in VGPRs for the
 //      whole loop (B operand), K comes from LDS (A operand).  The transposed
 //      product puts one query per lane column, so a row max over keys is an
@@ -14,18 +17,19 @@
 //      the keys; online softmax in log2 units (running max m, running sum l,
 //      O rescaled by 2^(m_old - m_new) only when some row's max moved).
 //   4. O^T += V^T . P^T on MFMA: the S^T accumulator is already laid out as
-//      the B operand of this product (keys are permuted consistently on both
-//      operands), so P never leaves registers.
+//      the B operand (keys permuted identically on both operands), and V^T
+//      fragments come from the row-major V tile through ds_read_b64_tr_b16.
 // Tiles wholly above the causal diagonal are never loaded.  The score
 // matrix never reaches memory.
 //
 // This follows the tiled, fused scheme of "FlashAttention-3 内核在最新大模型
 // 推理中的集成实践" (section 一: Q/K/V blocks in on-chip memory, online softmax
-// accumulated in place; section 二: varlen packing by cu_seqlens, causal,
-// paged blocks; section 四: keep the rescaling, and keep tiles within the
-// on-chip budget for head_dim 256) and the three-stage QK^T / softmax / PV
-// pipeline of "FlashInfer Attention Kernel技术解析" section 1.3, re-tiled for
-// 64-wide waves, 32x32 MFMA tiles and a 160 KiB LDS.
+// accumulated in place, loads overlapped with tensor-core work by double
+// buffering; section 二: varlen packing by cu_seqlens, causal, paged blocks;
+// section 四: keep the rescaling, and keep tiles within the on-chip budget for
+// head_dim 256) and the three-stage QK^T / softmax / PV pipeline of "FlashInfer
+// Attention Kernel技术解析" section 1.3 (bank-conflict avoidance: section 4),
+// re-tiled for 64-wide waves, 32x32 MFMA tiles and a 160 KiB LDS.
 #include "common.h"
 #include "launch.h"
 
@@ -34,33 +38,53 @@ namespace attn {
 namespace {
 
 constexpr int BM = kPrefillBM;   // query rows per workgroup
-constexpr int BN = 64;           // keys per tile
 constexpr int NWAVE = 4;
 constexpr int NT = NWAVE * 64;
 constexpr int kPage = 16;
 
 template <int D>
 struct Cfg {
-  static constexpr int KSTR = D + 8;                 // K row stride in LDS (bf16), padded
-  static constexpr int VSTR = BN + 8;                // V^T row stride in LDS (bf16), padded
-  static constexpr int K_PER_THREAD = BN * D / 8 / NT;      // 16-byte chunks
-  static constexpr int V_PER_THREAD = (BN / 4) * (D / 4) / NT;  // 4x4 blocks
-  static constexpr int QK = D / 16;                  // MFMA k-steps over D
-  static constexpr int DB = D / 32;                  // 32-row blocks of D in O^T
-  static_assert(BN * D / 8 % NT == 0 && (BN / 4) * (D / 4) % NT == 0, "tile split");
-  static constexpr int LDS_BYTES = (BN * KSTR + D * VSTR) * 2;
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static constexpr int BN = D == 128 ? 64 : 32;      // keys per tile
+  static constexpr int ROWB = D * 2;                  // bytes of one K/V row
+  static constexpr int TILEB = BN * ROWB;             // bytes of one K or V tile
+  static constexpr int STAGEB = 2 * TILEB;            // K + V
+  static constexpr int CH = D / 8;                    // 16-byte chunks per row
+  static constexpr int LOADS = BN * CH / NT;          // 16-byte chunks per thread (K or V)
+  static constexpr int QK = D / 16;                   // MFMA k-steps over D
+  static constexpr int DB = D / 32;                   // 32-row blocks of D in O^T
+  static constexpr int KB = BN / 32;                  // 32-key blocks per tile
+  static constexpr int PS = BN / 16;                  // 16-key k-steps of P.V
+  static_assert(BN * CH % NT == 0, "tile split");
+  static_assert(2 * STAGEB <= 80 * 1024, "two workgroups per CU");
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Byte offset of 16-byte chunk `c` of K row `r` in a K tile: chunk index
+// XOR (r mod 16), so 16 consecutive rows read at the same logical chunk land
+// in 16 different 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int k_off(int r, int c) {
+  return r * Cfg<D>::ROWB + ((c ^ (r & 15)) << 4);
+}
+// Byte offset of 16-byte chunk `c` of V row `r`: its 64-byte block is XORed
+// with (r mod 4), so the four rows that one 16-lane group of a transposing
+// read touches fall in four different 64-byte bank groups.
+template <int D>
+__device__ __forceinline__ int v_off(int r, int c) {
+  return r * Cfg<D>::ROWB + ((((c >> 2) ^ (r & 3)) << 2 | (c & 3)) << 4);
+}
+
 template <int D, bool PAGED>
-__global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillParams p) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 sK[BN * C::KSTR];
-  __shared__ __attribute__((aligned(16))) __bf16 sVt[D * C::VSTR];
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -76,8 +100,8 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   const int tile = p.q_tiles - 1 - (int)blockIdx.z;   // heaviest causal tiles first
 
   // Sequence extents, clamped so every access stays inside the tensors.
-  int q_start = min(max(p.cu_q[b], 0), p.total_q);
-  int q_end = min(max(p.cu_q[b + 1], q_start), p.total_q);
+  const int q_start = min(max(p.cu_q[b], 0), p.total_q);
+  const int q_end = min(max(p.cu_q[b + 1], q_start), p.total_q);
   const int Lq = q_end - q_start;
   const int r0 = tile * BM;
   if (r0 >= Lq) return;
@@ -97,22 +121,23 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   const int r_last = min(r0 + BM, Lq) - 1;
   int kend = p.causal ? min(Lk, r_last + off + 1) : Lk;
   if (kend < 0) kend = 0;
-  const int n_kt = (kend + BN - 1) / BN;
+  const int n_kt = (kend + C::BN - 1) / C::BN;
 
   const __bf16* qg = reinterpret_cast<const __bf16*>(p.q);
-  const __bf16* kg = reinterpret_cast<const __bf16*>(p.k);
-  const __bf16* vg = reinterpret_cast<const __bf16*>(p.v);
-  const size_t kv_row = (size_t)p.Hkv * D;       // elements between consecutive tokens
+  const char* kg = reinterpret_cast<const char*>(p.k);
+  const char* vg = reinterpret_cast<const char*>(p.v);
+  const size_t kv_rowb = (size_t)p.Hkv * C::ROWB;      // bytes between consecutive tokens
 
-  // Address of key `kj` (0 <= kj < Lk) of this sequence for our KV head.
-  auto key_row = [&](int kj, bool& ok) -> size_t {
+  // Byte address of key `kj` (clamped into [0, Lk)) for our KV head.  Keys past
+  // the end reuse the last key's row: finite data that the mask zeroes out.
+  auto key_addr = [&](int kj) -> size_t {
+    kj = min(kj, Lk - 1);
     if constexpr (PAGED) {
-      const int pid = table[kj >> 4];
-      ok = (unsigned)pid < (unsigned)p.num_pages;
-      return ok ? (((size_t)pid * kPage + (kj & 15)) * kv_row + (size_t)kvh * D) : 0;
+      int pid = table[kj >> 4];
+      if ((unsigned)pid >= (unsigned)p.num_pages) { bad = true; pid = 0; }
+      return ((size_t)pid * kPage + (kj & 15)) * kv_rowb + (size_t)kvh * C::ROWB;
     } else {
-      ok = true;
-      return (size_t)(k_start + kj) * kv_row + (size_t)kvh * D;
+      return (size_t)(k_start + kj) * kv_rowb + (size_t)kvh * C::ROWB;
     }
   };
 
@@ -129,59 +154,27 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
     }
   }
 
-  // ---- register staging of the next K/V tile
-  u32x4 kreg[C::K_PER_THREAD];
-  u32x2 vreg[C::V_PER_THREAD][4];
+  // ---- register staging of one K/V tile: thread owns chunks tid + NT*i
+  u32x4 kreg[C::LOADS], vreg[C::LOADS];
   auto load_tile = [&](int k0) {
 #pragma unroll
-    for (int r = 0; r < C::K_PER_THREAD; ++r) {
-      const int c = tid + NT * r;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int kj = k0 + row;
-      bool ok = false;
-      size_t a = 0;
-      if (kj < Lk) a = key_row(kj, ok);
-      if (kj < Lk && !ok) bad = true;
-      kreg[r] = ok ? *reinterpret_cast<const u32x4*>(kg + a + col) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int r = 0; r < C::V_PER_THREAD; ++r) {
-      const int bi = tid + NT * r;
-      const int dg = bi % (D / 4), kgp = bi / (D / 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kj = k0 + kgp * 4 + i;
-        bool ok = false;
-        size_t a = 0;
-        if (kj < Lk) a = key_row(kj, ok);
-        if (kj < Lk && !ok) bad = true;
-        vreg[r][i] = ok ? *reinterpret_cast<const u32x2*>(vg + a + dg * 4) : u32x2{0u, 0u};
-      }
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int ci = tid + NT * i;
+      const int row = ci / C::CH, c = ci % C::CH;
+      const size_t a = key_addr(k0 + row) + c * 16;
+      kreg[i] = *reinterpret_cast<const u32x4*>(kg + a);
+      vreg[i] = *reinterpret_cast<const u32x4*>(vg + a);
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int stage) {
+    char* sk = smem + stage * C::STAGEB;
+    char* sv = sk + C::TILEB;
 #pragma unroll
-    for (int r = 0; r < C::K_PER_THREAD; ++r) {
-      const int c = tid + NT * r;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&sK[row * C::KSTR + col]) = kreg[r];
-    }
-#pragma unroll
-    for (int r = 0; r < C::V_PER_THREAD; ++r) {
-      const int bi = tid + NT * r;
-      const int dg = bi % (D / 4), kgp = bi / (D / 4);
-      // 4 keys x 4 dims -> 4 dims x 4 keys (bf16 transpose in registers)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int w = j >> 1;
-        const bool hi = j & 1;
-        uint32_t e0 = hi ? (vreg[r][0][w] >> 16) : (vreg[r][0][w] & 0xffffu);
-        uint32_t e1 = hi ? (vreg[r][1][w] >> 16) : (vreg[r][1][w] & 0xffffu);
-        uint32_t e2 = hi ? (vreg[r][2][w] >> 16) : (vreg[r][2][w] & 0xffffu);
-        uint32_t e3 = hi ? (vreg[r][3][w] >> 16) : (vreg[r][3][w] & 0xffffu);
-        u32x2 t = {e0 | (e1 << 16), e2 | (e3 << 16)};
-        *reinterpret_cast<u32x2*>(&sVt[(dg * 4 + j) * C::VSTR + kgp * 4]) = t;
-      }
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int ci = tid + NT * i;
+      const int row = ci / C::CH, c = ci % C::CH;
+      *reinterpret_cast<u32x4*>(sk + k_off<D>(row, c)) = kreg[i];
+      *reinterpret_cast<u32x4*>(sv + v_off<D>(row, c)) = vreg[i];
     }
   };
 
@@ -194,87 +187,104 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillParams p) {
   const int w_first = r0 + wave * 32;                       // first row of this wave
   const int w_last = min(w_first + 31, Lq - 1);
   const bool wave_rows = w_first < Lq;
+  const int pos = my_row + off;   // last visible key index for this lane's query
 
-  if (n_kt > 0) load_tile(0);
+  // transposing-read geometry: 16-lane group g = lane / 16
+  const int grp = lane >> 4, gj = lane & 15;
+  const int tr_row = 4 * (grp >> 1) + (gj >> 2);           // + 16 * ks (+ 8 for the high half)
+  const int tr_col = 16 * (grp & 1) + 4 * (gj & 3);        // d within the 32-wide block
+
+  if (n_kt > 0) {
+    load_tile(0);
+    store_tile(0);
+    if (n_kt > 1) load_tile(C::BN);
+  }
+  __syncthreads();
+
   for (int kt = 0; kt < n_kt; ++kt) {
-    const int k0 = kt * BN;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < n_kt) load_tile(k0 + BN);
-
+    const int k0 = kt * C::BN;
+    const char* sk = smem + (kt & 1) * C::STAGEB;
+    const char* sv = sk + C::TILEB;
     const bool wave_sees = wave_rows && (!p.causal || k0 <= w_last + off);
-    if (!wave_sees) continue;
 
-    f32x16 s[2];
+    if (wave_sees) {
+      // S^T = K Q^T
+      f32x16 s[C::KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const __bf16* kr = &sK[(kb * 32 + l32) * C::KSTR + hl * 8];
+      for (int kb = 0; kb < C::KB; ++kb) {
+        s[kb] = f32x16{};
+        const int r = kb * 32 + l32;
 #pragma unroll
-      for (int ks = 0; ks < C::QK; ++ks)
-        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kr + ks * 16), qf[ks], s[kb]);
-    }
-
-    // scale to log2 units, mask where needed
-    const bool need_mask = (k0 + BN > Lk) || (p.causal && k0 + BN - 1 > w_first + off);
-    const int pos = my_row + off;   // last visible key index for this lane's query
-    float t[2][16];
-    float mt = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = s[kb][r] * c;
-        if (need_mask) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key >= Lk || (p.causal && key > pos)) v = kNegInf;
-        }
-        t[kb][r] = v;
-        mt = fmaxf(mt, v);
+        for (int ks = 0; ks < C::QK; ++ks)
+          s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(sk + k_off<D>(r, ks * 2 + hl)), qf[ks], s[kb]);
       }
-    }
-    mt = max_halves(mt);
-    const float mn = fmaxf(m, mt);
-    const float mu = mn == kNegInf ? 0.f : mn;
-    const float alpha = exp2_fast(m - mu);
-    m = mn;
-    float psum = 0.f;
-    bf16x8 pb[4];
+
+      // scale to log2 units, mask where needed, running max
+      const bool need_mask = (k0 + C::BN > Lk) || (p.causal && k0 + C::BN - 1 > w_first + off);
+      float mt = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
+        for (int r = 0; r < 16; ++r) {
+          float v = s[kb][r] * c;
+          if (need_mask) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            if (key >= Lk || (p.causal && key > pos)) v = kNegInf;
+          }
+          s[kb][r] = v;
+          mt = fmaxf(mt, v);
+        }
+      }
+      mt = max_halves(mt);
+      const float mn = fmaxf(m, mt);
+      const float mu = mn == kNegInf ? 0.f : mn;
+      const float alpha = exp2_fast(m - mu);
+      m = mn;
+      float psum = 0.f;
+      bf16x8 pb[C::PS];
+#pragma unroll
+      for (int ps = 0; ps < C::PS; ++ps) {
         bf16x8 v;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pe = exp2_fast(t[kb][half * 8 + e] - mu);
+          const float pe = exp2_fast(s[ps >> 1][(ps & 1) * 8 + e] - mu);
           psum += pe;
           v[e] = (__bf16)pe;
         }
-        pb[kb * 2 + half] = v;
+        pb[ps] = v;
       }
-    }
-    lsum = lsum * alpha + psum;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+      lsum = lsum * alpha + psum;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
+        for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
+
+      // O^T += V^T P^T, V^T fragments through the transposing LDS read
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+        for (int ps = 0; ps < C::PS; ++ps) {
+          const int r = ps * 16 + tr_row;
+          const int d = db * 32 + tr_col;     // 4 consecutive d of one 16-byte chunk half
+          const int cl = d >> 3, cb = (d & 7) * 2;
+          v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)((lds_char*)sv + v_off<D>(r, cl) + cb));
+          v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)((lds_char*)sv + v_off<D>(r + 8, cl) + cb));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = mfma32(a, pb[ps], o[db]);
+        }
+      }
     }
 
-    // O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-      const __bf16* vr = &sVt[(db * 32 + l32) * C::VSTR + hl * 4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + ks * 16);
-        bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + ks * 16 + 8);
-        bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = mfma32(a, pb[ks], o[db]);
-      }
+    // stage the next tile and fetch the one after it
+    if (kt + 1 < n_kt) {
+      store_tile((kt + 1) & 1);
+      if (kt + 2 < n_kt) load_tile(k0 + 2 * C::BN);
     }
+    __syncthreads();
   }
 
   const bool any_bad = __syncthreads_or(bad);
