@@ -65,7 +65,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib = ctypes.CDLL(p)
     c_int, c_float, c_size, vp = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
     lib.attn_decode_paged_workspace_size.restype = c_size
-    lib.attn_decode_paged_workspace_size.argtypes = [c_int] * 7
+    lib.attn_decode_paged_workspace_size.argtypes = [c_int] * 8
     lib.attn_decode_paged.restype = c_int
     lib.attn_decode_paged.argtypes = [c_int, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int,
                                       c_int, c_int, c_int, c_int, c_float, vp, vp, vp, c_size, vp]
@@ -131,9 +131,10 @@ def _scale(scale: Optional[float], D: int) -> float:
     return s
 
 
-def decode_paged_workspace_size(B: int, Hq: int, Hkv: int, D: int, page_size: int,
-                                max_kv_len: int, split_pages: int = 0) -> int:
-    return int(load_library().attn_decode_paged_workspace_size(B, Hq, Hkv, D, page_size,
+def decode_paged_workspace_size(dtype: torch.dtype, B: int, Hq: int, Hkv: int, D: int,
+                                page_size: int, max_kv_len: int, split_pages: int = 0) -> int:
+    code = ATTN_F32 if dtype == torch.float32 else ATTN_BF16
+    return int(load_library().attn_decode_paged_workspace_size(code, B, Hq, Hkv, D, page_size,
                                                                max_kv_len, split_pages))
 
 
@@ -174,7 +175,7 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
     _dev(lse, "lse", torch.float32, 2)
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq):
         raise ValueError("out/lse have the wrong shape")
-    ws_bytes = int(lib.attn_decode_paged_workspace_size(B, Hq, Hkv, D, page_size, max_kv_len,
+    ws_bytes = int(lib.attn_decode_paged_workspace_size(dt, B, Hq, Hkv, D, page_size, max_kv_len,
                                                         split_pages))
     if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)

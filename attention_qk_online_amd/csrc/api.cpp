@@ -75,15 +75,34 @@ int auto_split_pages(int B, int Hkv, int max_pages) {
 }
 
 struct DecodePlan {
-  int split_pages, n_splits;
+  int split_pages, n_splits;   // fp32 split grid
+  int min_run, max_segs;       // bf16 balanced runs
   size_t part_o_elems, part_lse_elems;
-  size_t bytes;  // 0 when no request can have more than one split
+  size_t bytes;                // workspace bytes (0: none needed)
 };
 
-DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int page_size, int max_kv_len,
+// Smallest run of the balanced bf16 schedule when the caller leaves the run
+// length to the library: partial states stay well below the KV bytes.
+constexpr int kMinRun = 8;
+
+size_t aligned_bytes(size_t floats) { return (floats * sizeof(float) + 255) & ~(size_t)255; }
+
+DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int D, int page_size, int max_kv_len,
                        int split_pages) {
   DecodePlan pl{};
   const int max_pages = page_size > 0 ? (max_kv_len + page_size - 1) / page_size : 0;
+  if (dtype == ATTN_BF16) {
+    // A (request, KV head) pair of at most max_pages units spans at most
+    // ceil(max_pages / run) + 1 runs, and every run has >= min_run units.
+    pl.split_pages = split_pages;
+    pl.min_run = split_pages > 0 ? split_pages : kMinRun;
+    pl.max_segs = (max_pages + pl.min_run - 1) / pl.min_run + 1;
+    const size_t slots = (size_t)B * Hkv * pl.max_segs * (Hq / (Hkv > 0 ? Hkv : 1));
+    pl.part_o_elems = slots * D;
+    pl.part_lse_elems = slots;
+    pl.bytes = aligned_bytes(pl.part_o_elems) + aligned_bytes(pl.part_lse_elems);
+    return pl;
+  }
   pl.split_pages = split_pages > 0 ? split_pages : auto_split_pages(B, Hkv, max_pages);
   if (pl.split_pages > kMaxSplitPages) pl.split_pages = kMaxSplitPages;
   pl.n_splits = max_pages > 0 ? (max_pages + pl.split_pages - 1) / pl.split_pages : 1;
@@ -91,11 +110,21 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D, int page_size, int max_kv_
   if (pl.n_splits == 1) return pl;
   pl.part_o_elems = (size_t)B * pl.n_splits * Hq * D;
   pl.part_lse_elems = (size_t)B * pl.n_splits * Hq;
-  // part_o first, then part_lse, each 256-byte aligned
-  size_t o_bytes = (pl.part_o_elems * sizeof(float) + 255) & ~(size_t)255;
-  size_t l_bytes = (pl.part_lse_elems * sizeof(float) + 255) & ~(size_t)255;
-  pl.bytes = o_bytes + l_bytes;
+  pl.bytes = aligned_bytes(pl.part_o_elems) + aligned_bytes(pl.part_lse_elems);
   return pl;
+}
+
+// Compute units of the current device (cached per device id).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev] = n;
+  return n;
 }
 
 bool dtype_ok(attn_dtype d) { return d == ATTN_F32 || d == ATTN_BF16; }
@@ -130,12 +159,12 @@ const char* attn_kernel_name(attn_kernel_kind kind) {
   }
 }
 
-size_t attn_decode_paged_workspace_size(int B, int Hq, int Hkv, int D, int page_size,
-                                        int max_kv_len, int split_pages) {
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || max_kv_len < 0 ||
-      split_pages < 0)
+size_t attn_decode_paged_workspace_size(attn_dtype dtype, int B, int Hq, int Hkv, int D,
+                                        int page_size, int max_kv_len, int split_pages) {
+  if (!dtype_ok(dtype) || B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 ||
+      max_kv_len < 0 || split_pages < 0 || Hq % Hkv != 0)
     return 0;
-  return plan_decode(B, Hq, Hkv, D, page_size, max_kv_len, split_pages).bytes;
+  return plan_decode((int)dtype, B, Hq, Hkv, D, page_size, max_kv_len, split_pages).bytes;
 }
 
 attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pages,
@@ -167,7 +196,7 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pag
     return fail(ATTN_E_NULL, "a required pointer is NULL");
   if (num_pages == 0 && max_kv_len > 0)
     return fail(ATTN_E_SHAPE, "num_pages is 0 but max_kv_len=%d", max_kv_len);
-  const DecodePlan pl = plan_decode(B, Hq, Hkv, D, page_size, max_kv_len, split_pages);
+  const DecodePlan pl = plan_decode((int)dtype, B, Hq, Hkv, D, page_size, max_kv_len, split_pages);
   if (pl.bytes > 0 && (!workspace || workspace_bytes < pl.bytes))
     return fail(ATTN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.bytes,
                 workspace ? workspace_bytes : (size_t)0);
@@ -185,6 +214,12 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pag
   }
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.num_pages = num_pages; p.max_pages = max_pages_per_req;
   p.max_kv_len = max_kv_len; p.split_pages = pl.split_pages; p.n_splits = pl.n_splits;
+  p.min_run = pl.min_run; p.max_segs = pl.max_segs;
+  // Balanced bf16 grid: one wave per KV head of a group of up to 8 heads,
+  // kDecodeGroupsPerCU workgroups per compute unit.
+  p.hw = Hkv < 8 ? Hkv : 8;
+  p.nhg = (Hkv + p.hw - 1) / p.hw;
+  p.n_groups = attn::kDecodeGroupsPerCU * device_cus();
   p.scale_log2 = scale * kLog2e;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -192,9 +227,9 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pag
                        [&] { return attn::launch_decode_split(p, (int)dtype, D, G, s); });
   if (e != hipSuccess)
     return fail(ATTN_E_HIP, "decode_split launch: %s", hipGetErrorString(e));
-  if (pl.n_splits > 1) {
+  if (dtype == ATTN_BF16 || pl.n_splits > 1) {
     e = timed(ATTN_KERNEL_DECODE_COMBINE, s,
-              [&] { return attn::launch_decode_combine(p, (int)dtype, D, s); });
+              [&] { return attn::launch_decode_combine(p, (int)dtype, D, G, s); });
     if (e != hipSuccess)
       return fail(ATTN_E_HIP, "decode_combine launch: %s", hipGetErrorString(e));
   }

@@ -26,11 +26,16 @@ namespace attn {
 namespace {
 
 constexpr int kPage = 16;   // tokens per page handled by this kernel
-constexpr int kNW = 4;      // waves per workgroup
+constexpr int kNW = 4;      // waves per workgroup (fp32 split kernel)
+constexpr int kMaxGroupWaves = 8;  // KV heads per workgroup (bf16 balanced kernel)
 #ifndef ATTN_DECODE_BATCH
 #define ATTN_DECODE_BATCH 2
 #endif
 constexpr int kBatch = ATTN_DECODE_BATCH;  // pages whose loads are issued together
+#ifndef ATTN_DECODE_MFMA_BATCH
+#define ATTN_DECODE_MFMA_BATCH 1
+#endif
+constexpr int kMfmaBatch = ATTN_DECODE_MFMA_BATCH;
 
 template <typename T, int D>
 struct Slice {
@@ -277,6 +282,384 @@ __global__ __launch_bounds__(kNW * 64) void decode_split_kernel(DecodeParams p) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 decode on the matrix cores with a balanced schedule.
+//
+// Schedule: the (request, KV head, page) units of the whole batch are laid
+// out request by request, KV head by KV head, and cut into equal runs, one
+// per wave of the grid, so every wave streams the same number of KV bytes
+// whatever the spread of request lengths ("FlashInfer内核库深度解析": batched
+// kernels balance load by sequence length; "FlashInfer Attention Kernel技术
+// 解析" section 2.2: schedule by length).  The cut is computed on the device
+// from kv_lens, so the host needs no copy of the lengths.  A run that covers a
+// whole (request, KV head) pair writes the final output; otherwise each run
+// writes a partial (o, lse) and decode_merge_kernel combines them.
+//
+// Per 16-token page, on the matrix cores:
+//   S^T[16 tokens x 16 head slots] = K_page . Q^T  (v_mfma_f32_16x16x32_bf16;
+//        A operand read straight from HBM, 16 bytes per lane; the G query
+//        heads of the KV head fill the first G of the 16 columns)
+//   online softmax per column (each lane owns one head and four tokens)
+//   O^T[16 d x 16 heads] += V^T . P^T            (v_mfma_f32_16x16x16_bf16;
+//        V rows go through a per-wave LDS buffer and come back as V^T
+//        fragments via ds_read_b64_tr_b16; P^T is the S^T accumulator as is)
+// so per page only a few dozen vector instructions remain and the kernel is
+// bound by HBM.  Pages are loaded in batches of NB per wave.
+template <int D>
+struct MfmaDecodeCfg {
+  static constexpr int KS = D / 32;          // 16x16x32 k-steps for Q.K
+  static constexpr int CHV = D / 8;          // 16-byte chunks per V row
+  static constexpr int LV = 16 * CHV / 64;   // V chunks per lane per page
+  static constexpr int DB = D / 16;          // 16-row blocks of O^T
+  static constexpr int ROWB = D * 2;         // bytes per V row in LDS
+  static constexpr int UMASK = (D / 16 < 8 ? D / 16 : 8) - 1;  // swizzle of 32-byte units
+  static constexpr int PAGEB = 16 * ROWB;    // LDS bytes of one page of V
+};
+
+// Byte offset in a page's V buffer of d-element `d` (multiple of 4) of row t:
+// 32-byte units XOR (t mod 8) so the 16 rows of a transposing read spread over banks.
+template <int D>
+__device__ __forceinline__ int vpage_off(int t, int d) {
+  using C = MfmaDecodeCfg<D>;
+  return t * C::ROWB + ((((d >> 4) ^ (t & C::UMASK)) << 5) | ((d & 15) << 1));
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ int pages_of(const DecodeParams& p, int b) {
+  bool bad;
+  const int len = request_len(p, b, bad);
+  return (len + kPage - 1) / kPage;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Units (pages x KV-head groups) of the whole batch.
+__device__ __forceinline__ int total_units(const DecodeParams& p) {
+  int tot = 0;
+  for (int c = 0; c < p.B; c += 64) {
+    const int b = c + __lane_id();
+    const int u = b < p.B ? pages_of(p, b) * p.nhg : 0;
+    tot += __builtin_amdgcn_readlane(wave_incl_scan(u), 63);
+  }
+  return tot;
+}
+
+__device__ __forceinline__ int run_length(const DecodeParams& p, int units) {
+  if (p.split_pages > 0) return p.split_pages;
+  const int w = (units + p.n_groups - 1) / p.n_groups;
+  return w > p.min_run ? w : p.min_run;
+}
+
+// Per-wave LDS buffer for one page of V rows.
+template <int D>
+__device__ __forceinline__ char* decode_vbuf(int wave) {
+  __shared__ __attribute__((aligned(16))) char vbuf[kMaxGroupWaves][MfmaDecodeCfg<D>::PAGEB];
+  return vbuf[wave];
+}
+
+// One run [u0, u1) of the balanced schedule.  A unit is one page of one
+// group of hw KV heads; wave w of the workgroup folds KV head hg * hw + w of
+// every unit, so a workgroup reads whole pages (all heads of a token are
+// adjacent in the NHD layout).
+template <int D, int G, int NB>
+__device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1, int W, int lane,
+                                           int wave) {
+  using C = MfmaDecodeCfg<D>;
+  const int l16 = lane & 15, gq = lane >> 4;
+  // Request holding unit u0 (scan of units per request, 64 requests at a time).
+  int b = 0, start_b = 0;
+  for (int c = 0, cum = 0; c < p.B; c += 64) {
+    const int bb = c + lane;
+    const int u = bb < p.B ? pages_of(p, bb) * p.nhg : 0;
+    const int incl = wave_incl_scan(u);
+    const int tot = __builtin_amdgcn_readlane(incl, 63);
+    if (cum + tot > u0) {
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(cum + incl > u0);
+      const int j = __builtin_ctzll(hit);
+      b = c + j;
+      start_b = cum + __builtin_amdgcn_readlane(incl, j) - __builtin_amdgcn_readlane(u, j);
+      break;
+    }
+    cum += tot;
+  }
+  int np = pages_of(p, b);
+
+  char* myv = decode_vbuf<D>(wave);
+  const char* kbase = reinterpret_cast<const char*>(p.k_pages);
+  const char* vbase = reinterpret_cast<const char*>(p.v_pages);
+  const size_t tok_b = (size_t)p.Hkv * C::ROWB;           // bytes between tokens
+  const float c = p.scale_log2;
+  const float qnan = __builtin_nanf("");
+
+  struct Page {
+    u32x4 k[C::KS], v[C::LV];
+    bool ok;
+  };
+
+  int u = u0;
+  while (u < u1) {
+    while (u >= start_b + p.nhg * np) {       // next request with units
+      start_b += p.nhg * np;
+      ++b;
+      np = pages_of(p, b);
+    }
+    const int r = u - start_b;
+    const int hg = r / np, pg0 = r % np;
+    const int start_pair = start_b + hg * np;
+    const int n = min(u1, start_pair + np) - u;        // pages of this piece
+    const int kvh = hg * p.hw + wave;
+    if (kvh >= p.Hkv) {                                // idle wave of a partial head group
+      u += n;
+      continue;
+    }
+    const bool whole = start_pair / W == (start_pair + np - 1) / W;
+    const int len = min(p.kv_lens[b], np * kPage);     // valid tokens (clamped, >= 1 page)
+
+    // Q^T fragments: lane (head l16, k-group gq) holds q[head][32 ks + 8 gq .. +8].
+    bf16x8 qf[C::KS];
+    {
+      const __bf16* qh = reinterpret_cast<const __bf16*>(p.q) +
+                         ((size_t)b * p.Hq + (size_t)kvh * G + (l16 < G ? l16 : 0)) * D + 8 * gq;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(qh + 32 * ks);
+        qf[ks] = l16 < G ? v : bf16x8{};
+      }
+    }
+    f32x4 o[C::DB];
+#pragma unroll
+    for (int i = 0; i < C::DB; ++i) o[i] = f32x4{};
+    float m = kNegInf, lsum = 0.f;
+    bool bad = false;
+    const char* kh = kbase + (size_t)kvh * C::ROWB;
+    const char* vh = vbase + (size_t)kvh * C::ROWB;
+    const int32_t* table = p.page_table + (size_t)b * p.max_pages + pg0;
+
+    for (int c0 = 0; c0 < n; c0 += 64) {
+      const int nc = min(64, n - c0);
+      const int ids = lane < nc ? table[c0 + lane] : 0;
+      auto fetch = [&](int i, Page& pg) {
+        int pid = __builtin_amdgcn_readlane(ids, i);
+        pg.ok = (unsigned)pid < (unsigned)p.num_pages;
+        pid = pg.ok ? pid : 0;
+        const char* kp = kh + (size_t)pid * kPage * tok_b;
+        const char* vp = vh + (size_t)pid * kPage * tok_b;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+          pg.k[ks] = *reinterpret_cast<const u32x4*>(kp + l16 * tok_b + (32 * ks + 8 * gq) * 2);
+#pragma unroll
+        for (int j = 0; j < C::LV; ++j) {
+          const int ci = lane + 64 * j;
+          pg.v[j] = *reinterpret_cast<const u32x4*>(vp + (ci / C::CHV) * tok_b + (ci % C::CHV) * 16);
+        }
+      };
+      auto fold = [&](int i, Page& pg) {
+        if (!pg.ok) {
+          bad = true;
+          return;
+        }
+        const int nval = len - (pg0 + c0 + i) * kPage;   // valid tokens in this page
+        // V rows to LDS (rows past the end zeroed: poisoned slots must not reach O)
+#pragma unroll
+        for (int j = 0; j < C::LV; ++j) {
+          const int ci = lane + 64 * j;
+          const int t = ci / C::CHV, ch = ci % C::CHV;
+          const u32x4 v = t < nval ? pg.v[j] : u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(myv + vpage_off<D>(t, ch * 8)) = v;
+        }
+        f32x4 s = {};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pg.k[ks]), qf[ks],
+                                                      s, 0, 0, 0);
+        float mx = kNegInf;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float v = 4 * gq + rr < nval ? s[rr] * c : kNegInf;
+          s[rr] = v;
+          mx = fmaxf(mx, v);
+        }
+        mx = max_halves(fmaxf(mx, shfl_xor_f32(mx, 16)));
+        const float mn = fmaxf(m, mx);
+        const float mu = mn == kNegInf ? 0.f : mn;
+        const float alpha = exp2_fast(m - mu);
+        m = mn;
+        bf16x4 pb;
+        float ps = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float e = exp2_fast(s[rr] - mu);
+          ps += e;
+          pb[rr] = (__bf16)e;
+        }
+        lsum = lsum * alpha + ps;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) o[db][rr] *= alpha;
+        }
+        const int t_rd = 4 * gq + (l16 >> 2);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)((lds_char*)myv + vpage_off<D>(t_rd, db * 16 + 4 * (l16 & 3))));
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a), pb,
+                                                            o[db], 0, 0, 0);
+        }
+      };
+      Page bufs[NB];
+      const int last = nc - 1;
+      for (int i = 0; i < nc; i += NB) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) fetch(min(i + j, last), bufs[j]);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          if (j == 0 || i + j < nc) fold(i + j, bufs[j]);
+      }
+    }
+
+    // Finish the piece: lane (head l16, group gq) holds d = 16 db + 4 gq + rr.
+    const float ltot = sum_halves(lsum + shfl_xor_f32(lsum, 16));
+    float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    float lse_nat = ltot > 0.f ? (m + log2_fast(ltot)) * kLn2 : kNegInf;
+    if (bad) { inv = qnan; lse_nat = qnan; }
+    if (l16 < G) {
+      const int h = kvh * G + l16;
+      if (whole) {
+        __bf16* og = reinterpret_cast<__bf16*>(p.out) + ((size_t)b * p.Hq + h) * D + 4 * gq;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          bf16x4 v;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) v[rr] = (__bf16)(o[db][rr] * inv);
+          *reinterpret_cast<bf16x4*>(og + 16 * db) = v;
+        }
+        if (gq == 0) p.lse[(size_t)b * p.Hq + h] = lse_nat;
+      } else {
+        const size_t slot = ((size_t)b * p.Hkv + kvh) * p.max_segs + (u / W - start_pair / W);
+        float* po = p.part_o + (slot * G + l16) * D + 4 * gq;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          f32x4 v;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) v[rr] = o[db][rr] * inv;
+          *reinterpret_cast<f32x4*>(po + 16 * db) = v;
+        }
+        if (gq == 0) p.part_lse[slot * G + l16] = lse_nat;
+      }
+    }
+    u += n;
+  }
+}
+
+template <int D, int G, int NB>
+__global__ __launch_bounds__(kMaxGroupWaves * 64, D == 256 ? 1 : 2) void decode_mfma_kernel(DecodeParams p) {
+  static_assert(G >= 1 && G <= 16, "one 16-column MFMA tile holds the query heads");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  const int U = total_units(p);
+  const int W = run_length(p, U);
+  for (int run = blockIdx.x; (long)run * W < U; run += gridDim.x) {
+    decode_run<D, G, NB>(p, run * W, min(run * W + W, U), W, lane, wave);
+  }
+}
+
+// Merge of the balanced runs: one workgroup per (KV head, request) and one
+// wave per query head of the group; lanes own d.  Pairs held by a single run
+// were written by that run; empty requests get out 0 and lse -inf and
+// inconsistent ones NaN.
+template <int D, int G>
+__global__ __launch_bounds__(G * 64) void decode_merge_kernel(DecodeParams p) {
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int U = 0, pre = 0;
+  for (int c = 0; c < p.B; c += 64) {
+    const int bb = c + lane;
+    const int u = bb < p.B ? pages_of(p, bb) * p.nhg : 0;
+    U += __builtin_amdgcn_readlane(wave_incl_scan(u), 63);
+    pre += __builtin_amdgcn_readlane(wave_incl_scan(bb < b ? u : 0), 63);
+  }
+  const int W = run_length(p, U);
+  bool bad;
+  request_len(p, b, bad);
+  const int np = pages_of(p, b);
+  const int start_pair = pre + (kvh / p.hw) * np;
+  const int nseg = np > 0 ? (start_pair + np - 1) / W - start_pair / W + 1 : 0;
+  if (nseg == 1) return;
+  const int h = kvh * G + g;
+  bf16_t* og = reinterpret_cast<bf16_t*>(p.out) + ((size_t)b * p.Hq + h) * D;
+  if (bad || nseg == 0) {
+    const float val = bad ? __builtin_nanf("") : 0.f;
+    for (int d = lane; d < D; d += 64) store_out(og + d, val);
+    if (lane == 0) p.lse[(size_t)b * p.Hq + h] = bad ? val : kNegInf;
+    return;
+  }
+  const size_t slot0 = ((size_t)b * p.Hkv + kvh) * p.max_segs;
+  const float* pl = p.part_lse + slot0 * G + g;           // stride G between segments
+  const float* po = p.part_o + (slot0 * G + g) * D;       // stride G*D between segments
+  constexpr int DL = D / 64 > 0 ? D / 64 : 1;
+  float acc[DL] = {};
+  float mx = kNegInf, ws = 0.f;
+  bool nan_seen = false;
+  // Segments in chunks of 64: lane j holds segment j's lse and weight, then
+  // the partial outputs are read eight segments at a time.
+  for (int j0 = 0; j0 < nseg; j0 += 64) {
+    const int nj = min(64, nseg - j0);
+    const float ls = lane < nj ? pl[(size_t)(j0 + lane) * G] : kNegInf;
+    nan_seen |= __builtin_amdgcn_ballot_w64(ls != ls) != 0;
+    float cm = ls;
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) cm = fmaxf(cm, shfl_xor_f32(cm, sh));
+    const float mnew = fmaxf(mx, cm);
+    const float mu = mnew == kNegInf ? 0.f : mnew;
+    const float resc = exp2_fast((mx - mu) * kLog2e);
+    float w = lane < nj ? exp2_fast((ls - mu) * kLog2e) : 0.f;
+    float wsum = w;
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) wsum += shfl_xor_f32(wsum, sh);
+    ws = ws * resc + wsum;
+#pragma unroll
+    for (int i = 0; i < DL; ++i) acc[i] *= resc;
+    mx = mnew;
+    for (int j = 0; j < nj; j += 8) {
+      float v[8][DL];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < DL; ++i)
+          v[t][i] = (j + t < nj && lane + 64 * i < D) ? po[(size_t)(j0 + j + t) * G * D + lane + 64 * i] : 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float wt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), min(j + t, 63)));
+#pragma unroll
+        for (int i = 0; i < DL; ++i) acc[i] += (j + t < nj ? wt : 0.f) * v[t][i];
+      }
+    }
+  }
+  const float mu = mx == kNegInf ? 0.f : mx;
+  const float inv = ws > 0.f ? 1.f / ws : 0.f;
+  float lse_nat = ws > 0.f ? mu + log2_fast(ws) * kLn2 : kNegInf;
+  if (nan_seen) lse_nat = __builtin_nanf("");
+#pragma unroll
+  for (int i = 0; i < DL; ++i)
+    if (lane + 64 * i < D) store_out(og + lane + 64 * i, nan_seen ? lse_nat : acc[i] * inv);
+  if (lane == 0) p.lse[(size_t)b * p.Hq + h] = lse_nat;
+}
+
 // One thread per (head, d); requests with a single split were finished above.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
@@ -311,8 +694,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
 
 template <typename T, int D, int G>
 hipError_t launch_split_t(const DecodeParams& p, hipStream_t s) {
-  dim3 grid(p.n_splits, p.Hkv, p.B);
-  hipLaunchKernelGGL((decode_split_kernel<T, D, G, kBatch>), grid, dim3(kNW * 64), 0, s, p);
+  if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL((decode_mfma_kernel<D, G, (D == 256 ? 1 : kMfmaBatch)>),
+                       dim3(p.n_groups), dim3(p.hw * 64), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<T, D, G, kBatch>), dim3(p.n_splits, p.Hkv, p.B),
+                       dim3(kNW * 64), 0, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -347,16 +735,17 @@ hipError_t launch_combine_t(const DecodeParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_combine_d(const DecodeParams& p, int D, hipStream_t s) {
-  switch (D) {
-    case 64: return launch_combine_t<T, 64>(p, s);
-    case 128: return launch_combine_t<T, 128>(p, s);
-    case 256:
-      if constexpr (sizeof(T) == 2) return launch_combine_t<T, 256>(p, s);
-      break;
+template <int D>
+hipError_t launch_merge_g(const DecodeParams& p, int G, hipStream_t s) {
+  dim3 grid(p.Hkv, p.B);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((decode_merge_kernel<D, 1>), grid, dim3(64), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((decode_merge_kernel<D, 2>), grid, dim3(128), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((decode_merge_kernel<D, 4>), grid, dim3(256), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((decode_merge_kernel<D, 8>), grid, dim3(512), 0, s, p); break;
+    default: return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -371,8 +760,16 @@ hipError_t launch_decode_split(const DecodeParams& p, int dtype, int D, int G, h
   return dtype == 0 ? launch_split_d<float>(p, D, G, s) : launch_split_d<bf16_t>(p, D, G, s);
 }
 
-hipError_t launch_decode_combine(const DecodeParams& p, int dtype, int D, hipStream_t s) {
-  return dtype == 0 ? launch_combine_d<float>(p, D, s) : launch_combine_d<bf16_t>(p, D, s);
+hipError_t launch_decode_combine(const DecodeParams& p, int dtype, int D, int G, hipStream_t s) {
+  if (dtype == 0) {
+    if (D == 64) return launch_combine_t<float, 64>(p, s);
+    if (D == 128) return launch_combine_t<float, 128>(p, s);
+    return hipErrorInvalidValue;
+  }
+  if (D == 64) return launch_merge_g<64>(p, G, s);
+  if (D == 128) return launch_merge_g<128>(p, G, s);
+  if (D == 256) return launch_merge_g<256>(p, G, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace attn

@@ -16,9 +16,20 @@ struct DecodeParams {
   const int32_t* kv_lens;     // [B]
   void* out;               // [B, Hq, D]
   float* lse;              // [B, Hq]
-  float* part_o;           // [B, n_splits, Hq, D]   (workspace)
-  float* part_lse;         // [B, n_splits, Hq]      (workspace)
-  int B, Hq, Hkv, num_pages, max_pages, max_kv_len, split_pages, n_splits;
+  float* part_o;           // workspace: partial outputs (layout per kernel below)
+  float* part_lse;         // workspace: partial log-sum-exp
+  int B, Hq, Hkv, num_pages, max_pages, max_kv_len, split_pages;
+  // fp32 split grid: n_splits splits of split_pages pages per request,
+  //   part_o [B, n_splits, Hq, D], part_lse [B, n_splits, Hq].
+  int n_splits;
+  // bf16 balanced schedule: KV heads form nhg groups of hw heads (one wave
+  //   each); the (request, head group, page) units are cut into equal runs,
+  //   one per workgroup (n_groups in the grid, looping when runs outnumber
+  //   them); a run has split_pages units when split_pages > 0, else
+  //   max(min_run, ceil(units / n_groups)).  A (request, head group) pair
+  //   spans at most max_segs runs;
+  //   part_o [B, Hkv, max_segs, G, D], part_lse [B, Hkv, max_segs, G].
+  int hw, nhg, n_groups, min_run, max_segs;
   float scale_log2;        // softmax scale * log2(e)
 };
 
@@ -42,7 +53,12 @@ struct PrefillParams {
 // dtype: 0 = f32, 1 = bf16 (values of attn_dtype).
 bool decode_supported(int dtype, int D, int G, int page_size);
 hipError_t launch_decode_split(const DecodeParams& p, int dtype, int D, int G, hipStream_t s);
-hipError_t launch_decode_combine(const DecodeParams& p, int dtype, int D, hipStream_t s);
+hipError_t launch_decode_combine(const DecodeParams& p, int dtype, int D, int G, hipStream_t s);
+// Workgroups (of up to 8 waves, one per KV head) per CU in the balanced bf16 grid.
+#ifndef ATTN_DECODE_GROUPS_PER_CU
+#define ATTN_DECODE_GROUPS_PER_CU 1
+#endif
+constexpr int kDecodeGroupsPerCU = ATTN_DECODE_GROUPS_PER_CU;
 
 // Query rows per workgroup of the prefill kernels (grid sizing on the host).
 constexpr int kPrefillBM = 128;

@@ -220,21 +220,26 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillPa
       }
 
       // scale to log2 units, mask where needed, running max
-      const bool need_mask = (k0 + C::BN > Lk) || (p.causal && k0 + C::BN - 1 > w_first + off);
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] *= c;
+      if (k0 + C::BN > Lk || (p.causal && k0 + C::BN - 1 > w_first + off)) {
+        // keys past the end or above the diagonal; lim = last visible key
+        const int lim = p.causal ? min(pos, Lk - 1) : Lk - 1;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            s[kb][r] = key > lim ? kNegInf : s[kb][r];
+          }
+      }
       float mt = kNegInf;
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = s[kb][r] * c;
-          if (need_mask) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (key >= Lk || (p.causal && key > pos)) v = kNegInf;
-          }
-          s[kb][r] = v;
-          mt = fmaxf(mt, v);
-        }
-      }
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
       mt = max_halves(mt);
       const float mn = fmaxf(m, mt);
       const float mu = mn == kNegInf ? 0.f : mn;

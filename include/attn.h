@@ -75,22 +75,28 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
 /* Batched decode over a paged KV cache.
  *
  * One query token per request attends to that request's kv_len cached tokens
- * (no mask).  The keys of a request are cut into splits of `split_pages`
- * pages; each (request, KV head, split) is one work item that streams its
- * K/V pages with 128-bit loads and keeps G = Hq/Hkv query heads in registers.
- * Splits are merged by their log-sum-exp in a second kernel (only requests
- * with more than one split touch the workspace).  Pages, page tables and
+ * (no mask).  The G = Hq/Hkv query heads that share a KV head are processed
+ * together, so every K/V byte is read from HBM once.  Pages, page tables and
  * per-request lengths follow "FlashInfer内核库深度解析" (PageAttention:
  * fixed-size pages addressed through a table) and "FlashAttention-3 ..."
  * section 二 (physical block addressing in continuous batching).
+ *
+ * bf16: the (request, KV head, page) units of the batch are cut into equal
+ * runs, one per wave, computed on the device from kv_lens (balanced over
+ * ragged lengths); Q.K^T and P.V run on the matrix cores.  Runs that cover
+ * only part of a (request, KV head) pair leave partial (o, lse) states in the
+ * workspace, merged by their log-sum-exp in a second kernel.  split_pages,
+ * when > 0, fixes the run length (in pages); 0 lets the library choose.
+ * fp32: each request is cut into splits of split_pages pages (0: default);
+ * one work item per (request, KV head, split), merged the same way.
  *
  *  q           [B, Hq, D]                   dtype
  *  k_pages     [num_pages, page_size, Hkv, D] dtype
  *  v_pages     [num_pages, page_size, Hkv, D] dtype
  *  page_table  [B, max_pages_per_req]       int32
  *  kv_lens     [B]                          int32, 0 <= kv_len <= max_kv_len
- *  max_kv_len  host int: an upper bound of every kv_len (sizes the grid)
- *  split_pages host int: pages per split; 0 picks a default from the sizes
+ *  max_kv_len  host int: an upper bound of every kv_len (sizes the plan)
+ *  split_pages host int: run / split length in pages; 0 picks a default
  *  scale       finite float (the caller's softmax scale, usually 1/sqrt(D))
  *  out         [B, Hq, D]                   dtype
  *  lse         [B, Hq]                      float
@@ -100,10 +106,11 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  *
  * Supported: dtype BF16 with D in {64, 128, 256}, or F32 with D in {64, 128};
  * Hq/Hkv in {1, 2, 4, 8}; page_size 16.  Anything else returns
- * ATTN_E_UNSUPPORTED.
+ * ATTN_E_UNSUPPORTED.  The workspace size depends on dtype, the sizes and
+ * split_pages only (not on the device or on kv_lens).
  */
-size_t attn_decode_paged_workspace_size(int B, int Hq, int Hkv, int D, int page_size,
-                                        int max_kv_len, int split_pages);
+size_t attn_decode_paged_workspace_size(attn_dtype dtype, int B, int Hq, int Hkv, int D,
+                                        int page_size, int max_kv_len, int split_pages);
 
 attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pages,
                               const void* v_pages, const int32_t* page_table,

@@ -69,6 +69,7 @@ def _decode(lib, **kw):
     (dict(q=None), E_NULL),
     (dict(table=None), E_NULL),
     (dict(ws=None, split=2), E_WS),
+    (dict(ws=None), E_WS),                    # bf16 always needs its run partials
     (dict(ws_bytes=8, split=2), E_WS),
     (dict(q=8), E_UNSUP),                     # misaligned
     (dict(num_pages=0), E_SHAPE),
@@ -83,13 +84,21 @@ def test_decode_empty_batch_is_noop(lib):
 
 
 def test_workspace_size(lib):
-    # one split -> no workspace; forced small splits -> B*splits*Hq*(D+1) floats (256-aligned parts)
-    assert lib.attn_decode_paged_workspace_size(4, 8, 2, 128, 16, 100, 0) == 0
-    n = lib.attn_decode_paged_workspace_size(4, 8, 2, 128, 16, 160, 2)   # 10 pages -> 5 splits
-    o = 4 * 5 * 8 * 128 * 4
-    lse = 4 * 5 * 8 * 4
+    # fp32 split grid: one split -> no workspace; forced small splits ->
+    # B*splits*Hq*(D+1) floats (two 256-byte aligned parts)
+    assert lib.attn_decode_paged_workspace_size(0, 4, 8, 2, 128, 16, 100, 0) == 0
+    n = lib.attn_decode_paged_workspace_size(0, 4, 8, 2, 128, 16, 160, 2)   # 10 pages -> 5 splits
+    o, lse = 4 * 5 * 8 * 128 * 4, 4 * 5 * 8 * 4
     assert n == ((o + 255) // 256 + (lse + 255) // 256) * 256
-    assert lib.attn_decode_paged_workspace_size(-1, 8, 2, 128, 16, 160, 2) == 0
+    # bf16 balanced runs: B*Hkv*max_segs*G*(D+1) floats, max_segs = ceil(max_pages/run)+1
+    n = lib.attn_decode_paged_workspace_size(1, 4, 8, 2, 128, 16, 160, 2)   # run 2 -> 6 segs
+    slots = 4 * 2 * 6 * 4
+    assert n == ((slots * 128 * 4 + 255) // 256 + (slots * 4 + 255) // 256) * 256
+    n = lib.attn_decode_paged_workspace_size(1, 4, 8, 2, 128, 16, 160, 0)   # run >= 8 -> 3 segs
+    slots = 4 * 2 * 3 * 4
+    assert n == ((slots * 128 * 4 + 255) // 256 + (slots * 4 + 255) // 256) * 256
+    assert lib.attn_decode_paged_workspace_size(1, -1, 8, 2, 128, 16, 160, 2) == 0
+    assert lib.attn_decode_paged_workspace_size(9, 4, 8, 2, 128, 16, 160, 2) == 0
 
 
 def _prefill(lib, **kw):

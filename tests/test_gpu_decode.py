@@ -128,10 +128,20 @@ def test_large_logits(gpu):
     assert_parity(out, lse, ro, rl, torch.bfloat16, "large logits")
 
 
-def test_paged_config_full(gpu):
+@pytest.fixture(scope="module")
+def paged_config(gpu):
     """Batched paged GQA decode at full size: B 64, Hq 32, Hkv 8, D 128, page 16,
-    kv_len in [512, 4096], pages scattered over a 300k-page pool."""
+    kv_len in [512, 4096], pages scattered over a 300k-page pool (inputs on the
+    GPU and the oracle's answer)."""
     case = workloads.make_config(2)
-    out, lse = _run(case, gpu)
+    pools = case.pools(gpu)
     ro, rl = _oracle(case)
-    assert_parity(out, lse, ro, rl, torch.bfloat16, case.name)
+    return case, pools, ro, rl
+
+
+@pytest.mark.parametrize("split_pages", [0, 8, 64])
+def test_paged_config_full(gpu, paged_config, split_pages):
+    """Auto runs, and fixed runs that outnumber the waves of the grid (8 pages)."""
+    case, pools, ro, rl = paged_config
+    out, lse = _run(case, gpu, split_pages=split_pages, pools=pools)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, f"{case.name} split_pages={split_pages}")
