@@ -2,34 +2,43 @@
 //
 // One workgroup = one (query tile of BM = 128 rows, query head) of one
 // sequence; four waves own 32 query rows each, and two workgroups share a CU
-// so that one wave's matrix work overlaps another's softmax.  Per key tile
-// of BN keys (64 for head_dim 128, 32 for head_dim 256):
-//   1. The tile's K and V rows were fetched into registers during the
-//      previous tile and are written to one of two LDS stages (row-major,
-//      XOR-swizzled so the reads below hit every bank once); the next tile's
-//      global loads are issued right after, so HBM latency hides behind a
-//      whole tile of MFMA work.  One barrier per tile.
-//   2. S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: Q stays in VGPRs for the
-//      whole loop (B operand), K comes from LDS (A operand).  The transposed
-//      product puts one query per lane column, so a row max over keys is an
-//      in-lane reduction plus one lane^32 exchange.
-//   3. Causal/tail mask only on tiles that cross the diagonal or the end of
-//      the keys; online softmax in log2 units (running max m, running sum l,
-//      O rescaled by 2^(m_old - m_new) only when some row's max moved).
-//   4. O^T += V^T . P^T on MFMA: the S^T accumulator is already laid out as
-//      the B operand (keys permuted identically on both operands), and V^T
-//      fragments come from the row-major V tile through ds_read_b64_tr_b16.
+// so that one wave's matrix work overlaps another's vector work.  Key tiles
+// have BN keys (64 for head_dim 128, 32 for head_dim 256).
+//
+// Data movement: K and V tiles go from HBM straight into LDS with
+// global_load_lds_dwordx4 (no register staging), each into a ring of two
+// buffers.  While tile j is processed, the DMA for K(j+2) and V(j+1) is in
+// flight; one wait and one barrier per tile.  Each lane loads the 16-byte
+// chunk that belongs at its LDS position under an XOR swizzle (K: chunk XOR
+// row mod 16; V: 64-byte block XOR row mod 4), so the MFMA operand reads
+// below hit every bank once.
+//
+// Per tile j (the loop is unrolled by two so every LDS address is a per-lane
+// constant plus an immediate):
+//   1. S^T(j+1) = K(j+1) . Q^T on v_mfma_f32_32x32x16_bf16, issued alongside
+//      the softmax of tile j (independent work, interleaved on the SIMD).
+//      Q stays in VGPRs (B operand); the transposed product gives each lane
+//      one query column, so a row max is in-lane plus one lane^32 exchange.
+//   2. Softmax of S^T(j) in log2 units: masks only on tiles crossing the
+//      diagonal or the end of the keys; p = 2^(s*c - m) with one FMA; the
+//      running max m is raised (and O, l rescaled) only when a row's tile
+//      max exceeds it by more than 2^8, so rescaling is rare while p stays
+//      below 256.
+//   3. O^T += V^T(j) . P^T(j) on MFMA: the S^T accumulator is already laid
+//      out as the B operand (keys permuted identically on both operands), and
+//      V^T fragments come from the row-major V tile through ds_read_b64_tr_b16.
 // Tiles wholly above the causal diagonal are never loaded.  The score
 // matrix never reaches memory.
 //
 // This follows the tiled, fused scheme of "FlashAttention-3 内核在最新大模型
 // 推理中的集成实践" (section 一: Q/K/V blocks in on-chip memory, online softmax
-// accumulated in place, loads overlapped with tensor-core work by double
-// buffering; section 二: varlen packing by cu_seqlens, causal, paged blocks;
-// section 四: keep the rescaling, and keep tiles within the on-chip budget for
-// head_dim 256) and the three-stage QK^T / softmax / PV pipeline of "FlashInfer
-// Attention Kernel技术解析" section 1.3 (bank-conflict avoidance: section 4),
-// re-tiled for 64-wide waves, 32x32 MFMA tiles and a 160 KiB LDS.
+// accumulated in place, asynchronous global-to-shared copies overlapped with
+// tensor-core work by double buffering; section 二: varlen packing by
+// cu_seqlens, causal, paged blocks; section 四: keep the rescaling, and keep
+// tiles within the on-chip budget for head_dim 256) and the three-stage QK^T /
+// softmax / PV pipeline of "FlashInfer Attention Kernel技术解析" section 1.3
+// (bank-conflict avoidance: section 4), re-tiled for 64-wide waves, 32x32
+// MFMA tiles and a 160 KiB LDS.
 #include "common.h"
 #include "launch.h"
 
@@ -41,21 +50,24 @@ constexpr int BM = kPrefillBM;   // query rows per workgroup
 constexpr int NWAVE = 4;
 constexpr int NT = NWAVE * 64;
 constexpr int kPage = 16;
+constexpr float kRescaleSlack = 8.f;   // log2 units the running max may lag behind
 
 template <int D>
 struct Cfg {
   static constexpr int BN = D == 128 ? 64 : 32;      // keys per tile
   static constexpr int ROWB = D * 2;                  // bytes of one K/V row
   static constexpr int TILEB = BN * ROWB;             // bytes of one K or V tile
-  static constexpr int STAGEB = 2 * TILEB;            // K + V
   static constexpr int CH = D / 8;                    // 16-byte chunks per row
-  static constexpr int LOADS = BN * CH / NT;          // 16-byte chunks per thread (K or V)
+  static constexpr int DMA = TILEB / 1024 / NWAVE;    // 1 KiB DMA instructions per wave per tile
+  static constexpr int WROWS = BN / NWAVE;            // tile rows written by one wave
   static constexpr int QK = D / 16;                   // MFMA k-steps over D
   static constexpr int DB = D / 32;                   // 32-row blocks of D in O^T
   static constexpr int KB = BN / 32;                  // 32-key blocks per tile
   static constexpr int PS = BN / 16;                  // 16-key k-steps of P.V
-  static_assert(BN * CH % NT == 0, "tile split");
-  static_assert(2 * STAGEB <= 80 * 1024, "two workgroups per CU");
+  static constexpr int LDSB = 4 * TILEB;                // K ring [2] + V ring [2]
+  static_assert(TILEB % (1024 * NWAVE) == 0, "tile split into 1 KiB DMA instructions");
+  static_assert(WROWS <= kPage && kPage % WROWS == 0, "a wave's rows stay inside one page");
+  static_assert(LDSB <= 80 * 1024, "two workgroups per CU");
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -65,26 +77,25 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Byte offset of 16-byte chunk `c` of K row `r` in a K tile: chunk index
-// XOR (r mod 16), so 16 consecutive rows read at the same logical chunk land
-// in 16 different 16-byte bank groups.
-template <int D>
-__device__ __forceinline__ int k_off(int r, int c) {
-  return r * Cfg<D>::ROWB + ((c ^ (r & 15)) << 4);
-}
-// Byte offset of 16-byte chunk `c` of V row `r`: its 64-byte block is XORed
-// with (r mod 4), so the four rows that one 16-lane group of a transposing
-// read touches fall in four different 64-byte bank groups.
-template <int D>
-__device__ __forceinline__ int v_off(int r, int c) {
-  return r * Cfg<D>::ROWB + ((((c >> 2) ^ (r & 3)) << 2 | (c & 3)) << 4);
-}
+// Logical 16-byte chunk stored at physical chunk q of K row r / V row r.
+__device__ __forceinline__ int k_chunk(int r, int q) { return q ^ (r & 15); }
+__device__ __forceinline__ int v_chunk(int r, int q) { return (((q >> 2) ^ (r & 3)) << 2) | (q & 3); }
+
+struct Par0 { static constexpr int value = 0; };
+struct Par1 { static constexpr int value = 1; };
 
 template <int D, bool PAGED>
 __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillParams p) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGEB];
+  // Four separate arrays (not one): the compiler can then tell that a DMA into
+  // one ring slot does not alias operand reads from another, and does not
+  // stall those reads on the DMA's completion.
+  __shared__ __attribute__((aligned(1024))) char k_ring0[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char k_ring1[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char v_ring0[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char v_ring1[C::TILEB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -123,173 +134,204 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillPa
   if (kend < 0) kend = 0;
   const int n_kt = (kend + C::BN - 1) / C::BN;
 
-  const __bf16* qg = reinterpret_cast<const __bf16*>(p.q);
-  const char* kg = reinterpret_cast<const char*>(p.k);
-  const char* vg = reinterpret_cast<const char*>(p.v);
-  const size_t kv_rowb = (size_t)p.Hkv * C::ROWB;      // bytes between consecutive tokens
-
-  // Byte address of key `kj` (clamped into [0, Lk)) for our KV head.  Keys past
-  // the end reuse the last key's row: finite data that the mask zeroes out.
-  auto key_addr = [&](int kj) -> size_t {
-    kj = min(kj, Lk - 1);
-    if constexpr (PAGED) {
-      int pid = table[kj >> 4];
-      if ((unsigned)pid >= (unsigned)p.num_pages) { bad = true; pid = 0; }
-      return ((size_t)pid * kPage + (kj & 15)) * kv_rowb + (size_t)kvh * C::ROWB;
-    } else {
-      return (size_t)(k_start + kj) * kv_rowb + (size_t)kvh * C::ROWB;
-    }
-  };
+  // Scores are used as s * c with c > 0: a negative scale flips the sign of Q,
+  // a zero scale becomes a tiny one (every weight rounds to exactly 1).
+  float c = p.scale_log2;
+  const bool flip = c < 0.f;
+  c = flip ? -c : (c == 0.f ? 1e-30f : c);
 
   // ---- Q fragments (B operand of S^T = K Q^T): row l32 of this wave's 32 rows.
   const int my_row = r0 + wave * 32 + l32;
   const bool row_ok = my_row < Lq;
   bf16x8 qf[C::QK];
   {
-    const __bf16* qr = qg + ((size_t)(q_start + (row_ok ? my_row : 0)) * p.Hq + head) * D + hl * 8;
+    const __bf16* qr = reinterpret_cast<const __bf16*>(p.q) +
+                       ((size_t)(q_start + (row_ok ? my_row : 0)) * p.Hq + head) * D + hl * 8;
 #pragma unroll
     for (int s = 0; s < C::QK; ++s) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(qr + s * 16);
-      qf[s] = row_ok ? v : bf16x8{};
+      u32x4 v = *reinterpret_cast<const u32x4*>(qr + s * 16);
+      if (flip) v ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      qf[s] = row_ok ? __builtin_bit_cast(bf16x8, v) : bf16x8{};
     }
   }
 
-  // ---- register staging of one K/V tile: thread owns chunks tid + NT*i
-  u32x4 kreg[C::LOADS], vreg[C::LOADS];
-  auto load_tile = [&](int k0) {
+  // ---- DMA geometry: instruction i of this wave fills 16-byte units
+  // u = (wave * DMA + i) * 64 + lane of a tile, i.e. row u / CH, physical chunk u % CH.
+  const char* kg = reinterpret_cast<const char*>(p.k);
+  const char* vg = reinterpret_cast<const char*>(p.v);
+  const int kv_rowb = p.Hkv * C::ROWB;                 // bytes between consecutive tokens
+  const int wrow0 = wave * C::WROWS;                   // first tile row of this wave
+  int koff[C::DMA], voff[C::DMA], drow[C::DMA];        // per-lane byte offsets inside a row
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int ci = tid + NT * i;
-      const int row = ci / C::CH, c = ci % C::CH;
-      const size_t a = key_addr(k0 + row) + c * 16;
-      kreg[i] = *reinterpret_cast<const u32x4*>(kg + a);
-      vreg[i] = *reinterpret_cast<const u32x4*>(vg + a);
+  for (int i = 0; i < C::DMA; ++i) {
+    const int u = (wave * C::DMA + i) * 64 + lane;
+    const int r = u / C::CH, q = u % C::CH;
+    drow[i] = r;
+    koff[i] = k_chunk(r, q) * 16;
+    voff[i] = v_chunk(r, q) * 16;
+  }
+  // Issue the DMA of K (is_v = false) or V rows k0 .. k0 + BN - 1 into LDS tile `dst`.
+  // Rows past the end of the keys repeat the last key (finite data that the mask drops).
+  auto dma = [&](int k0, char* dst, bool is_v) {
+    const char* g = is_v ? vg : kg;
+    if constexpr (PAGED) {
+      // this wave's rows lie in one page (clamped rows past the end too)
+      const int kr = min(k0 + wrow0, Lk - 1);
+      int pid = table[kr >> 4];
+      if ((unsigned)pid >= (unsigned)p.num_pages) { bad = true; pid = 0; }
+      const char* base = g + (size_t)pid * kPage * kv_rowb + (size_t)kvh * C::ROWB;
+#pragma unroll
+      for (int i = 0; i < C::DMA; ++i) {
+        const int kj = min(k0 + drow[i], Lk - 1);
+        const int o = (kj & 15) * kv_rowb + (is_v ? voff[i] : koff[i]);
+        __builtin_amdgcn_global_load_lds(base + o, (lds_void*)(dst + (wave * C::DMA + i) * 1024),
+                                         16, 0, 0);
+      }
+    } else {
+      const char* base = g + ((size_t)k_start * kv_rowb + (size_t)kvh * C::ROWB);
+#pragma unroll
+      for (int i = 0; i < C::DMA; ++i) {
+        const int kj = min(k0 + drow[i], Lk - 1);
+        const size_t o = (size_t)kj * kv_rowb + (is_v ? voff[i] : koff[i]);
+        __builtin_amdgcn_global_load_lds(base + o, (lds_void*)(dst + (wave * C::DMA + i) * 1024),
+                                         16, 0, 0);
+      }
     }
   };
-  auto store_tile = [&](int stage) {
-    char* sk = smem + stage * C::STAGEB;
-    char* sv = sk + C::TILEB;
+
+  // ---- per-lane LDS read offsets (the buffer and block go in the immediate)
+  int kro[C::QK];                 // K: row l32 of a 32-key block, logical chunk 2 ks + hl
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int ci = tid + NT * i;
-      const int row = ci / C::CH, c = ci % C::CH;
-      *reinterpret_cast<u32x4*>(sk + k_off<D>(row, c)) = kreg[i];
-      *reinterpret_cast<u32x4*>(sv + v_off<D>(row, c)) = vreg[i];
-    }
-  };
+  for (int ks = 0; ks < C::QK; ++ks) kro[ks] = l32 * C::ROWB + (k_chunk(l32, 2 * ks + hl) << 4);
+  const int grp = lane >> 4, gj = lane & 15;
+  const int tr_row = 4 * (grp >> 1) + (gj >> 2);       // + 16 ps (+ 8 for the high half)
+  const int tr_col = 16 * (grp & 1) + 4 * (gj & 3);    // d within a 32-wide block
+  int vro[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    const int d = db * 32 + tr_col;
+    vro[db] = tr_row * C::ROWB + (v_chunk(tr_row, d >> 3) << 4) + (d & 7) * 2;
+  }
 
   f32x16 o[C::DB];
 #pragma unroll
   for (int i = 0; i < C::DB; ++i) o[i] = f32x16{};
   float m = kNegInf, lsum = 0.f;
-  const float c = p.scale_log2;
 
   const int w_first = r0 + wave * 32;                       // first row of this wave
   const int w_last = min(w_first + 31, Lq - 1);
   const bool wave_rows = w_first < Lq;
   const int pos = my_row + off;   // last visible key index for this lane's query
-
-  // transposing-read geometry: 16-lane group g = lane / 16
-  const int grp = lane >> 4, gj = lane & 15;
-  const int tr_row = 4 * (grp >> 1) + (gj >> 2);           // + 16 * ks (+ 8 for the high half)
-  const int tr_col = 16 * (grp & 1) + 4 * (gj & 3);        // d within the 32-wide block
-
-  if (n_kt > 0) {
-    load_tile(0);
-    store_tile(0);
-    if (n_kt > 1) load_tile(C::BN);
+  // Tiles this wave needs: keys up to its last row's diagonal.
+  int w_kt = 0;
+  if (wave_rows) {
+    const int wkend = p.causal ? max(0, min(Lk, w_last + off + 1)) : Lk;
+    w_kt = min(n_kt, (wkend + C::BN - 1) / C::BN);
   }
-  __syncthreads();
 
-  for (int kt = 0; kt < n_kt; ++kt) {
+  auto qk = [&](const char* kbuf, f32x16 (&s)[C::KB]) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < C::QK; ++ks)
+        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kbuf + kb * 32 * C::ROWB + kro[ks]),
+                       qf[ks], s[kb]);
+    }
+  };
+
+  auto softmax_pv = [&](int kt, f32x16 (&s)[C::KB], char* vbuf) {
     const int k0 = kt * C::BN;
-    const char* sk = smem + (kt & 1) * C::STAGEB;
-    const char* sv = sk + C::TILEB;
-    const bool wave_sees = wave_rows && (!p.causal || k0 <= w_last + off);
-
-    if (wave_sees) {
-      // S^T = K Q^T
-      f32x16 s[C::KB];
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        s[kb] = f32x16{};
-        const int r = kb * 32 + l32;
-#pragma unroll
-        for (int ks = 0; ks < C::QK; ++ks)
-          s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(sk + k_off<D>(r, ks * 2 + hl)), qf[ks], s[kb]);
-      }
-
-      // scale to log2 units, mask where needed, running max
+    if (k0 + C::BN > Lk || (p.causal && k0 + C::BN - 1 > w_first + off)) {
+      const int lim = p.causal ? min(pos, Lk - 1) : Lk - 1;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] *= c;
-      if (k0 + C::BN > Lk || (p.causal && k0 + C::BN - 1 > w_first + off)) {
-        // keys past the end or above the diagonal; lim = last visible key
-        const int lim = p.causal ? min(pos, Lk - 1) : Lk - 1;
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          s[kb][r] = key > lim ? kNegInf : s[kb][r];
+        }
+    }
+    float mr = kNegInf;
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            s[kb][r] = key > lim ? kNegInf : s[kb][r];
-          }
+      for (int r = 0; r < 16; ++r) mr = fmaxf(mr, s[kb][r]);
+    const float mt = max_halves(mr) * c;                 // tile max in log2 units
+    const bool raise = mt > m + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      // Lanes that do not raise keep alpha = 1 (m may still be -inf there);
+      // a raise from m = -inf gives alpha = 0.
+      const float alpha = raise ? exp2_fast(m - mt) : 1.f;
+      m = raise ? mt : m;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    const float nm = m == kNegInf ? 0.f : -m;
+    float psum = 0.f;
+    bf16x8 pb[C::PS];
+#pragma unroll
+    for (int ps = 0; ps < C::PS; ++ps) {
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = exp2_fast(__builtin_fmaf(s[ps >> 1][(ps & 1) * 8 + e], c, nm));
+        psum += pe;
+        v[e] = (__bf16)pe;
       }
-      float mt = kNegInf;
+      pb[ps] = v;
+    }
+    lsum += psum;
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-      mt = max_halves(mt);
-      const float mn = fmaxf(m, mt);
-      const float mu = mn == kNegInf ? 0.f : mn;
-      const float alpha = exp2_fast(m - mu);
-      m = mn;
-      float psum = 0.f;
-      bf16x8 pb[C::PS];
+    for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
       for (int ps = 0; ps < C::PS; ++ps) {
-        bf16x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pe = exp2_fast(s[ps >> 1][(ps & 1) * 8 + e] - mu);
-          psum += pe;
-          v[e] = (__bf16)pe;
-        }
-        pb[ps] = v;
-      }
-      lsum = lsum * alpha + psum;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      }
-
-      // O^T += V^T P^T, V^T fragments through the transposing LDS read
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-#pragma unroll
-        for (int ps = 0; ps < C::PS; ++ps) {
-          const int r = ps * 16 + tr_row;
-          const int d = db * 32 + tr_col;     // 4 consecutive d of one 16-byte chunk half
-          const int cl = d >> 3, cb = (d & 7) * 2;
-          v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16*)((lds_char*)sv + v_off<D>(r, cl) + cb));
-          v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16*)((lds_char*)sv + v_off<D>(r + 8, cl) + cb));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[db] = mfma32(a, pb[ps], o[db]);
-        }
+        const int ro = ps * 16 * C::ROWB + vro[db];
+        v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_char*)vbuf + ro));
+        v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16*)((lds_char*)vbuf + ro + 8 * C::ROWB));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[db] = mfma32(a, pb[ps], o[db]);
       }
     }
+  };
 
-    // stage the next tile and fetch the one after it
-    if (kt + 1 < n_kt) {
-      store_tile((kt + 1) & 1);
-      if (kt + 2 < n_kt) load_tile(k0 + 2 * C::BN);
+  // One tile step; PAR = kt % 2 picks the ring buffers at compile time.
+  //   K(kt+1) is in K ring [PAR^1], V(kt) in V ring [PAR]; this step starts the
+  //   DMA of K(kt+2) into K ring [PAR] and of V(kt+1) into V ring [PAR^1].
+  f32x16 sa[C::KB], sb[C::KB];
+  auto step = [&](auto par_tag, int kt, f32x16 (&scur)[C::KB], f32x16 (&snext)[C::KB]) {
+    constexpr int PAR = decltype(par_tag)::value;
+    char* const KCUR = PAR ? k_ring1 : k_ring0;
+    char* const KNXT = PAR ? k_ring0 : k_ring1;
+    char* const VCUR = PAR ? v_ring1 : v_ring0;
+    char* const VNXT = PAR ? v_ring0 : v_ring1;
+    if (kt + 2 < n_kt) dma((kt + 2) * C::BN, KCUR, false);
+    if (kt + 1 < n_kt) dma((kt + 1) * C::BN, VNXT, true);
+    if (kt < w_kt) {
+      if (kt + 1 < w_kt) qk(KNXT, snext);
+      softmax_pv(kt, scur, VCUR);
     }
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this wave's DMA has landed
+    __syncthreads();                      // ... and every wave's; ring slots are free
+  };
+
+  // prologue: K(0), V(0), K(1) in LDS, S^T(0) in registers
+  if (n_kt > 0) {
+    dma(0, k_ring0, false);
+    dma(0, v_ring0, true);
+    if (n_kt > 1) dma(C::BN, k_ring1, false);
+    __builtin_amdgcn_s_waitcnt(0x3f70);
+  }
+  __syncthreads();
+  if (0 < w_kt) qk(k_ring0, sa);
+  __syncthreads();   // every wave is done with K(0) before step 0 refills its buffer
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    step(Par0{}, kt, sa, sb);
+    if (kt + 1 < n_kt) step(Par1{}, kt + 1, sb, sa);
   }
 
   const bool any_bad = __syncthreads_or(bad);
