@@ -6,6 +6,7 @@ written next to this file so it travels with the package.
 """
 from __future__ import annotations
 
+import ctypes
 import os
 import shutil
 import subprocess
@@ -65,6 +66,14 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # A shared library links even with undefined symbols (e.g. a kernel whose
+    # host-side launch stub the compiler silently dropped); resolve them all
+    # now so such a build fails here rather than at first use.
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW)
+    except OSError as e:
+        os.remove(tmp)
+        raise RuntimeError(f"built library does not load: {e}") from None
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

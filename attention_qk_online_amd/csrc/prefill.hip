@@ -64,6 +64,7 @@ struct Cfg {
   static constexpr int DB = D / 32;                   // 32-row blocks of D in O^T
   static constexpr int KB = BN / 32;                  // 32-key blocks per tile
   static constexpr int PS = BN / 16;                  // 16-key k-steps of P.V
+  static constexpr int VALU_PER_QK = D == 128 ? 6 : 3;  // vector work issued per S^T MFMA
   static constexpr int LDSB = 4 * TILEB;                // K ring [2] + V ring [2]
   static_assert(TILEB % (1024 * NWAVE) == 0, "tile split into 1 KiB DMA instructions");
   static_assert(WROWS <= kPage && kPage % WROWS == 0, "a wave's rows stay inside one page");
@@ -155,44 +156,57 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillPa
     }
   }
 
-  // ---- DMA geometry: instruction i of this wave fills 16-byte units
-  // u = (wave * DMA + i) * 64 + lane of a tile, i.e. row u / CH, physical chunk u % CH.
+  // ---- DMA geometry.  Instruction i of this wave fills the 1 KiB of LDS at
+  // tile byte (wave * DMA + i) * 1024: RPI whole rows, lane -> row
+  // (wave * DMA + i) * RPI + lane / CH, physical chunk lane % CH, fetching the
+  // logical chunk that the swizzle puts there.
+  constexpr int RPI = 64 / C::CH;                      // rows per DMA instruction
   const char* kg = reinterpret_cast<const char*>(p.k);
   const char* vg = reinterpret_cast<const char*>(p.v);
   const int kv_rowb = p.Hkv * C::ROWB;                 // bytes between consecutive tokens
   const int wrow0 = wave * C::WROWS;                   // first tile row of this wave
-  int koff[C::DMA], voff[C::DMA], drow[C::DMA];        // per-lane byte offsets inside a row
+  const int lane_row = lane / C::CH, lane_q = lane % C::CH;
+  const int lane_rowb = lane_row * kv_rowb;
+  // Per-lane part of each DMA address (row within the instruction + swizzled
+  // chunk); the instruction's first row is wave-uniform and goes in the base.
+  unsigned klane[C::DMA], vlane[C::DMA];
 #pragma unroll
   for (int i = 0; i < C::DMA; ++i) {
-    const int u = (wave * C::DMA + i) * 64 + lane;
-    const int r = u / C::CH, q = u % C::CH;
-    drow[i] = r;
-    koff[i] = k_chunk(r, q) * 16;
-    voff[i] = v_chunk(r, q) * 16;
+    const int rlo = ((wave * C::DMA + i) * RPI) & 15;  // a multiple of RPI, so OR adds lane_row
+    klane[i] = (unsigned)(lane_rowb + k_chunk(rlo | lane_row, lane_q) * 16);
+    vlane[i] = (unsigned)(lane_rowb + v_chunk(rlo | lane_row, lane_q) * 16);
   }
+  const int t_full = Lk / C::BN;                       // tiles wholly inside the keys
   // Issue the DMA of K (is_v = false) or V rows k0 .. k0 + BN - 1 into LDS tile `dst`.
-  // Rows past the end of the keys repeat the last key (finite data that the mask drops).
-  auto dma = [&](int k0, char* dst, bool is_v) {
+  // The last, partial tile repeats the last key in rows past the end (finite
+  // data that the mask drops).
+  auto dma = [&](int kt, char* dst, bool is_v) {
+    const int k0 = kt * C::BN;
     const char* g = is_v ? vg : kg;
+    const char* base;
     if constexpr (PAGED) {
       // this wave's rows lie in one page (clamped rows past the end too)
       const int kr = min(k0 + wrow0, Lk - 1);
       int pid = table[kr >> 4];
       if ((unsigned)pid >= (unsigned)p.num_pages) { bad = true; pid = 0; }
-      const char* base = g + (size_t)pid * kPage * kv_rowb + (size_t)kvh * C::ROWB;
+      base = g + (size_t)pid * kPage * kv_rowb + (size_t)kvh * C::ROWB;
+    } else {
+      base = g + ((size_t)k_start * kv_rowb + (size_t)kvh * C::ROWB);
+    }
+    if (kt < t_full) {
 #pragma unroll
       for (int i = 0; i < C::DMA; ++i) {
-        const int kj = min(k0 + drow[i], Lk - 1);
-        const int o = (kj & 15) * kv_rowb + (is_v ? voff[i] : koff[i]);
-        __builtin_amdgcn_global_load_lds(base + o, (lds_void*)(dst + (wave * C::DMA + i) * 1024),
-                                         16, 0, 0);
+        const int r0i = (wave * C::DMA + i) * RPI;     // first tile row of instruction i
+        const char* bi = base + (size_t)(PAGED ? (r0i & (kPage - 1)) : k0 + r0i) * kv_rowb;
+        __builtin_amdgcn_global_load_lds(bi + (size_t)(is_v ? vlane[i] : klane[i]),
+                                         (lds_void*)(dst + (wave * C::DMA + i) * 1024), 16, 0, 0);
       }
     } else {
-      const char* base = g + ((size_t)k_start * kv_rowb + (size_t)kvh * C::ROWB);
 #pragma unroll
       for (int i = 0; i < C::DMA; ++i) {
-        const int kj = min(k0 + drow[i], Lk - 1);
-        const size_t o = (size_t)kj * kv_rowb + (is_v ? voff[i] : koff[i]);
+        const int kj = min(k0 + (wave * C::DMA + i) * RPI + lane_row, Lk - 1);
+        const int row = PAGED ? (kj & (kPage - 1)) : kj;
+        const size_t o = (size_t)row * kv_rowb - lane_rowb + (is_v ? vlane[i] : klane[i]);
         __builtin_amdgcn_global_load_lds(base + o, (lds_void*)(dst + (wave * C::DMA + i) * 1024),
                                          16, 0, 0);
       }
@@ -200,15 +214,19 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillPa
   };
 
   // ---- per-lane LDS read offsets (the buffer and block go in the immediate)
-  int kro[C::QK];                 // K: row l32 of a 32-key block, logical chunk 2 ks + hl
+  // K: row l32 of a 32-key block, logical chunk 2 ks + hl.  The swizzle only
+  // touches the low four chunk bits, so k-steps 8.. are 256 bytes further on.
+  int kro[8];
 #pragma unroll
-  for (int ks = 0; ks < C::QK; ++ks) kro[ks] = l32 * C::ROWB + (k_chunk(l32, 2 * ks + hl) << 4);
+  for (int ks = 0; ks < 8; ++ks) kro[ks] = l32 * C::ROWB + (k_chunk(l32, 2 * ks + hl) << 4);
   const int grp = lane >> 4, gj = lane & 15;
   const int tr_row = 4 * (grp >> 1) + (gj >> 2);       // + 16 ps (+ 8 for the high half)
   const int tr_col = 16 * (grp & 1) + 4 * (gj & 3);    // d within a 32-wide block
-  int vro[C::DB];
+  // V: the swizzle touches 64-byte block bits 0-1 only, so 32-wide d blocks
+  // 4.. are 256 bytes further on.
+  int vro[4];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
+  for (int db = 0; db < 4; ++db) {
     const int d = db * 32 + tr_col;
     vro[db] = tr_row * C::ROWB + (v_chunk(tr_row, d >> 3) << 4) + (d & 7) * 2;
   }
@@ -222,11 +240,15 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillPa
   const int w_last = min(w_first + 31, Lq - 1);
   const bool wave_rows = w_first < Lq;
   const int pos = my_row + off;   // last visible key index for this lane's query
-  // Tiles this wave needs: keys up to its last row's diagonal.
-  int w_kt = 0;
+  // Tiles this wave needs (keys up to its last row's diagonal), and the
+  // leading ones in which every row of the wave sees every key (no mask).
+  int w_kt = 0, w_fast = 0;
   if (wave_rows) {
     const int wkend = p.causal ? max(0, min(Lk, w_last + off + 1)) : Lk;
     w_kt = min(n_kt, (wkend + C::BN - 1) / C::BN);
+    int lim = t_full;
+    if (p.causal) lim = min(lim, max(0, w_first + off + 1) / C::BN);
+    w_fast = min(lim, w_kt);
   }
 
   auto qk = [&](const char* kbuf, f32x16 (&s)[C::KB]) {
@@ -235,23 +257,27 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillPa
       s[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < C::QK; ++ks)
-        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kbuf + kb * 32 * C::ROWB + kro[ks]),
+        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kbuf + kb * 32 * C::ROWB + (ks >> 3) * 256 + kro[ks & 7]),
                        qf[ks], s[kb]);
     }
   };
 
-  auto softmax_pv = [&](int kt, f32x16 (&s)[C::KB], char* vbuf) {
+  // Scores past the end of the keys or right of this lane's diagonal -> -inf.
+  auto mask = [&](int kt, f32x16 (&s)[C::KB]) {
     const int k0 = kt * C::BN;
-    if (k0 + C::BN > Lk || (p.causal && k0 + C::BN - 1 > w_first + off)) {
-      const int lim = p.causal ? min(pos, Lk - 1) : Lk - 1;
+    const int lim = p.causal ? min(pos, Lk - 1) : Lk - 1;
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          s[kb][r] = key > lim ? kNegInf : s[kb][r];
-        }
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        s[kb][r] = key > lim ? kNegInf : s[kb][r];
+      }
+  };
+
+  // Row max of the tile; raise the running max (and rescale O, l) only when
+  // some row's tile max passes it by more than the slack.
+  auto update_max = [&](f32x16 (&s)[C::KB]) {
     float mr = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
@@ -270,26 +296,33 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillPa
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
-    const float nm = m == kNegInf ? 0.f : -m;
+  };
+
+  // P = 2^(s c - m) rounded to bf16 (laid out as the B operand of O^T += V^T P^T);
+  // the row sum adds the rounded weights, the ones that multiply V.
+  auto weights = [&](f32x16 (&s)[C::KB], bf16x8 (&pb)[C::PS], float nm) {
     float psum = 0.f;
-    bf16x8 pb[C::PS];
+    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
     for (int ps = 0; ps < C::PS; ++ps) {
       bf16x8 v;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pe = exp2_fast(__builtin_fmaf(s[ps >> 1][(ps & 1) * 8 + e], c, nm));
-        psum += pe;
-        v[e] = (__bf16)pe;
-      }
+      for (int e = 0; e < 8; ++e)
+        v[e] = (__bf16)exp2_fast(__builtin_fmaf(s[ps >> 1][(ps & 1) * 8 + e], c, nm));
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[e], v[e + 1]}, one, psum, false);
       pb[ps] = v;
     }
     lsum += psum;
+  };
+
+  auto pv = [&](const char* vbuf, bf16x8 (&pb)[C::PS]) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
       for (int ps = 0; ps < C::PS; ++ps) {
-        const int ro = ps * 16 * C::ROWB + vro[db];
+        const int ro = ps * 16 * C::ROWB + (db >> 2) * 256 + vro[db & 3];
         v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_char*)vbuf + ro));
         v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_v4i16*)((lds_char*)vbuf + ro + 8 * C::ROWB));
@@ -302,36 +335,88 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillPa
   // One tile step; PAR = kt % 2 picks the ring buffers at compile time.
   //   K(kt+1) is in K ring [PAR^1], V(kt) in V ring [PAR]; this step starts the
   //   DMA of K(kt+2) into K ring [PAR] and of V(kt+1) into V ring [PAR^1].
+  // FAST steps are the steady state: no row of any wave masks tile kt, and
+  // every wave needs tile kt + 1.
   f32x16 sa[C::KB], sb[C::KB];
-  auto step = [&](auto par_tag, int kt, f32x16 (&scur)[C::KB], f32x16 (&snext)[C::KB]) {
+  auto step = [&](auto par_tag, auto fast_tag, int kt, f32x16 (&scur)[C::KB],
+                  f32x16 (&snext)[C::KB]) {
     constexpr int PAR = decltype(par_tag)::value;
+    constexpr bool FAST = decltype(fast_tag)::value != 0;
     char* const KCUR = PAR ? k_ring1 : k_ring0;
     char* const KNXT = PAR ? k_ring0 : k_ring1;
     char* const VCUR = PAR ? v_ring1 : v_ring0;
     char* const VNXT = PAR ? v_ring0 : v_ring1;
-    if (kt + 2 < n_kt) dma((kt + 2) * C::BN, KCUR, false);
-    if (kt + 1 < n_kt) dma((kt + 1) * C::BN, VNXT, true);
-    if (kt < w_kt) {
+    if (kt + 2 < n_kt) dma(kt + 2, KCUR, false);
+    if (kt + 1 < n_kt) dma(kt + 1, VNXT, true);
+    bf16x8 pb[C::PS];
+    if constexpr (FAST) {
+      // One block in which the S^T(kt+1) MFMAs hide the exponentials of tile kt.
+      update_max(scur);
+      qk(KNXT, snext);
+      weights(scur, pb, -m);                 // m is finite once a tile is unmasked
+      pv(VCUR, pb);
+      // Issue order: K fragment reads ahead of the S^T MFMAs, each MFMA
+      // followed by a share of the vector work, then the V^T fragment reads
+      // ahead of the O^T MFMAs.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);              // 4 K reads
+#pragma unroll
+      for (int i = 0; i < C::KB * C::QK - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // S^T MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);            // next K read
+        __builtin_amdgcn_sched_group_barrier(0x002, C::VALU_PER_QK, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);            // first V reads
+        __builtin_amdgcn_sched_group_barrier(0x002, C::VALU_PER_QK, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < C::DB * C::PS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // O^T MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);            // V reads ahead
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+    } else if (kt < w_kt) {
+      if (kt >= w_fast) mask(kt, scur);
+      update_max(scur);
       if (kt + 1 < w_kt) qk(KNXT, snext);
-      softmax_pv(kt, scur, VCUR);
+      weights(scur, pb, m == kNegInf ? 0.f : -m);
+      pv(VCUR, pb);
     }
     __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this wave's DMA has landed
     __syncthreads();                      // ... and every wave's; ring slots are free
   };
 
+  // Steady-state steps: [0, n_fast), an even count.  Wave 0 has the fewest
+  // unmasked and needed tiles (its rows come first); waves past the last
+  // row compute on zero queries and store nothing.
+  int n_fast = t_full;
+  if (p.causal) n_fast = min(n_fast, max(0, r0 + off + 1) / C::BN);
+  {
+    const int wkend0 = p.causal ? max(0, min(Lk, min(r0 + 31, Lq - 1) + off + 1)) : Lk;
+    const int w_kt0 = min(n_kt, (wkend0 + C::BN - 1) / C::BN);
+    n_fast = min(n_fast, w_kt0 - 1) & ~1;
+  }
+
   // prologue: K(0), V(0), K(1) in LDS, S^T(0) in registers
   if (n_kt > 0) {
     dma(0, k_ring0, false);
     dma(0, v_ring0, true);
-    if (n_kt > 1) dma(C::BN, k_ring1, false);
+    if (n_kt > 1) dma(1, k_ring1, false);
     __builtin_amdgcn_s_waitcnt(0x3f70);
   }
   __syncthreads();
-  if (0 < w_kt) qk(k_ring0, sa);
+  if (n_kt > 0) qk(k_ring0, sa);
   __syncthreads();   // every wave is done with K(0) before step 0 refills its buffer
-  for (int kt = 0; kt < n_kt; kt += 2) {
-    step(Par0{}, kt, sa, sb);
-    if (kt + 1 < n_kt) step(Par1{}, kt + 1, sb, sa);
+  int kt = 0;
+  for (; kt < n_fast; kt += 2) {
+    step(Par0{}, Par1{}, kt, sa, sb);
+    step(Par1{}, Par1{}, kt + 1, sb, sa);
+  }
+  for (; kt < n_kt; kt += 2) {
+    step(Par0{}, Par0{}, kt, sa, sb);
+    if (kt + 1 < n_kt) step(Par1{}, Par0{}, kt + 1, sb, sa);
   }
 
   const bool any_bad = __syncthreads_or(bad);
