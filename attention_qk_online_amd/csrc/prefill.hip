@@ -51,6 +51,7 @@ constexpr int NWAVE = 4;
 constexpr int NT = NWAVE * 64;
 constexpr int kPage = 16;
 constexpr float kRescaleSlack = 8.f;   // log2 units the running max may lag behind
+constexpr int kBufferWord3 = 0x00020000;   // buffer descriptor word 3 for gfx950 (32-bit data format)
 
 template <int D>
 struct Cfg {
@@ -177,38 +178,45 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillPa
     vlane[i] = (unsigned)(lane_rowb + v_chunk(rlo | lane_row, lane_q) * 16);
   }
   const int t_full = Lk / C::BN;                       // tiles wholly inside the keys
-  // Issue the DMA of K (is_v = false) or V rows k0 .. k0 + BN - 1 into LDS tile `dst`.
-  // The last, partial tile repeats the last key in rows past the end (finite
-  // data that the mask drops).
+  // Issue the DMA of K (is_v = false) or V rows k0 .. k0 + BN - 1 into LDS tile `dst`
+  // with buffer loads (a wave-uniform descriptor whose range ends at the last
+  // row this tile may touch, so the hardware drops anything past it).  The
+  // last, partial tile repeats the last key in rows past the end (finite data
+  // that the mask drops).
   auto dma = [&](int kt, char* dst, bool is_v) {
     const int k0 = kt * C::BN;
     const char* g = is_v ? vg : kg;
     const char* base;
+    int nrec;
     if constexpr (PAGED) {
       // this wave's rows lie in one page (clamped rows past the end too)
       const int kr = min(k0 + wrow0, Lk - 1);
       int pid = table[kr >> 4];
       if ((unsigned)pid >= (unsigned)p.num_pages) { bad = true; pid = 0; }
       base = g + (size_t)pid * kPage * kv_rowb + (size_t)kvh * C::ROWB;
+      nrec = (kPage - 1) * kv_rowb + C::ROWB;
     } else {
-      base = g + ((size_t)k_start * kv_rowb + (size_t)kvh * C::ROWB);
+      base = g + ((size_t)(k_start + k0) * kv_rowb + (size_t)kvh * C::ROWB);
+      nrec = (min(C::BN, Lk - k0) - 1) * kv_rowb + C::ROWB;
     }
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, nrec, kBufferWord3);
     if (kt < t_full) {
 #pragma unroll
       for (int i = 0; i < C::DMA; ++i) {
         const int r0i = (wave * C::DMA + i) * RPI;     // first tile row of instruction i
-        const char* bi = base + (size_t)(PAGED ? (r0i & (kPage - 1)) : k0 + r0i) * kv_rowb;
-        __builtin_amdgcn_global_load_lds(bi + (size_t)(is_v ? vlane[i] : klane[i]),
-                                         (lds_void*)(dst + (wave * C::DMA + i) * 1024), 16, 0, 0);
+        const int soff = (PAGED ? (r0i & (kPage - 1)) : r0i) * kv_rowb;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + (wave * C::DMA + i) * 1024), 16,
+                                                 (int)(is_v ? vlane[i] : klane[i]), soff, 0, 0);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < C::DMA; ++i) {
         const int kj = min(k0 + (wave * C::DMA + i) * RPI + lane_row, Lk - 1);
-        const int row = PAGED ? (kj & (kPage - 1)) : kj;
-        const size_t o = (size_t)row * kv_rowb - lane_rowb + (is_v ? vlane[i] : klane[i]);
-        __builtin_amdgcn_global_load_lds(base + o, (lds_void*)(dst + (wave * C::DMA + i) * 1024),
-                                         16, 0, 0);
+        const int row = PAGED ? (kj & (kPage - 1)) : kj - k0;
+        const int o = row * kv_rowb - lane_rowb + (int)(is_v ? vlane[i] : klane[i]);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + (wave * C::DMA + i) * 1024), 16,
+                                                 o, 0, 0, 0);
       }
     }
   };
