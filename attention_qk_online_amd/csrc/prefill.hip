@@ -66,10 +66,14 @@ struct Cfg {
   static constexpr int KB = BN / 32;                  // 32-key blocks per tile
   static constexpr int PS = BN / 16;                  // 16-key k-steps of P.V
   static constexpr int VALU_PER_QK = D == 128 ? 6 : 3;  // vector work issued per S^T MFMA
-  static constexpr int LDSB = 4 * TILEB;                // K ring [2] + V ring [2]
+  // Ring slots per operand: two for head_dim 128 (two workgroups share a CU),
+  // four for head_dim 256 (one workgroup per CU; tiles arrive three steps early).
+  static constexpr int R = D == 128 ? 2 : 4;
+  static constexpr int LDSB = 2 * R * TILEB;
   static_assert(TILEB % (1024 * NWAVE) == 0, "tile split into 1 KiB DMA instructions");
   static_assert(WROWS <= kPage && kPage % WROWS == 0, "a wave's rows stay inside one page");
-  static_assert(LDSB <= 80 * 1024, "two workgroups per CU");
+  static_assert(D != 128 || LDSB <= 80 * 1024, "two workgroups per CU");
+  static_assert(LDSB <= 160 * 1024, "LDS per CU");
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -85,19 +89,45 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ int k_chunk(int r, int q) { return q ^ (r & 15); }
 __device__ __forceinline__ int v_chunk(int r, int q) { return (((q >> 2) ^ (r & 3)) << 2) | (q & 3); }
 
-struct Par0 { static constexpr int value = 0; };
-struct Par1 { static constexpr int value = 1; };
+template <int N>
+struct Idx { static constexpr int value = N; };
 
+// s_waitcnt immediates (gfx9 encoding): vmcnt(n) with expcnt and lgkmcnt
+// unconstrained, and lgkmcnt(0) alone.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 0xc07f;
+
+// The page table comes as its own restrict-qualified argument so that its
+// wave-uniform reads compile to scalar loads.
 template <int D, bool PAGED>
-__global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
+    PrefillParams p, const int32_t* __restrict__ page_table) {
   using C = Cfg<D>;
-  // Four separate arrays (not one): the compiler can then tell that a DMA into
-  // one ring slot does not alias operand reads from another, and does not
-  // stall those reads on the DMA's completion.
+  // One array per ring slot (not one array): the compiler can then tell that a
+  // DMA into one slot does not alias operand reads from another, and does not
+  // stall those reads on the DMA's completion.  Slots past R are unused.
   __shared__ __attribute__((aligned(1024))) char k_ring0[C::TILEB];
   __shared__ __attribute__((aligned(1024))) char k_ring1[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char k_ring2[C::R > 2 ? C::TILEB : 1];
+  __shared__ __attribute__((aligned(1024))) char k_ring3[C::R > 3 ? C::TILEB : 1];
   __shared__ __attribute__((aligned(1024))) char v_ring0[C::TILEB];
   __shared__ __attribute__((aligned(1024))) char v_ring1[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char v_ring2[C::R > 2 ? C::TILEB : 1];
+  __shared__ __attribute__((aligned(1024))) char v_ring3[C::R > 3 ? C::TILEB : 1];
+  auto kslot = [&](auto i) -> char* {
+    constexpr int S = decltype(i)::value % C::R;
+    if constexpr (S == 0) return k_ring0;
+    else if constexpr (S == 1) return k_ring1;
+    else if constexpr (S == 2) return k_ring2;
+    else return k_ring3;
+  };
+  auto vslot = [&](auto i) -> char* {
+    constexpr int S = decltype(i)::value % C::R;
+    if constexpr (S == 0) return v_ring0;
+    else if constexpr (S == 1) return v_ring1;
+    else if constexpr (S == 2) return v_ring2;
+    else return v_ring3;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -124,7 +154,7 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillPa
   if constexpr (PAGED) {
     Lk = p.kv_lens[b];
     if (Lk < 0 || Lk > p.max_pages * kPage) { bad = true; Lk = 0; }
-    table = p.page_table + (size_t)b * p.max_pages;
+    table = page_table + (size_t)b * p.max_pages;
   } else {
     k_start = min(max(p.cu_k[b], 0), p.total_k);
     const int k_end = min(max(p.cu_k[b + 1], k_start), p.total_k);
@@ -183,16 +213,23 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillPa
   // row this tile may touch, so the hardware drops anything past it).  The
   // last, partial tile repeats the last key in rows past the end (finite data
   // that the mask drops).
-  auto dma = [&](int kt, char* dst, bool is_v) {
+  // Physical page holding this wave's rows of tile t (paged; clamped rows
+  // past the end stay in the same page); an out-of-range entry marks the
+  // request bad and reads page 0 instead.
+  auto load_pid = [&](int t) -> int {
+    int pid = 0;
+    if constexpr (PAGED) {
+      pid = table[min(t * C::BN + wrow0, Lk - 1) >> 4];
+      if ((unsigned)pid >= (unsigned)p.num_pages) { bad = true; pid = 0; }
+    }
+    return pid;
+  };
+  auto dma = [&](int kt, char* dst, bool is_v, int pid) {
     const int k0 = kt * C::BN;
     const char* g = is_v ? vg : kg;
     const char* base;
     int nrec;
     if constexpr (PAGED) {
-      // this wave's rows lie in one page (clamped rows past the end too)
-      const int kr = min(k0 + wrow0, Lk - 1);
-      int pid = table[kr >> 4];
-      if ((unsigned)pid >= (unsigned)p.num_pages) { bad = true; pid = 0; }
       base = g + (size_t)pid * kPage * kv_rowb + (size_t)kvh * C::ROWB;
       nrec = (kPage - 1) * kv_rowb + C::ROWB;
     } else {
@@ -340,22 +377,23 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillPa
     }
   };
 
-  // One tile step; PAR = kt % 2 picks the ring buffers at compile time.
-  //   K(kt+1) is in K ring [PAR^1], V(kt) in V ring [PAR]; this step starts the
-  //   DMA of K(kt+2) into K ring [PAR] and of V(kt+1) into V ring [PAR^1].
-  // FAST steps are the steady state: no row of any wave masks tile kt, and
-  // every wave needs tile kt + 1.
+  // One tile step.  SLOT = kt % R picks the ring slots at compile time: K(kt+1)
+  // is in slot kt+1, V(kt) in slot kt; this step starts the DMA of V(kt+R-1)
+  // into slot kt-1 and of K(kt+R) into slot kt, both last read in the step
+  // before.  FAST steps are the steady state: no row of any wave masks tile
+  // kt, and every wave needs tile kt + 1.
   f32x16 sa[C::KB], sb[C::KB];
-  auto step = [&](auto par_tag, auto fast_tag, int kt, f32x16 (&scur)[C::KB],
+  int pid_v = 0, pid_k = 0;     // pages of V(kt+R-1) and K(kt+R) for the next step
+  auto step = [&](auto slot_tag, auto fast_tag, int kt, f32x16 (&scur)[C::KB],
                   f32x16 (&snext)[C::KB]) {
-    constexpr int PAR = decltype(par_tag)::value;
+    constexpr int SLOT = decltype(slot_tag)::value;
     constexpr bool FAST = decltype(fast_tag)::value != 0;
-    char* const KCUR = PAR ? k_ring1 : k_ring0;
-    char* const KNXT = PAR ? k_ring0 : k_ring1;
-    char* const VCUR = PAR ? v_ring1 : v_ring0;
-    char* const VNXT = PAR ? v_ring0 : v_ring1;
-    if (kt + 2 < n_kt) dma(kt + 2, KCUR, false);
-    if (kt + 1 < n_kt) dma(kt + 1, VNXT, true);
+    char* const KDST = kslot(Idx<SLOT>{});
+    char* const KNXT = kslot(Idx<SLOT + 1>{});
+    char* const VCUR = vslot(Idx<SLOT>{});
+    char* const VDST = vslot(Idx<SLOT + C::R - 1>{});
+    if (kt + C::R - 1 < n_kt) dma(kt + C::R - 1, VDST, true, pid_v);
+    if (kt + C::R < n_kt) dma(kt + C::R, KDST, false, pid_k);
     bf16x8 pb[C::PS];
     if constexpr (FAST) {
       // One block in which the S^T(kt+1) MFMAs hide the exponentials of tile kt.
@@ -392,11 +430,25 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillPa
       weights(scur, pb, m == kNegInf ? 0.f : -m);
       pv(VCUR, pb);
     }
-    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this wave's DMA has landed
-    __syncthreads();                      // ... and every wave's; ring slots are free
+    if constexpr (PAGED) {
+      pid_v = pid_k;
+      if (kt + C::R + 1 < n_kt) pid_k = load_pid(kt + C::R + 1);
+    }
+    // Next step reads K(kt+2) and V(kt+1), issued R-2 steps before this one;
+    // the DMAs of the R-2 steps since (two tiles each) may stay in flight.
+    if (C::R > 2 && kt + C::R < n_kt)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::R - 2) * 2 * C::DMA));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wave's LDS reads (and page ids) are done
+    // Every wave's DMA for the next step has landed and every read of the
+    // slots refilled next has completed.  (A workgroup fence here would also
+    // wait for the DMAs still in flight, so the barrier stands alone; the
+    // memory clobber keeps the compiler from moving LDS accesses across it.)
+    asm volatile("s_barrier" ::: "memory");
   };
 
-  // Steady-state steps: [0, n_fast), an even count.  Wave 0 has the fewest
+  // Steady-state steps: [0, n_fast), a multiple of R.  Wave 0 has the fewest
   // unmasked and needed tiles (its rows come first); waves past the last
   // row compute on zero queries and store nothing.
   int n_fast = t_full;
@@ -404,27 +456,43 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillPa
   {
     const int wkend0 = p.causal ? max(0, min(Lk, min(r0 + 31, Lq - 1) + off + 1)) : Lk;
     const int w_kt0 = min(n_kt, (wkend0 + C::BN - 1) / C::BN);
-    n_fast = min(n_fast, w_kt0 - 1) & ~1;
+    n_fast = max(0, min(n_fast, w_kt0 - 1));
+    n_fast -= n_fast % C::R;
   }
 
-  // prologue: K(0), V(0), K(1) in LDS, S^T(0) in registers
-  if (n_kt > 0) {
-    dma(0, k_ring0, false);
-    dma(0, v_ring0, true);
-    if (n_kt > 1) dma(1, k_ring1, false);
-    __builtin_amdgcn_s_waitcnt(0x3f70);
+  // prologue: K(0 .. R-1) and V(0 .. R-2) in LDS, S^T(0) in registers
+#pragma unroll
+  for (int t = 0; t < C::R; ++t) {
+    if (t < n_kt) {
+      const int pid = load_pid(t);
+      char* kd = t == 0 ? kslot(Idx<0>{}) : t == 1 ? kslot(Idx<1>{}) : t == 2 ? kslot(Idx<2>{}) : kslot(Idx<3>{});
+      char* vd = t == 0 ? vslot(Idx<0>{}) : t == 1 ? vslot(Idx<1>{}) : t == 2 ? vslot(Idx<2>{}) : vslot(Idx<3>{});
+      dma(t, kd, false, pid);
+      if (t + 1 < C::R) dma(t, vd, true, pid);
+      else pid_v = pid;
+    }
   }
+  if (C::R < n_kt) pid_k = load_pid(C::R);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
   if (n_kt > 0) qk(k_ring0, sa);
-  __syncthreads();   // every wave is done with K(0) before step 0 refills its buffer
+  __syncthreads();   // every wave is done with K(0) before step 0 refills its slot
   int kt = 0;
-  for (; kt < n_fast; kt += 2) {
-    step(Par0{}, Par1{}, kt, sa, sb);
-    step(Par1{}, Par1{}, kt + 1, sb, sa);
+  for (; kt < n_fast; kt += C::R) {
+    step(Idx<0>{}, Idx<1>{}, kt, sa, sb);
+    step(Idx<1>{}, Idx<1>{}, kt + 1, sb, sa);
+    if constexpr (C::R == 4) {
+      step(Idx<2>{}, Idx<1>{}, kt + 2, sa, sb);
+      step(Idx<3>{}, Idx<1>{}, kt + 3, sb, sa);
+    }
   }
-  for (; kt < n_kt; kt += 2) {
-    step(Par0{}, Par0{}, kt, sa, sb);
-    if (kt + 1 < n_kt) step(Par1{}, Par0{}, kt + 1, sb, sa);
+  for (; kt < n_kt; kt += C::R) {
+    step(Idx<0>{}, Idx<0>{}, kt, sa, sb);
+    if (kt + 1 < n_kt) step(Idx<1>{}, Idx<0>{}, kt + 1, sb, sa);
+    if constexpr (C::R == 4) {
+      if (kt + 2 < n_kt) step(Idx<2>{}, Idx<0>{}, kt + 2, sa, sb);
+      if (kt + 3 < n_kt) step(Idx<3>{}, Idx<0>{}, kt + 3, sb, sa);
+    }
   }
 
   const bool any_bad = __syncthreads_or(bad);
@@ -456,7 +524,7 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(PrefillPa
 template <int D, bool PAGED>
 hipError_t launch_t(const PrefillParams& p, hipStream_t s) {
   dim3 grid(p.Hq, p.B, p.q_tiles);
-  hipLaunchKernelGGL((prefill_kernel<D, PAGED>), grid, dim3(NT), 0, s, p);
+  hipLaunchKernelGGL((prefill_kernel<D, PAGED>), grid, dim3(NT), 0, s, p, p.page_table);
   return hipGetLastError();
 }
 
