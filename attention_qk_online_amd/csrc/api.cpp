@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -248,6 +249,12 @@ static attn_status check_prefill_common(attn_dtype dtype, int B, int Hq, int Hkv
   if (!attn::prefill_supported((int)dtype, D))
     return fail(ATTN_E_UNSUPPORTED, "prefill: dtype=%d D=%d not built (bf16, D in {128,256})",
                 dtype, D);
+  // One workgroup per (query head, sequence, query tile), indexed by an int.
+  const long long items =
+      (long long)Hq * B * ((max_seqlen_q + attn::kPrefillBM - 1) / attn::kPrefillBM);
+  if (items > INT_MAX - 8)
+    return fail(ATTN_E_SHAPE, "Hq x B x ceil(max_seqlen_q / %d) = %lld work items exceeds %d",
+                attn::kPrefillBM, items, INT_MAX - 8);
   return ATTN_OK;
 }
 

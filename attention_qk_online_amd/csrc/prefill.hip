@@ -134,13 +134,27 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
 
-  // Heads that share a KV head land on the same XCD (workgroups are dealt
-  // round-robin over the 8 XCDs, each with its own L2).
-  const int x = blockIdx.x;
-  const int head = (p.Hq % 8 == 0) ? (x % 8) * (p.Hq / 8) + x / 8 : x;
-  const int kvh = head / (p.Hq / p.Hkv);
-  const int b = blockIdx.y;
-  const int tile = p.q_tiles - 1 - (int)blockIdx.z;   // heaviest causal tiles first
+  // Work order.  Workgroups are dealt round-robin over the 8 XCDs (each with
+  // its own L2); XCD c takes the c-th contiguous eighth of the work items
+  // ordered by (KV head, sequence, query tile heaviest first, query head of
+  // the KV head's group).  Workgroups running together on one XCD then share
+  // their K/V reads: the query heads of one KV head, the tiles of one sequence.
+  int head, kvh, b, tile;
+  {
+    const int G = p.Hq / p.Hkv;
+    const int total = p.Hq * p.B * p.q_tiles;          // fits an int (checked on the host)
+    const int chunk = (total + 7) / 8;
+    const int w = blockIdx.x;
+    int r = (w % 8) * chunk + w / 8;
+    if (r >= total) return;
+    const int hg = r % G;
+    r /= G;
+    tile = p.q_tiles - 1 - r % p.q_tiles;
+    r /= p.q_tiles;
+    b = r % p.B;
+    kvh = r / p.B;
+    head = kvh * G + hg;
+  }
 
   // Sequence extents, clamped so every access stays inside the tensors.
   const int q_start = min(max(p.cu_q[b], 0), p.total_q);
@@ -523,7 +537,8 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
 
 template <int D, bool PAGED>
 hipError_t launch_t(const PrefillParams& p, hipStream_t s) {
-  dim3 grid(p.Hq, p.B, p.q_tiles);
+  const int total = p.Hq * p.B * p.q_tiles;
+  dim3 grid(8 * ((total + 7) / 8));
   hipLaunchKernelGGL((prefill_kernel<D, PAGED>), grid, dim3(NT), 0, s, p, p.page_table);
   return hipGetLastError();
 }

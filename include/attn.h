@@ -135,7 +135,8 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pag
  *
  * Query tiles of 128 rows run on bf16 MFMA with fp32 accumulation; K/V tiles
  * are staged through LDS; tiles wholly above the causal diagonal are never
- * loaded.  Supported: dtype BF16; D in {128, 256}; any Hq multiple of Hkv.
+ * loaded.  Supported: dtype BF16; D in {128, 256}; any Hq multiple of Hkv;
+ * Hq * B * ceil(max_seqlen_q / 128) below 2^31 - 8 (else ATTN_E_SHAPE).
  * Rows of out/lse outside every [cu_seqlens_q[b], cu_seqlens_q[b+1]) are
  * not written.
  */
@@ -159,7 +160,8 @@ attn_status attn_prefill_varlen(attn_dtype dtype, const void* q, const void* k, 
  *  max_seqlen_q, max_kv_len  host bounds
  *  out [total_q, Hq, D] bf16;  lse [total_q, Hq] float
  *
- * Supported: dtype BF16; D in {128, 256}; page_size 16.
+ * Supported: dtype BF16; D in {128, 256}; page_size 16; the same work-item
+ * bound as attn_prefill_varlen.
  */
 attn_status attn_prefill_paged(attn_dtype dtype, const void* q, const int32_t* cu_seqlens_q,
                                const void* k_pages, const void* v_pages,

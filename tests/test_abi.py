@@ -121,6 +121,7 @@ def _prefill(lib, **kw):
     (dict(cq=None), E_NULL),
     (dict(out=None), E_NULL),
     (dict(k=24), E_UNSUP),
+    (dict(B=1 << 14, Hq=1 << 10, Hkv=1 << 10, mq=1 << 15), E_SHAPE),   # > INT_MAX work items
 ])
 def test_prefill_rejects(lib, kw, status):
     assert _prefill(lib, **kw) == status
