@@ -51,7 +51,8 @@ constexpr int NWAVE = 4;
 constexpr int NT = NWAVE * 64;
 constexpr int kPage = 16;
 constexpr float kRescaleSlack = 8.f;   // log2 units the running max may lag behind
-constexpr int kBufferWord3 = 0x00020000;   // buffer descriptor word 3 for gfx950 (32-bit data format)
+constexpr int kBufferWord3 = 0x00020000;
+   // buffer descriptor word 3 for gfx950 (32-bit data format)
 
 template <int D>
 struct Cfg {
@@ -391,6 +392,69 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
     }
   };
 
+  // Steady-state body written in issue order: the S^T(kt+1) MFMAs, each with
+  // the next K fragment read PF ahead and a share of tile kt's exponentials,
+  // then the O^T MFMAs with V^T fragments read PF ahead.  Used for head_dim
+  // 256, whose one wave per SIMD leaves the compiler no room to reorder.
+  auto fused = [&](const char* kbuf, const char* vbuf, f32x16 (&scur)[C::KB],
+                   f32x16 (&snext)[C::KB], bf16x8 (&pb)[C::PS]) {
+    constexpr int NQ = C::KB * C::QK;       // S^T MFMAs
+    constexpr int NE = C::KB * 16;          // weights per lane
+    constexpr int EPM = NE / NQ;            // weights per S^T MFMA
+    constexpr int PF = 2;                   // fragments in flight (measured best)
+    const float nm = -m;
+    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+    auto kfrag = [&](int i) {
+      const int kb = i / C::QK, ks = i % C::QK;
+      return *reinterpret_cast<const bf16x8*>(kbuf + kb * 32 * C::ROWB + (ks >> 3) * 256 + kro[ks & 7]);
+    };
+    bf16x8 kf[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) kf[i] = kfrag(i);
+    f32x16 acc[C::KB];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) acc[kb] = f32x16{};
+    float psum = 0.f;
+    bf16x8 w;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int kb = i / C::QK, ks = i % C::QK;
+      acc[kb] = mfma32(kf[i % PF], qf[ks], acc[kb]);
+      if (i + PF < NQ) kf[i % PF] = kfrag(i + PF);
+#pragma unroll
+      for (int e = 0; e < EPM; ++e) {
+        const int idx = i * EPM + e;
+        w[idx % 8] = (__bf16)exp2_fast(__builtin_fmaf(scur[idx / 16][idx % 16], c, nm));
+        if (idx % 8 == 7) {
+#pragma unroll
+          for (int t = 0; t < 8; t += 2)
+            psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w[t], w[t + 1]}, one, psum, false);
+          pb[idx / 8] = w;
+        }
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) snext[kb] = acc[kb];
+    lsum += psum;
+    constexpr int NP = C::DB * C::PS;       // O^T MFMAs
+    auto vfrag = [&](int j) {
+      const int db = j / C::PS, ps = j % C::PS;
+      const int ro = ps * 16 * C::ROWB + (db >> 2) * 256 + vro[db & 3];
+      v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_char*)vbuf + ro));
+      v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_char*)vbuf + ro + 8 * C::ROWB));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 vf[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) vf[j] = vfrag(j);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+      const int db = j / C::PS, ps = j % C::PS;
+      o[db] = mfma32(vf[j % PF], pb[ps], o[db]);
+      if (j + PF < NP) vf[j % PF] = vfrag(j + PF);
+    }
+  };
+
   // One tile step.  SLOT = kt % R picks the ring slots at compile time: K(kt+1)
   // is in slot kt+1, V(kt) in slot kt; this step starts the DMA of V(kt+R-1)
   // into slot kt-1 and of K(kt+R) into slot kt, both last read in the step
@@ -409,7 +473,10 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
     if (kt + C::R - 1 < n_kt) dma(kt + C::R - 1, VDST, true, pid_v);
     if (kt + C::R < n_kt) dma(kt + C::R, KDST, false, pid_k);
     bf16x8 pb[C::PS];
-    if constexpr (FAST) {
+    if constexpr (FAST && D == 256) {
+      update_max(scur);
+      fused(KNXT, VCUR, scur, snext, pb);
+    } else if constexpr (FAST) {
       // One block in which the S^T(kt+1) MFMAs hide the exponentials of tile kt.
       update_max(scur);
       qk(KNXT, snext);
