@@ -50,6 +50,9 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also time the 1K-32K single-sequence sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="finish with three plain device-to-device copies of MIB MiB, the "
+                         "reference for HBM byte counters read under a profiler")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -72,7 +75,7 @@ def main():
     d_lse = torch.empty((dec.B, dec.Hq), dtype=torch.float32, device=dev)
     ws_bytes = A.decode_paged_workspace_size(dec.dtype, dec.B, dec.Hq, dec.Hkv, dec.D, dec.page_size,
                                              dec.max_kv_len, 0)
-    d_ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    d_ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)   # zero on first use
 
     pre = workloads.make_config(3)
     p_q, p_k, p_v = pre.q.to(dev), pre.k.to(dev), pre.v.to(dev)
@@ -134,8 +137,8 @@ def main():
     ms_decode, ms_prefill, ms_paged = seg
 
     def avg(kind):
-        ms, n = kt[kind]
-        return ms / n if n else float("nan")
+        ms, n = kt.get(kind, (0.0, 0))
+        return ms / n if n else None
 
     kv_bytes = dec.kv_bytes()
     pre_flops = pre.flops()
@@ -145,15 +148,15 @@ def main():
     paged_ms = avg("prefill_paged")
     decode_gbs = kv_bytes / (ms_decode * 1e-3) / 1e9
 
-    def roofline_hbm(nbytes, ms):
+    def roofline_hbm(nbytes, ms, kernel):
         a = nbytes / (ms * 1e-3) / 1e9
         return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": measured_traffic(kernel)}
 
-    def roofline_mfma(flops, ms):
+    def roofline_mfma(flops, ms, kernel):
         a = flops / (ms * 1e-3) / 1e12
         return {"bound": "mfma", "achieved": round(a, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(a / BF16_PEAK_TFLOPS, 4), "traffic": None}
+                "frac": round(a / BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(kernel)}
 
     res = {
         "metric": METRIC,
@@ -173,22 +176,23 @@ def main():
                    "sum_kv_len": int(dec.kv_lens.sum()), "kv_bytes": kv_bytes,
                    "step": "paged decode + ragged causal prefill + chunked paged prefill"},
         "decode": {"call_ms": round(ms_decode, 5), "split_kernel_ms": round(split_ms, 5),
-                   "combine_kernel_ms": round(avg("decode_combine"), 5),
+                   "combine_kernel_ms": None if avg("decode_combine") is None
+                   else round(avg("decode_combine"), 5),
                    "frac_of_hbm_peak": round(decode_gbs / HBM_PEAK_GBS, 4)},
-        "roofline": roofline_hbm(kv_bytes, split_ms),
+        "roofline": roofline_hbm(kv_bytes, split_ms, "decode_split"),
         "prefill": {
             "metric": "causal prefill TFLOPS", "unit": "TFLOP/s",
             "value": round(pre_flops / (ms_prefill * 1e-3) / 1e12, 2),
             "workload": workloads.CONFIG_NAMES[3], "flops": pre_flops,
             "call_ms": round(ms_prefill, 4), "kernel_ms": round(prefill_ms, 4),
-            "roofline": roofline_mfma(pre_flops, prefill_ms),
+            "roofline": roofline_mfma(pre_flops, prefill_ms, "prefill"),
         },
         "prefill_paged": {
             "metric": "chunked paged prefill TFLOPS", "unit": "TFLOP/s",
             "value": round(pg_flops / (ms_paged * 1e-3) / 1e12, 2),
             "workload": workloads.CONFIG_NAMES[5], "flops": pg_flops,
             "call_ms": round(ms_paged, 4), "kernel_ms": round(paged_ms, 4),
-            "roofline": roofline_mfma(pg_flops, paged_ms),
+            "roofline": roofline_mfma(pg_flops, paged_ms, "prefill_paged"),
         },
     }
 
@@ -223,7 +227,61 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(dec, args.cpu_seconds)
 
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["calibrate_copy_bytes"] = n
+
     print(json.dumps(res), flush=True)
+
+
+# Measured HBM traffic per launch (FETCH_SIZE + WRITE_SIZE under rocprofv3,
+# scaled by what the same counters read for a plain copy of known size) is
+# kept in a profile summary together with the SHA-256 of the sources it was
+# measured on; it is reported only while those sources are unchanged.
+TRAFFIC_FILES = {
+    "decode_split": "profiles/traffic__decode_split__paged_decode_b64_hq32_hkv8_d128.md",
+    "prefill": "profiles/traffic__prefill__ragged_causal_b8_hq64_hkv8_d128.md",
+    "prefill_paged": "profiles/traffic__prefill_paged__chunked_b16_q512_kv8704_h16_d256.md",
+}
+KERNEL_SOURCES = {
+    "decode_split": ["decode.hip"],
+    "prefill": ["prefill.hip"],
+    "prefill_paged": ["prefill.hip"],
+}
+
+
+def source_digest(kind):
+    """SHA-256 over the sources that build one kernel (its .hip file plus the
+    shared headers and the host-side launch code)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "attention_qk_online_amd", "csrc")
+    for name in KERNEL_SOURCES[kind] + ["common.h", "launch.h", "api.cpp"]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kind):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, TRAFFIC_FILES[kind])
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    start = text.find("```json")
+    if start < 0:
+        return None
+    rec = json.loads(text[start + 7:text.index("```", start + 7)])
+    if rec.get("source_sha256") != source_digest(kind):
+        return None
+    return int(rec["hbm_bytes_per_launch"])
 
 
 def cpu_baseline(dec, seconds):
@@ -231,7 +289,8 @@ def cpu_baseline(dec, seconds):
     repeated until at least ``seconds`` have passed; GB/s of algorithmic KV bytes."""
     import torch
     import oracle
-    torch.set_num_threads(os.cpu_count() or 1)
+    # The host's CPU share: OMP_NUM_THREADS when set, else at most 16 threads.
+    torch.set_num_threads(int(os.environ.get("OMP_NUM_THREADS") or min(16, os.cpu_count() or 1)))
     log("bench: cpu baseline (oracle)")
     # The oracle only reads referenced pages, so the pool is left unfilled elsewhere.
     shape = (dec.num_pages, dec.page_size, dec.Hkv, dec.D)

@@ -145,3 +145,24 @@ def test_paged_config_full(gpu, paged_config, split_pages):
     case, pools, ro, rl = paged_config
     out, lse = _run(case, gpu, split_pages=split_pages, pools=pools)
     assert_parity(out, lse, ro, rl, torch.bfloat16, f"{case.name} split_pages={split_pages}")
+
+
+def test_workspace_contents_do_not_matter(gpu):
+    """One caller workspace, filled with NaN bit patterns, reused across bf16 calls
+    of different shapes and run lengths: every result equals a fresh-workspace
+    call bit for bit."""
+    import attention_qk_online_amd as A
+    c1 = workloads.make_decode(B=8, Hq=8, Hkv=2, D=128, page_size=16,
+                               kv_lens=[700, 1, 33, 512, 0, 129, 64, 1000], dtype=torch.bfloat16,
+                               seed=410, extra_pages=5)
+    c2 = workloads.make_decode(B=5, Hq=16, Hkv=4, D=128, page_size=16, kv_lens=[300, 2048, 17, 5, 900],
+                               dtype=torch.bfloat16, seed=411, extra_pages=3)
+    ws = torch.full((1 << 22,), 0xFF, dtype=torch.uint8, device=gpu)
+    for case, split in ((c1, 2), (c2, 0), (c1, 8), (c2, 1)):
+        kp, vp = case.pools(gpu)
+        args = (case.q.to(gpu), kp, vp, case.page_table.to(gpu), case.kv_lens.to(gpu))
+        kw = dict(scale=case.scale, max_kv_len=case.max_kv_len, split_pages=split)
+        o_ref, l_ref = A.decode_paged(*args, **kw)
+        out, lse = A.decode_paged(*args, workspace=ws, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_ref) and torch.equal(lse, l_ref), (case.name, split)
