@@ -13,14 +13,19 @@ already resident in HBM:
 
 The headline value is decode KV throughput (algorithmic K+V bytes / decode
 call time, GB/s); prefill TFLOPS (algorithmic causal flops / call time) is
-reported beside it.  Call times come from one event pair per segment of the
-timed steps; per-kernel durations (the roofline figures) from a second pass
-in which the library records HIP events around each of its launches on the
-launch stream.  The CPU
-oracle is timed on the host cores over the whole decode workload (repeated
-to at least ~10 s), as a reported baseline.
+reported beside it.  Before each timed segment a 1 GiB scratch buffer is
+read (outside the segment's event pair) so every call starts with the inputs
+in HBM but not in the MALL or the L2s.  Call times come from one event
+pair per segment of the timed steps (mean, median and minimum); per-kernel
+durations (the roofline figures) from a second pass in which the library
+records HIP events around each of its launches on the launch stream.  Also
+reported: the launch-bound fp32 single-sequence decode and the 1K-32K
+single-sequence causal prefill sweep.  The CPU oracle is timed on the host
+cores over the whole decode workload (repeated to at least ~10 s), as a
+reported baseline.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-flush]
+                       [--no-cpu-baseline] [--calibrate-copy MIB]
 Prints one JSON line.
 """
 import argparse
@@ -47,7 +52,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--sweep", action="store_true", help="also time the 1K-32K single-sequence sweep")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 1K-32K single-sequence sweep")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not read a 1 GiB scratch buffer before each timed segment")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -102,6 +109,16 @@ def main():
         A.prefill_paged(g_q, g_cq, g_kp, g_vp, g_table, g_lens, pg.max_seqlen_q, pg.max_kv_len,
                         causal=True, scale=pg.scale, out=g_out, lse=g_lse)
 
+    # Before each timed segment (outside its event pair) a 1 GiB scratch buffer
+    # is read, which evicts the inputs from the 256 MB MALL and the L2s and
+    # leaves clean lines behind (a write would leave dirty ones whose
+    # write-back then competes with the timed call).
+    scratch = None if args.no_flush else torch.ones(1 << 28, dtype=torch.int32, device=dev)
+
+    def flush():
+        if scratch is not None:
+            scratch.sum()
+
     stream = torch.cuda.current_stream(dev)
     log("bench: warmup")
     for _ in range(args.warmup):
@@ -115,14 +132,13 @@ def main():
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev_end = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     for i in range(K):
-        ev[i][0].record(stream)
-        decode()
-        ev[i][1].record(stream)
-        prefill()
-        ev[i][2].record(stream)
-        paged()
-        ev[i][3].record(stream)
+        for j, seg in enumerate((decode, prefill, paged)):
+            flush()
+            ev[i][j].record(stream)
+            seg()
+            ev_end[i][j].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     log("bench: timed", K, "steps in", t1 - t0, "s")
@@ -130,11 +146,17 @@ def main():
     # of its kernel launches by HIP events on the launch stream.
     A.timing_begin(8 * K + 16)
     for i in range(K):
-        decode(); prefill(); paged()
+        for seg in (decode, prefill, paged):
+            flush()
+            seg()
     kt = A.timing_end()
 
-    seg = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K for j in range(3)]
-    ms_decode, ms_prefill, ms_paged = seg
+    seg_ms = [sorted(ev[i][j].elapsed_time(ev_end[i][j]) for i in range(K)) for j in range(3)]
+
+    def stats(ms):
+        return {"mean": round(sum(ms) / len(ms), 5), "median": round(ms[len(ms) // 2], 5),
+                "min": round(ms[0], 5)}
+    ms_decode, ms_prefill, ms_paged = (sum(x) / len(x) for x in seg_ms)
 
     def avg(kind):
         ms, n = kt.get(kind, (0.0, 0))
@@ -175,7 +197,9 @@ def main():
                    "D": dec.D, "page_size": dec.page_size, "pool_pages": dec.num_pages,
                    "sum_kv_len": int(dec.kv_lens.sum()), "kv_bytes": kv_bytes,
                    "step": "paged decode + ragged causal prefill + chunked paged prefill"},
-        "decode": {"call_ms": round(ms_decode, 5), "split_kernel_ms": round(split_ms, 5),
+        "cache_flush_bytes": 0 if scratch is None else scratch.numel() * 4,
+        "decode": {"call_ms": round(ms_decode, 5), "call_ms_stats": stats(seg_ms[0]),
+                   "split_kernel_ms": round(split_ms, 5),
                    "combine_kernel_ms": None if avg("decode_combine") is None
                    else round(avg("decode_combine"), 5),
                    "frac_of_hbm_peak": round(decode_gbs / HBM_PEAK_GBS, 4)},
@@ -184,19 +208,46 @@ def main():
             "metric": "causal prefill TFLOPS", "unit": "TFLOP/s",
             "value": round(pre_flops / (ms_prefill * 1e-3) / 1e12, 2),
             "workload": workloads.CONFIG_NAMES[3], "flops": pre_flops,
-            "call_ms": round(ms_prefill, 4), "kernel_ms": round(prefill_ms, 4),
+            "call_ms": round(ms_prefill, 4), "call_ms_stats": stats(seg_ms[1]),
+            "kernel_ms": round(prefill_ms, 4),
             "roofline": roofline_mfma(pre_flops, prefill_ms, "prefill"),
         },
         "prefill_paged": {
             "metric": "chunked paged prefill TFLOPS", "unit": "TFLOP/s",
             "value": round(pg_flops / (ms_paged * 1e-3) / 1e12, 2),
             "workload": workloads.CONFIG_NAMES[5], "flops": pg_flops,
-            "call_ms": round(ms_paged, 4), "kernel_ms": round(paged_ms, 4),
+            "call_ms": round(ms_paged, 4), "call_ms_stats": stats(seg_ms[2]),
+            "kernel_ms": round(paged_ms, 4),
             "roofline": roofline_mfma(pg_flops, paged_ms, "prefill_paged"),
         },
     }
 
-    if args.sweep:
+    # Single-sequence fp32 decode (1 query token, 4 heads, head_dim 64, 256
+    # contiguous keys as an identity-paged NHD view): launch-latency bound.
+    one = workloads.make_config(1)
+    o_kp, o_vp = one.pools(dev)
+    o_q, o_t, o_l = one.q.to(dev), one.page_table.to(dev), one.kv_lens.to(dev)
+
+    def single():
+        A.decode_paged(o_q, o_kp, o_vp, o_t, o_l, scale=one.scale, max_kv_len=one.max_kv_len)
+    for _ in range(5):
+        single()
+    torch.cuda.synchronize()
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    for i in range(K):
+        e0[i].record(stream)
+        single()
+        e1[i].record(stream)
+    torch.cuda.synchronize()
+    one_ms = sorted(e0[i].elapsed_time(e1[i]) for i in range(K))
+    res["decode_fp32_single"] = {
+        "workload": workloads.CONFIG_NAMES[1], "kv_bytes": one.kv_bytes(),
+        "call_us_median": round(one_ms[K // 2] * 1e3, 2), "call_us_min": round(one_ms[0] * 1e3, 2),
+        "GBs_at_median": round(one.kv_bytes() / (one_ms[K // 2] * 1e-3) / 1e9, 2),
+        "note": "launch-latency bound (512 KiB of KV); includes the binding's output allocation"}
+
+    if not args.no_sweep:
         del p_q, p_k, p_v, p_out, p_lse
         long = workloads.make_config(4)
         q, k, v = long.q.to(dev), long.k.to(dev), long.v.to(dev)
