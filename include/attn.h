@@ -43,10 +43,14 @@
  *    attn_last_error() then describes the failure (thread-local text).
  *    Device-resident index data (page tables, lengths, cu_seqlens) cannot be
  *    checked on the host without a sync, so the kernels clamp it instead:
- *    every memory access stays inside the sizes passed here, and a request
- *    whose device data are inconsistent (a page id outside [0, num_pages), a
- *    kv_len above max_kv_len or max_pages_per_req * page_size, a length
- *    above max_seqlen_*) gets NaN in its out and lse rows.
+ *    every memory access stays inside the sizes passed here, and output
+ *    computed from inconsistent device data is NaN.  Decode: a request with
+ *    a page id outside [0, num_pages) or a kv_len above max_kv_len or
+ *    max_pages_per_req * page_size gets NaN in all its out and lse rows.
+ *    Prefill: rows whose visible keys reach an out-of-range page id, and the
+ *    rows of a sequence longer than max_seqlen_q (or whose kv_len exceeds
+ *    max_pages_per_req * page_size), are NaN; of such a sequence only its
+ *    first ceil(max_seqlen_q / 128) * 128 rows are written.
  */
 #ifndef ATTN_H
 #define ATTN_H

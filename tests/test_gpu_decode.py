@@ -166,3 +166,18 @@ def test_workspace_contents_do_not_matter(gpu):
         out, lse = A.decode_paged(*args, workspace=ws, **kw)
         torch.cuda.synchronize()
         assert torch.equal(out, o_ref) and torch.equal(lse, l_ref), (case.name, split)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_many_requests(gpu, dtype):
+    """More than 64 requests: the device-side schedule scans kv_lens 64 at a time."""
+    g = torch.Generator().manual_seed(420)
+    lens = torch.randint(0, 300, (150,), generator=g).tolist()
+    lens[7] = 0
+    lens[100] = 1
+    case = workloads.make_decode(B=150, Hq=8, Hkv=2, D=128, page_size=16, kv_lens=lens, dtype=dtype,
+                                 seed=421, extra_pages=4)
+    for split in (0, 3):
+        out, lse = _run(case, gpu, split)
+        ro, rl = _oracle(case)
+        assert_parity(out, lse, ro, rl, dtype, f"B150 {dtype} split{split}")

@@ -174,3 +174,65 @@ def test_chunked_paged_config_sampled(gpu):
                                       case.page_table, case.kv_lens, True, case.scale, rows=rows)
     assert_parity(out, lse, ro, rl, torch.bfloat16, case.name + " (sampled rows)", rows=rows)
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3])
+def test_zero_and_negative_scale(gpu, scale):
+    """scale 0: every visible key weighs the same; a negative scale flips the scores."""
+    case = workloads.make_prefill(B=2, Hq=4, Hkv=2, D=128, lens_q=[200, 77], dtype=torch.bfloat16,
+                                  seed=280, causal=True, scale=scale)
+    out, lse = _varlen(case, gpu)
+    ro, rl = _ref(case)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, f"scale {scale}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_q_and_k_lengths_differ(gpu, causal):
+    """Lq != Lk in both directions, with and without the (bottom-right) causal mask, D 256."""
+    case = workloads.make_prefill(B=4, Hq=4, Hkv=1, D=256, lens_q=[50, 300, 129, 1],
+                                  lens_k=[400, 140, 129, 33], dtype=torch.bfloat16, seed=290,
+                                  causal=causal)
+    out, lse = _varlen(case, gpu)
+    ro, rl = _ref(case)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, f"Lq!=Lk causal={causal}")
+
+
+def test_group_of_sixteen_and_many_sequences(gpu):
+    """16 query heads per KV head; 100 short sequences (one work item per head and tile)."""
+    g = torch.Generator().manual_seed(300)
+    lens = torch.randint(1, 200, (100,), generator=g).tolist()
+    case = workloads.make_prefill(B=100, Hq=32, Hkv=2, D=128, lens_q=lens, dtype=torch.bfloat16,
+                                  seed=301, causal=True)
+    out, lse = _varlen(case, gpu)
+    ro, rl = _ref(case)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, "G16 B100")
+
+
+def test_overlong_sequence_is_nan(gpu):
+    """A sequence longer than max_seqlen_q: the rows the launch covers are NaN; other
+    sequences are unaffected."""
+    import attention_qk_online_amd as A
+    case = workloads.make_prefill(B=2, Hq=4, Hkv=2, D=128, lens_q=[100, 300], dtype=torch.bfloat16,
+                                  seed=310, causal=True)
+    out, lse = A.prefill_varlen(case.q.to(gpu), case.k.to(gpu), case.v.to(gpu),
+                                case.cu_seqlens_q.to(gpu), case.cu_seqlens_k.to(gpu), 256, 300,
+                                causal=True, scale=case.scale)
+    torch.cuda.synchronize()
+    ro, rl = _ref(case)
+    assert_parity(out[:100], lse[:100], ro[:100], rl[:100], torch.bfloat16, "good sequence")
+    assert torch.isnan(out[100:356].float()).all() and torch.isnan(lse[100:356]).all()
+
+
+def test_paged_bad_page_is_nan(gpu):
+    """A page id outside the pool: rows whose keys reach it are NaN (here every row of
+    that request, as its chunk sees all cached tokens); other requests are unaffected."""
+    case = workloads.make_paged_prefill(B=2, Hq=4, Hkv=2, D=128, page_size=16, chunk=40, cached=100,
+                                        shared_prefix=0, dtype=torch.bfloat16, seed=320)
+    table = case.page_table.clone()
+    table[1, 2] = case.num_pages + 5
+    out, lse = _paged(case, gpu, table=table)
+    ro, rl = oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, case.pool_k, case.pool_v,
+                                      case.page_table, case.kv_lens, True, case.scale)
+    n0 = int(case.cu_seqlens_q[1])
+    assert_parity(out[:n0], lse[:n0], ro[:n0], rl[:n0], torch.bfloat16, "good request")
+    assert torch.isnan(out[n0:].float()).all() and torch.isnan(lse[n0:]).all()
