@@ -1,29 +1,30 @@
 // Ragged causal prefill for gfx950 on bf16 MFMA with fp32 accumulation.
 //
 // One workgroup = one (query tile of BM = 128 rows, query head) of one
-// sequence; four waves own 32 query rows each, and two workgroups share a CU
-// so that one wave's matrix work overlaps another's vector work.  Key tiles
-// have BN keys (64 for head_dim 128, 32 for head_dim 256).
+// sequence; four waves own 32 query rows each.  Key tiles have BN keys (64
+// for head_dim 128, 32 for head_dim 256).  Head_dim 128 runs two workgroups
+// per CU, so one wave's matrix work overlaps another's vector work; head_dim
+// 256 needs the whole register file and runs one.
 //
 // Data movement: K and V tiles go from HBM straight into LDS with
-// global_load_lds_dwordx4 (no register staging), each into a ring of two
-// buffers.  While tile j is processed, the DMA for K(j+2) and V(j+1) is in
-// flight; one wait and one barrier per tile.  Each lane loads the 16-byte
-// chunk that belongs at its LDS position under an XOR swizzle (K: chunk XOR
-// row mod 16; V: 64-byte block XOR row mod 4), so the MFMA operand reads
-// below hit every bank once.
+// buffer_load_dwordx4 ... lds (no register staging), into rings of R slots
+// (2 for head_dim 128, 4 for head_dim 256): while tile j is processed, the
+// DMA for K(j+R) and V(j+R-1) is in flight; one wait and one barrier per
+// tile.  Each lane loads the 16-byte chunk that belongs at its LDS position
+// under an XOR swizzle (K: chunk XOR row mod 16; V: 64-byte block XOR row mod
+// 4), so the MFMA operand reads below hit every bank once.
 //
-// Per tile j (the loop is unrolled by two so every LDS address is a per-lane
+// Per tile j (the loop is unrolled by R so every LDS address is a per-lane
 // constant plus an immediate):
 //   1. S^T(j+1) = K(j+1) . Q^T on v_mfma_f32_32x32x16_bf16, issued alongside
 //      the softmax of tile j (independent work, interleaved on the SIMD).
 //      Q stays in VGPRs (B operand); the transposed product gives each lane
 //      one query column, so a row max is in-lane plus one lane^32 exchange.
 //   2. Softmax of S^T(j) in log2 units: masks only on tiles crossing the
-//      diagonal or the end of the keys; p = 2^(s*c - m) with one FMA; the
-//      running max m is raised (and O, l rescaled) only when a row's tile
-//      max exceeds it by more than 2^8, so rescaling is rare while p stays
-//      below 256.
+//      diagonal or the end of the keys (a separate, generic step); p =
+//      2^(s*c - m) with one FMA; the running max m is raised (and O, l
+//      rescaled) only when a row's tile max exceeds it by more than 2^8, so
+//      rescaling is rare while p stays below 256.
 //   3. O^T += V^T(j) . P^T(j) on MFMA: the S^T accumulator is already laid
 //      out as the B operand (keys permuted identically on both operands), and
 //      V^T fragments come from the row-major V tile through ds_read_b64_tr_b16.
@@ -51,8 +52,7 @@ constexpr int NWAVE = 4;
 constexpr int NT = NWAVE * 64;
 constexpr int kPage = 16;
 constexpr float kRescaleSlack = 8.f;   // log2 units the running max may lag behind
-constexpr int kBufferWord3 = 0x00020000;
-   // buffer descriptor word 3 for gfx950 (32-bit data format)
+constexpr int kBufferWord3 = 0x00020000;   // buffer descriptor word 3 for gfx950 (32-bit data format)
 
 template <int D>
 struct Cfg {

@@ -306,15 +306,24 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text):
+    """Source text without comments and blank space, so that a comment edit
+    does not count as a kernel change."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(kind):
-    """SHA-256 over the sources that build one kernel (its .hip file plus the
-    shared headers and the host-side launch code)."""
+    """SHA-256 over the code (comments dropped) of the sources that build one
+    kernel: its .hip file plus the shared headers and the host-side launch code."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "attention_qk_online_amd", "csrc")
     for name in KERNEL_SOURCES[kind] + ["common.h", "launch.h", "api.cpp"]:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()
 
 
