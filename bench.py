@@ -241,11 +241,40 @@ def main():
         e1[i].record(stream)
     torch.cuda.synchronize()
     one_ms = sorted(e0[i].elapsed_time(e1[i]) for i in range(K))
+    # The same call captured 20 times back to back in one HIP graph (static
+    # buffers) and replayed: the per-call share of a replay, as when the
+    # decode of many layers is captured together.
+    NG = 20
+    g_out, g_lse = torch.empty_like(o_q), torch.empty(one.B, one.Hq, device=dev)
+
+    def single_static():
+        A.decode_paged(o_q, o_kp, o_vp, o_t, o_l, scale=one.scale, max_kv_len=one.max_kv_len,
+                       out=g_out, lse=g_lse)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        single_static()
+    stream.wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(NG):
+            single_static()
+    graph.replay()
+    torch.cuda.synchronize()
+    for i in range(K):
+        e0[i].record(stream)
+        graph.replay()
+        e1[i].record(stream)
+    torch.cuda.synchronize()
+    rep_ms = sorted(e0[i].elapsed_time(e1[i]) / NG for i in range(K))
     res["decode_fp32_single"] = {
         "workload": workloads.CONFIG_NAMES[1], "kv_bytes": one.kv_bytes(),
         "call_us_median": round(one_ms[K // 2] * 1e3, 2), "call_us_min": round(one_ms[0] * 1e3, 2),
         "GBs_at_median": round(one.kv_bytes() / (one_ms[K // 2] * 1e-3) / 1e9, 2),
-        "note": "launch-latency bound (512 KiB of KV); includes the binding's output allocation"}
+        "graph_us_per_call_median": round(rep_ms[K // 2] * 1e3, 2),
+        "graph_us_per_call_min": round(rep_ms[0] * 1e3, 2),
+        "note": "launch-latency bound (512 KiB of KV). Eager: one event pair around one call "
+                "(host overhead included). Graph: 20 calls captured in one graph, replay time / 20"}
 
     if not args.no_sweep:
         del p_q, p_k, p_v, p_out, p_lse
