@@ -35,7 +35,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libattn.so")
 _lib = None
 
-ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
 KERNEL_KINDS = ("decode_split", "decode_combine", "prefill", "prefill_paged")
 _STATUS = {0: "ok", 1: "null", 2: "shape", 3: "dtype", 4: "unsupported", 5: "value",
            6: "workspace", 7: "hip"}
@@ -103,7 +103,9 @@ def _dtype_code(t: torch.Tensor) -> int:
         return ATTN_F32
     if t.dtype == torch.bfloat16:
         return ATTN_BF16
-    raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    if t.dtype == torch.float16:
+        return ATTN_F16
+    raise ValueError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float16)")
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None, dim=None) -> int:
@@ -133,7 +135,9 @@ def _scale(scale: Optional[float], D: int) -> float:
 
 def decode_paged_workspace_size(dtype: torch.dtype, B: int, Hq: int, Hkv: int, D: int,
                                 page_size: int, max_kv_len: int, split_pages: int = 0) -> int:
-    code = ATTN_F32 if dtype == torch.float32 else ATTN_BF16
+    code = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}.get(dtype)
+    if code is None:
+        raise ValueError(f"unsupported dtype {dtype} (float32, bfloat16 or float16)")
     return int(load_library().attn_decode_paged_workspace_size(code, B, Hq, Hkv, D, page_size,
                                                                max_kv_len, split_pages))
 

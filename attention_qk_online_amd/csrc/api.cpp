@@ -92,7 +92,7 @@ DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int D, int page_size, 
                        int split_pages) {
   DecodePlan pl{};
   const int max_pages = page_size > 0 ? (max_kv_len + page_size - 1) / page_size : 0;
-  if (dtype == ATTN_BF16) {
+  if (dtype == ATTN_BF16 || dtype == ATTN_F16) {
     // A (request, KV head) pair of at most max_pages units spans at most
     // ceil(max_pages / run) + 1 runs, and every run has >= min_run units.
     pl.split_pages = split_pages;
@@ -128,7 +128,7 @@ int device_cus() {
   return n;
 }
 
-bool dtype_ok(attn_dtype d) { return d == ATTN_F32 || d == ATTN_BF16; }
+bool dtype_ok(attn_dtype d) { return d == ATTN_F32 || d == ATTN_BF16 || d == ATTN_F16; }
 
 }  // namespace
 
@@ -176,7 +176,7 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pag
                               float* lse, void* workspace, size_t workspace_bytes,
                               void* stream) {
   g_last_error[0] = 0;
-  if (!dtype_ok(dtype)) return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32/ATTN_BF16", dtype);
+  if (!dtype_ok(dtype)) return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32/ATTN_BF16/ATTN_F16", dtype);
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || num_pages < 0 ||
       max_pages_per_req < 0 || max_kv_len < 0 || split_pages < 0)
     return fail(ATTN_E_SHAPE,
@@ -191,7 +191,7 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pag
   const int G = Hq / Hkv;
   if (!attn::decode_supported((int)dtype, D, G, page_size))
     return fail(ATTN_E_UNSUPPORTED, "decode: dtype=%d D=%d G=%d page_size=%d not built "
-                "(bf16: D in {64,128,256}; f32: D in {64,128}; G in {1,2,4,8}; page_size 16)", dtype, D, G, page_size);
+                "(bf16/f16: D in {64,128,256}; f32: D in {64,128}; G in {1,2,4,8}; page_size 16)", dtype, D, G, page_size);
   if (B == 0) return ATTN_OK;
   if (!q || !k_pages || !v_pages || !page_table || !kv_lens || !out || !lse)
     return fail(ATTN_E_NULL, "a required pointer is NULL");
@@ -228,7 +228,7 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pag
                        [&] { return attn::launch_decode_split(p, (int)dtype, D, G, s); });
   if (e != hipSuccess)
     return fail(ATTN_E_HIP, "decode_split launch: %s", hipGetErrorString(e));
-  if (dtype == ATTN_BF16 || pl.n_splits > 1) {
+  if (dtype != ATTN_F32 || pl.n_splits > 1) {
     e = timed(ATTN_KERNEL_DECODE_COMBINE, s,
               [&] { return attn::launch_decode_combine(p, (int)dtype, D, G, s); });
     if (e != hipSuccess)
@@ -239,7 +239,7 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pag
 
 static attn_status check_prefill_common(attn_dtype dtype, int B, int Hq, int Hkv, int D,
                                         int total_q, int max_seqlen_q, int causal, float scale) {
-  if (!dtype_ok(dtype)) return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32/ATTN_BF16", dtype);
+  if (!dtype_ok(dtype)) return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32/ATTN_BF16/ATTN_F16", dtype);
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || total_q < 0 || max_seqlen_q < 0)
     return fail(ATTN_E_SHAPE, "negative or zero size (B=%d Hq=%d Hkv=%d D=%d total_q=%d "
                 "max_seqlen_q=%d)", B, Hq, Hkv, D, total_q, max_seqlen_q);
@@ -247,7 +247,7 @@ static attn_status check_prefill_common(attn_dtype dtype, int B, int Hq, int Hkv
   if (causal != 0 && causal != 1) return fail(ATTN_E_VALUE, "causal must be 0 or 1");
   if (!std::isfinite(scale)) return fail(ATTN_E_VALUE, "scale is not finite");
   if (!attn::prefill_supported((int)dtype, D))
-    return fail(ATTN_E_UNSUPPORTED, "prefill: dtype=%d D=%d not built (bf16, D in {128,256})",
+    return fail(ATTN_E_UNSUPPORTED, "prefill: dtype=%d D=%d not built (bf16/f16, D in {128,256})",
                 dtype, D);
   // One workgroup per (query head, sequence, query tile), indexed by an int.
   const long long items =
@@ -281,7 +281,7 @@ attn_status attn_prefill_varlen(attn_dtype dtype, const void* q, const void* k, 
   p.q_tiles = (max_seqlen_q + attn::kPrefillBM - 1) / attn::kPrefillBM;
   p.scale_log2 = scale * kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = timed(ATTN_KERNEL_PREFILL, s, [&] { return attn::launch_prefill(p, D, false, s); });
+  hipError_t e = timed(ATTN_KERNEL_PREFILL, s, [&] { return attn::launch_prefill(p, (int)dtype, D, false, s); });
   if (e != hipSuccess) return fail(ATTN_E_HIP, "prefill launch: %s", hipGetErrorString(e));
   return ATTN_OK;
 }
@@ -322,7 +322,7 @@ attn_status attn_prefill_paged(attn_dtype dtype, const void* q, const int32_t* c
   p.scale_log2 = scale * kLog2e;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e =
-      timed(ATTN_KERNEL_PREFILL_PAGED, s, [&] { return attn::launch_prefill(p, D, true, s); });
+      timed(ATTN_KERNEL_PREFILL_PAGED, s, [&] { return attn::launch_prefill(p, (int)dtype, D, true, s); });
   if (e != hipSuccess) return fail(ATTN_E_HIP, "prefill_paged launch: %s", hipGetErrorString(e));
   return ATTN_OK;
 }

@@ -16,9 +16,60 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// bfloat16 stored as raw bits.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// bfloat16 / IEEE half stored as raw bits (element tags of the 16-bit paths).
 struct bf16_t {
   uint16_t bits;
+};
+struct f16_t {
+  uint16_t bits;
+};
+
+// The two 16-bit input formats on the matrix cores: operand vectors, the
+// element type (float -> element conversion rounds to nearest even) and the
+// MFMA shapes and dot product the kernels use, all with fp32 accumulation.
+template <typename E>
+struct Half16;
+template <>
+struct Half16<bf16_t> {
+  typedef __bf16 elem;
+  typedef bf16x2 v2;
+  typedef bf16x4 v4;
+  typedef bf16x8 v8;
+  static __device__ __forceinline__ f32x4 mfma16x16x32(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16x16x16(v4 a, v4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x16 mfma32x32x16(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float dot2(v2 a, v2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+  }
+};
+template <>
+struct Half16<f16_t> {
+  typedef _Float16 elem;
+  typedef f16x2 v2;
+  typedef f16x4 v4;
+  typedef f16x8 v8;
+  static __device__ __forceinline__ f32x4 mfma16x16x32(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16x16x16(v4 a, v4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x16 mfma32x32x16(v8 a, v8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ float dot2(v2 a, v2 b, float c) {
+    return __builtin_amdgcn_fdot2(a, b, c, false);
+  }
 };
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -93,6 +93,10 @@ template <>
 __device__ __forceinline__ void store_out<bf16_t>(bf16_t* dst, float x) {
   dst->bits = (uint16_t)f32_to_bf16_bits(x);
 }
+template <>
+__device__ __forceinline__ void store_out<f16_t>(f16_t* dst, float x) {
+  dst->bits = __builtin_bit_cast(uint16_t, (_Float16)x);
+}
 
 // Number of valid tokens of request b after clamping inconsistent device data
 // (negative, above max_kv_len or above the page table's capacity -> bad).
@@ -283,7 +287,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_split_kernel(DecodeParams p) 
 }
 
 // ---------------------------------------------------------------------------
-// bf16 decode on the matrix cores with a balanced schedule.
+// bf16 / fp16 decode on the matrix cores with a balanced schedule.
 //
 // Schedule: the (request, KV head, page) units of the whole batch are laid
 // out request by request, KV head by KV head, and cut into equal runs, one
@@ -372,10 +376,12 @@ __device__ __forceinline__ char* decode_vbuf(int wave) {
 // group of hw KV heads; wave w of the workgroup folds KV head hg * hw + w of
 // every unit, so a workgroup reads whole pages (all heads of a token are
 // adjacent in the NHD layout).
-template <int D, int G, int NB>
+template <typename E, int D, int G, int NB>
 __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1, int W, int lane,
                                            int wave) {
   using C = MfmaDecodeCfg<D>;
+  using H = Half16<E>;
+  using elem = typename H::elem;
   const int l16 = lane & 15, gq = lane >> 4;
   // Request holding unit u0 (scan of units per request, 64 requests at a time).
   int b = 0, start_b = 0;
@@ -427,14 +433,14 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
     const int len = min(p.kv_lens[b], np * kPage);     // valid tokens (clamped, >= 1 page)
 
     // Q^T fragments: lane (head l16, k-group gq) holds q[head][32 ks + 8 gq .. +8].
-    bf16x8 qf[C::KS];
+    typename H::v8 qf[C::KS];
     {
-      const __bf16* qh = reinterpret_cast<const __bf16*>(p.q) +
+      const elem* qh = reinterpret_cast<const elem*>(p.q) +
                          ((size_t)b * p.Hq + (size_t)kvh * G + (l16 < G ? l16 : 0)) * D + 8 * gq;
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 v = *reinterpret_cast<const bf16x8*>(qh + 32 * ks);
-        qf[ks] = l16 < G ? v : bf16x8{};
+        const typename H::v8 v = *reinterpret_cast<const typename H::v8*>(qh + 32 * ks);
+        qf[ks] = l16 < G ? v : typename H::v8{};
       }
     }
     f32x4 o[C::DB];
@@ -481,8 +487,7 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
         f32x4 s = {};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pg.k[ks]), qf[ks],
-                                                      s, 0, 0, 0);
+          s = H::mfma16x16x32(__builtin_bit_cast(typename H::v8, pg.k[ks]), qf[ks], s);
         float mx = kNegInf;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -495,13 +500,13 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
         const float mu = mn == kNegInf ? 0.f : mn;
         const float alpha = exp2_fast(m - mu);
         m = mn;
-        bf16x4 pb;
+        typename H::v4 pb;
         float ps = 0.f;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const float e = exp2_fast(s[rr] - mu);
           ps += e;
-          pb[rr] = (__bf16)e;
+          pb[rr] = (elem)e;
         }
         lsum = lsum * alpha + ps;
         if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
@@ -515,8 +520,7 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
         for (int db = 0; db < C::DB; ++db) {
           const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_v4i16*)((lds_char*)myv + vpage_off<D>(t_rd, db * 16 + 4 * (l16 & 3))));
-          o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a), pb,
-                                                            o[db], 0, 0, 0);
+          o[db] = H::mfma16x16x16(__builtin_bit_cast(typename H::v4, a), pb, o[db]);
         }
       };
       Page bufs[NB];
@@ -538,13 +542,13 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
     if (l16 < G) {
       const int h = kvh * G + l16;
       if (whole) {
-        __bf16* og = reinterpret_cast<__bf16*>(p.out) + ((size_t)b * p.Hq + h) * D + 4 * gq;
+        elem* og = reinterpret_cast<elem*>(p.out) + ((size_t)b * p.Hq + h) * D + 4 * gq;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          bf16x4 v;
+          typename H::v4 v;
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) v[rr] = (__bf16)(o[db][rr] * inv);
-          *reinterpret_cast<bf16x4*>(og + 16 * db) = v;
+          for (int rr = 0; rr < 4; ++rr) v[rr] = (elem)(o[db][rr] * inv);
+          *reinterpret_cast<typename H::v4*>(og + 16 * db) = v;
         }
         if (gq == 0) p.lse[(size_t)b * p.Hq + h] = lse_nat;
       } else {
@@ -564,7 +568,7 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
   }
 }
 
-template <int D, int G, int NB>
+template <typename E, int D, int G, int NB>
 __global__ __launch_bounds__(kMaxGroupWaves * 64, D == 256 ? 1 : 2) void decode_mfma_kernel(DecodeParams p) {
   static_assert(G >= 1 && G <= 16, "one 16-column MFMA tile holds the query heads");
   const int lane = threadIdx.x & 63;
@@ -573,7 +577,7 @@ __global__ __launch_bounds__(kMaxGroupWaves * 64, D == 256 ? 1 : 2) void decode_
   const int U = total_units(p);
   const int W = run_length(p, U);
   for (int run = blockIdx.x; (long)run * W < U; run += gridDim.x) {
-    decode_run<D, G, NB>(p, run * W, min(run * W + W, U), W, lane, wave);
+    decode_run<E, D, G, NB>(p, run * W, min(run * W + W, U), W, lane, wave);
   }
 }
 
@@ -581,7 +585,7 @@ __global__ __launch_bounds__(kMaxGroupWaves * 64, D == 256 ? 1 : 2) void decode_
 // wave per query head of the group; lanes own d.  Pairs held by a single run
 // were written by that run; empty requests get out 0 and lse -inf and
 // inconsistent ones NaN.
-template <int D, int G>
+template <typename E, int D, int G>
 __global__ __launch_bounds__(G * 64) void decode_merge_kernel(DecodeParams p) {
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -601,7 +605,7 @@ __global__ __launch_bounds__(G * 64) void decode_merge_kernel(DecodeParams p) {
   const int nseg = np > 0 ? (start_pair + np - 1) / W - start_pair / W + 1 : 0;
   if (nseg == 1) return;
   const int h = kvh * G + g;
-  bf16_t* og = reinterpret_cast<bf16_t*>(p.out) + ((size_t)b * p.Hq + h) * D;
+  E* og = reinterpret_cast<E*>(p.out) + ((size_t)b * p.Hq + h) * D;
   if (bad || nseg == 0) {
     const float val = bad ? __builtin_nanf("") : 0.f;
     for (int d = lane; d < D; d += 64) store_out(og + d, val);
@@ -695,7 +699,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
 template <typename T, int D, int G>
 hipError_t launch_split_t(const DecodeParams& p, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((decode_mfma_kernel<D, G, (D == 256 ? 1 : kMfmaBatch)>),
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, (D == 256 ? 1 : kMfmaBatch)>),
                        dim3(p.n_groups), dim3(p.hw * 64), 0, s, p);
   } else {
     hipLaunchKernelGGL((decode_split_kernel<T, D, G, kBatch>), dim3(p.n_splits, p.Hkv, p.B),
@@ -735,14 +739,14 @@ hipError_t launch_combine_t(const DecodeParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D>
+template <typename E, int D>
 hipError_t launch_merge_g(const DecodeParams& p, int G, hipStream_t s) {
   dim3 grid(p.Hkv, p.B);
   switch (G) {
-    case 1: hipLaunchKernelGGL((decode_merge_kernel<D, 1>), grid, dim3(64), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((decode_merge_kernel<D, 2>), grid, dim3(128), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((decode_merge_kernel<D, 4>), grid, dim3(256), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((decode_merge_kernel<D, 8>), grid, dim3(512), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((decode_merge_kernel<E, D, 1>), grid, dim3(64), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((decode_merge_kernel<E, D, 2>), grid, dim3(128), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((decode_merge_kernel<E, D, 4>), grid, dim3(256), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((decode_merge_kernel<E, D, 8>), grid, dim3(512), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -751,13 +755,14 @@ hipError_t launch_merge_g(const DecodeParams& p, int G, hipStream_t s) {
 }  // namespace
 
 bool decode_supported(int dtype, int D, int G, int page_size) {
-  const bool d_ok = dtype == 1 ? (D == 64 || D == 128 || D == 256) : (dtype == 0 && D <= 128 &&
-                                                                      (D == 64 || D == 128));
+  const bool d_ok = (dtype == 1 || dtype == 2) ? (D == 64 || D == 128 || D == 256)
+                                                : (dtype == 0 && (D == 64 || D == 128));
   return d_ok && (G == 1 || G == 2 || G == 4 || G == 8) && page_size == kPage;
 }
 
 hipError_t launch_decode_split(const DecodeParams& p, int dtype, int D, int G, hipStream_t s) {
-  return dtype == 0 ? launch_split_d<float>(p, D, G, s) : launch_split_d<bf16_t>(p, D, G, s);
+  if (dtype == 0) return launch_split_d<float>(p, D, G, s);
+  return dtype == 1 ? launch_split_d<bf16_t>(p, D, G, s) : launch_split_d<f16_t>(p, D, G, s);
 }
 
 hipError_t launch_decode_combine(const DecodeParams& p, int dtype, int D, int G, hipStream_t s) {
@@ -766,9 +771,15 @@ hipError_t launch_decode_combine(const DecodeParams& p, int dtype, int D, int G,
     if (D == 128) return launch_combine_t<float, 128>(p, s);
     return hipErrorInvalidValue;
   }
-  if (D == 64) return launch_merge_g<64>(p, G, s);
-  if (D == 128) return launch_merge_g<128>(p, G, s);
-  if (D == 256) return launch_merge_g<256>(p, G, s);
+  if (dtype == 2) {
+    if (D == 64) return launch_merge_g<f16_t, 64>(p, G, s);
+    if (D == 128) return launch_merge_g<f16_t, 128>(p, G, s);
+    if (D == 256) return launch_merge_g<f16_t, 256>(p, G, s);
+    return hipErrorInvalidValue;
+  }
+  if (D == 64) return launch_merge_g<bf16_t, 64>(p, G, s);
+  if (D == 128) return launch_merge_g<bf16_t, 128>(p, G, s);
+  if (D == 256) return launch_merge_g<bf16_t, 256>(p, G, s);
   return hipErrorInvalidValue;
 }
 

@@ -50,7 +50,7 @@ struct PrefillParams {
   float scale_log2;
 };
 
-// dtype: 0 = f32, 1 = bf16 (values of attn_dtype).
+// dtype: 0 = f32, 1 = bf16, 2 = f16 (values of attn_dtype).
 bool decode_supported(int dtype, int D, int G, int page_size);
 hipError_t launch_decode_split(const DecodeParams& p, int dtype, int D, int G, hipStream_t s);
 hipError_t launch_decode_combine(const DecodeParams& p, int dtype, int D, int G, hipStream_t s);
@@ -63,6 +63,6 @@ constexpr int kDecodeGroupsPerCU = ATTN_DECODE_GROUPS_PER_CU;
 // Query rows per workgroup of the prefill kernels (grid sizing on the host).
 constexpr int kPrefillBM = 128;
 bool prefill_supported(int dtype, int D);
-hipError_t launch_prefill(const PrefillParams& p, int D, bool paged, hipStream_t s);
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, bool paged, hipStream_t s);
 
 }  // namespace attn

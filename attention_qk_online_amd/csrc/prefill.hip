@@ -1,4 +1,4 @@
-// Ragged causal prefill for gfx950 on bf16 MFMA with fp32 accumulation.
+// Ragged causal prefill for gfx950 on bf16 / fp16 MFMA with fp32 accumulation.
 //
 // One workgroup = one (query tile of BM = 128 rows, query head) of one
 // sequence; four waves own 32 query rows each.  Key tiles have BN keys (64
@@ -16,7 +16,7 @@
 //
 // Per tile j (the loop is unrolled by R so every LDS address is a per-lane
 // constant plus an immediate):
-//   1. S^T(j+1) = K(j+1) . Q^T on v_mfma_f32_32x32x16_bf16, issued alongside
+//   1. S^T(j+1) = K(j+1) . Q^T on v_mfma_f32_32x32x16_bf16 (_f16), issued alongside
 //      the softmax of tile j (independent work, interleaved on the SIMD).
 //      Q stays in VGPRs (B operand); the transposed product gives each lane
 //      one query column, so a row max is in-lane plus one lane^32 exchange.
@@ -77,9 +77,6 @@ struct Cfg {
   static_assert(LDSB <= 160 * 1024, "LDS per CU");
 };
 
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -100,10 +97,15 @@ constexpr int kWaitLgkm0 = 0xc07f;
 
 // The page table comes as its own restrict-qualified argument so that its
 // wave-uniform reads compile to scalar loads.
-template <int D, bool PAGED>
+template <typename E, int D, bool PAGED>
 __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
     PrefillParams p, const int32_t* __restrict__ page_table) {
   using C = Cfg<D>;
+  using H = Half16<E>;            // bf16 or fp16 inputs
+  using elem = typename H::elem;
+  using v8 = typename H::v8;
+  using v2 = typename H::v2;
+  auto mfma32 = [](v8 a, v8 b, f32x16 c) { return H::mfma32x32x16(a, b, c); };
   // One array per ring slot (not one array): the compiler can then tell that a
   // DMA into one slot does not alias operand reads from another, and does not
   // stall those reads on the DMA's completion.  Slots past R are unused.
@@ -190,15 +192,15 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
   // ---- Q fragments (B operand of S^T = K Q^T): row l32 of this wave's 32 rows.
   const int my_row = r0 + wave * 32 + l32;
   const bool row_ok = my_row < Lq;
-  bf16x8 qf[C::QK];
+  v8 qf[C::QK];
   {
-    const __bf16* qr = reinterpret_cast<const __bf16*>(p.q) +
+    const elem* qr = reinterpret_cast<const elem*>(p.q) +
                        ((size_t)(q_start + (row_ok ? my_row : 0)) * p.Hq + head) * D + hl * 8;
 #pragma unroll
     for (int s = 0; s < C::QK; ++s) {
       u32x4 v = *reinterpret_cast<const u32x4*>(qr + s * 16);
       if (flip) v ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-      qf[s] = row_ok ? __builtin_bit_cast(bf16x8, v) : bf16x8{};
+      qf[s] = row_ok ? __builtin_bit_cast(v8, v) : v8{};
     }
   }
 
@@ -317,7 +319,7 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
       s[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < C::QK; ++ks)
-        s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kbuf + kb * 32 * C::ROWB + (ks >> 3) * 256 + kro[ks & 7]),
+        s[kb] = mfma32(*reinterpret_cast<const v8*>(kbuf + kb * 32 * C::ROWB + (ks >> 3) * 256 + kro[ks & 7]),
                        qf[ks], s[kb]);
     }
   };
@@ -358,26 +360,26 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
     }
   };
 
-  // P = 2^(s c - m) rounded to bf16 (laid out as the B operand of O^T += V^T P^T);
+  // P = 2^(s c - m) rounded to the input type (laid out as the B operand of O^T += V^T P^T);
   // the row sum adds the rounded weights, the ones that multiply V.
-  auto weights = [&](f32x16 (&s)[C::KB], bf16x8 (&pb)[C::PS], float nm) {
+  auto weights = [&](f32x16 (&s)[C::KB], v8 (&pb)[C::PS], float nm) {
     float psum = 0.f;
-    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+    const v2 one = {(elem)1.f, (elem)1.f};
 #pragma unroll
     for (int ps = 0; ps < C::PS; ++ps) {
-      bf16x8 v;
+      v8 v;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        v[e] = (__bf16)exp2_fast(__builtin_fmaf(s[ps >> 1][(ps & 1) * 8 + e], c, nm));
+        v[e] = (elem)exp2_fast(__builtin_fmaf(s[ps >> 1][(ps & 1) * 8 + e], c, nm));
 #pragma unroll
       for (int e = 0; e < 8; e += 2)
-        psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[e], v[e + 1]}, one, psum, false);
+        psum = H::dot2(v2{v[e], v[e + 1]}, one, psum);
       pb[ps] = v;
     }
     lsum += psum;
   };
 
-  auto pv = [&](const char* vbuf, bf16x8 (&pb)[C::PS]) {
+  auto pv = [&](const char* vbuf, v8 (&pb)[C::PS]) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
         v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_char*)vbuf + ro));
         v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_v4i16*)((lds_char*)vbuf + ro + 8 * C::ROWB));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const v8 a = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[db] = mfma32(a, pb[ps], o[db]);
       }
     }
@@ -397,25 +399,25 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
   // then the O^T MFMAs with V^T fragments read PF ahead.  Used for head_dim
   // 256, whose one wave per SIMD leaves the compiler no room to reorder.
   auto fused = [&](const char* kbuf, const char* vbuf, f32x16 (&scur)[C::KB],
-                   f32x16 (&snext)[C::KB], bf16x8 (&pb)[C::PS]) {
+                   f32x16 (&snext)[C::KB], v8 (&pb)[C::PS]) {
     constexpr int NQ = C::KB * C::QK;       // S^T MFMAs
     constexpr int NE = C::KB * 16;          // weights per lane
     constexpr int EPM = NE / NQ;            // weights per S^T MFMA
     constexpr int PF = 2;                   // fragments in flight (measured best)
     const float nm = -m;
-    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+    const v2 one = {(elem)1.f, (elem)1.f};
     auto kfrag = [&](int i) {
       const int kb = i / C::QK, ks = i % C::QK;
-      return *reinterpret_cast<const bf16x8*>(kbuf + kb * 32 * C::ROWB + (ks >> 3) * 256 + kro[ks & 7]);
+      return *reinterpret_cast<const v8*>(kbuf + kb * 32 * C::ROWB + (ks >> 3) * 256 + kro[ks & 7]);
     };
-    bf16x8 kf[PF];
+    v8 kf[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) kf[i] = kfrag(i);
     f32x16 acc[C::KB];
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) acc[kb] = f32x16{};
     float psum = 0.f;
-    bf16x8 w;
+    v8 w;
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       const int kb = i / C::QK, ks = i % C::QK;
@@ -424,11 +426,11 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
 #pragma unroll
       for (int e = 0; e < EPM; ++e) {
         const int idx = i * EPM + e;
-        w[idx % 8] = (__bf16)exp2_fast(__builtin_fmaf(scur[idx / 16][idx % 16], c, nm));
+        w[idx % 8] = (elem)exp2_fast(__builtin_fmaf(scur[idx / 16][idx % 16], c, nm));
         if (idx % 8 == 7) {
 #pragma unroll
           for (int t = 0; t < 8; t += 2)
-            psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{w[t], w[t + 1]}, one, psum, false);
+            psum = H::dot2(v2{w[t], w[t + 1]}, one, psum);
           pb[idx / 8] = w;
         }
       }
@@ -442,9 +444,9 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
       const int ro = ps * 16 * C::ROWB + (db >> 2) * 256 + vro[db & 3];
       v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_char*)vbuf + ro));
       v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_char*)vbuf + ro + 8 * C::ROWB));
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    bf16x8 vf[PF];
+    v8 vf[PF];
 #pragma unroll
     for (int j = 0; j < PF; ++j) vf[j] = vfrag(j);
 #pragma unroll
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
     char* const VDST = vslot(Idx<SLOT + C::R - 1>{});
     if (kt + C::R - 1 < n_kt) dma(kt + C::R - 1, VDST, true, pid_v);
     if (kt + C::R < n_kt) dma(kt + C::R, KDST, false, pid_k);
-    bf16x8 pb[C::PS];
+    v8 pb[C::PS];
     if constexpr (FAST && D == 256) {
       update_max(scur);
       fused(KNXT, VCUR, scur, snext, pb);
@@ -588,35 +590,42 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
   }
   if (!row_ok) return;
   const size_t orow = (size_t)(q_start + my_row) * p.Hq + head;
-  __bf16* og = reinterpret_cast<__bf16*>(p.out) + orow * D;
+  elem* og = reinterpret_cast<elem*>(p.out) + orow * D;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
-      bf16x4 v;
+      typename H::v4 v;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = (__bf16)(o[db][a4 * 4 + j] * inv);
-      *reinterpret_cast<bf16x4*>(og + db * 32 + a4 * 8 + hl * 4) = v;
+      for (int j = 0; j < 4; ++j) v[j] = (elem)(o[db][a4 * 4 + j] * inv);
+      *reinterpret_cast<typename H::v4*>(og + db * 32 + a4 * 8 + hl * 4) = v;
     }
   }
   if (hl == 0) p.lse[orow] = lse_v;
 }
 
-template <int D, bool PAGED>
+template <typename E, int D, bool PAGED>
 hipError_t launch_t(const PrefillParams& p, hipStream_t s) {
   const int total = p.Hq * p.B * p.q_tiles;
   dim3 grid(8 * ((total + 7) / 8));
-  hipLaunchKernelGGL((prefill_kernel<D, PAGED>), grid, dim3(NT), 0, s, p, p.page_table);
+  hipLaunchKernelGGL((prefill_kernel<E, D, PAGED>), grid, dim3(NT), 0, s, p, p.page_table);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool prefill_supported(int dtype, int D) { return dtype == 1 && (D == 128 || D == 256); }
+bool prefill_supported(int dtype, int D) { return (dtype == 1 || dtype == 2) && (D == 128 || D == 256); }
 
-hipError_t launch_prefill(const PrefillParams& p, int D, bool paged, hipStream_t s) {
-  if (D == 128) return paged ? launch_t<128, true>(p, s) : launch_t<128, false>(p, s);
-  if (D == 256) return paged ? launch_t<256, true>(p, s) : launch_t<256, false>(p, s);
+template <typename E>
+hipError_t launch_e(const PrefillParams& p, int D, bool paged, hipStream_t s) {
+  if (D == 128) return paged ? launch_t<E, 128, true>(p, s) : launch_t<E, 128, false>(p, s);
+  if (D == 256) return paged ? launch_t<E, 256, true>(p, s) : launch_t<E, 256, false>(p, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, bool paged, hipStream_t s) {
+  if (dtype == 1) return launch_e<bf16_t>(p, D, paged, s);
+  if (dtype == 2) return launch_e<f16_t>(p, D, paged, s);
   return hipErrorInvalidValue;
 }
 

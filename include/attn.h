@@ -19,8 +19,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All tensors are dense, row-major, and live in device memory unless the
- *    argument says "host".  Element types: ATTN_F32 (float) or ATTN_BF16
- *    (bfloat16 bits).  `out` has the input element type; `lse` is float.
+ *    argument says "host".  Element types: ATTN_F32 (float), ATTN_BF16
+ *    (bfloat16 bits) or ATTN_F16 (IEEE half bits).  `out` has the input
+ *    element type; `lse` is float.
  *  - Grouped heads: query head h reads KV head h / (Hq / Hkv); Hq must be a
  *    multiple of Hkv ("FlashAttention-3 ..." section 二: queries carry
  *    num_heads, keys/values num_kv_heads).
@@ -73,7 +74,7 @@ typedef enum {
   ATTN_E_HIP = 7          /* the HIP runtime rejected a launch                    */
 } attn_status;
 
-typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_F16 = 2 } attn_dtype;
 
 /* ------------------------------------------------------------------------ */
 /* Batched decode over a paged KV cache.
@@ -85,7 +86,7 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  * fixed-size pages addressed through a table) and "FlashAttention-3 ..."
  * section 二 (physical block addressing in continuous batching).
  *
- * bf16: the (request, KV head, page) units of the batch are cut into equal
+ * bf16 / f16: the (request, KV head, page) units of the batch are cut into equal
  * runs, one per wave, computed on the device from kv_lens (balanced over
  * ragged lengths); Q.K^T and P.V run on the matrix cores.  Runs that cover
  * only part of a (request, KV head) pair leave partial (o, lse) states in the
@@ -108,7 +109,7 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
  *              bytes (may be NULL when that size is 0); contents on entry
  *              do not matter and are clobbered.
  *
- * Supported: dtype BF16 with D in {64, 128, 256}, or F32 with D in {64, 128};
+ * Supported: dtype BF16 or F16 with D in {64, 128, 256}, or F32 with D in {64, 128};
  * Hq/Hkv in {1, 2, 4, 8}; page_size 16.  Anything else returns
  * ATTN_E_UNSUPPORTED.  The workspace size depends on dtype, the sizes and
  * split_pages only (not on the device or on kv_lens).
@@ -129,17 +130,18 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pag
  * packed [total_tokens, heads, head_dim] tensors, prefix offsets of length
  * batch+1, max_seqlen_q / max_seqlen_k, softmax_scale and causal).
  *
- *  q            [total_q, Hq, D]   bf16
- *  k, v         [total_k, Hkv, D]  bf16
+ *  q            [total_q, Hq, D]   bf16 or f16
+ *  k, v         [total_k, Hkv, D]  same type
  *  cu_seqlens_q [B+1] int32, nondecreasing, cu[0] = 0, cu[B] <= total_q
  *  cu_seqlens_k [B+1] int32, same rules against total_k
  *  max_seqlen_q, max_seqlen_k  host ints bounding every per-sequence length
  *  causal       0 or 1 (bottom-right aligned)
- *  out          [total_q, Hq, D] bf16;  lse [total_q, Hq] float
+ *  out          [total_q, Hq, D] same type;  lse [total_q, Hq] float
  *
- * Query tiles of 128 rows run on bf16 MFMA with fp32 accumulation; K/V tiles
- * are staged through LDS; tiles wholly above the causal diagonal are never
- * loaded.  Supported: dtype BF16; D in {128, 256}; any Hq multiple of Hkv;
+ * Query tiles of 128 rows run on bf16 / f16 MFMA with fp32 accumulation; K/V
+ * tiles are staged through LDS; tiles wholly above the causal diagonal are
+ * never loaded.  Supported: dtype BF16 or F16; D in {128, 256}; any Hq
+ * multiple of Hkv;
  * Hq * B * ceil(max_seqlen_q / 128) below 2^31 - 8 (else ATTN_E_SHAPE).
  * Rows of out/lse outside every [cu_seqlens_q[b], cu_seqlens_q[b+1]) are
  * not written.
@@ -158,13 +160,13 @@ attn_status attn_prefill_varlen(attn_dtype dtype, const void* q, const void* k, 
  * the causal mask is bottom-right aligned.  Pages may be shared between
  * requests (a common prefix).
  *
- *  q            [total_q, Hq, D] bf16;   cu_seqlens_q [B+1] int32
- *  k_pages, v_pages [num_pages, page_size, Hkv, D] bf16
+ *  q            [total_q, Hq, D] bf16 or f16;   cu_seqlens_q [B+1] int32
+ *  k_pages, v_pages [num_pages, page_size, Hkv, D] same type
  *  page_table   [B, max_pages_per_req] int32;  kv_lens [B] int32
  *  max_seqlen_q, max_kv_len  host bounds
- *  out [total_q, Hq, D] bf16;  lse [total_q, Hq] float
+ *  out [total_q, Hq, D] same type;  lse [total_q, Hq] float
  *
- * Supported: dtype BF16; D in {128, 256}; page_size 16; the same work-item
+ * Supported: dtype BF16 or F16; D in {128, 256}; page_size 16; the same work-item
  * bound as attn_prefill_varlen.
  */
 attn_status attn_prefill_paged(attn_dtype dtype, const void* q, const int32_t* cu_seqlens_q,

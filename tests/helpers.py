@@ -7,8 +7,11 @@ import oracle
 
 # Tolerances of the parity gate: bf16 inputs 2e-2, fp32 inputs 1e-5, applied
 # to max|d| and to the normwise relative error max|d| / max|ref|, separately
-# for out and lse.
-TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-5}
+# for out and lse.  fp16 inputs: 5e-3.  The fp16 paths round the softmax
+# weights and the output to half (relative step 2^-11 = 4.9e-4 each, against
+# 2^-8 = 3.9e-3 for bf16) and accumulate in fp32, so their error is about
+# 8x below the bf16 paths'; 5e-3 keeps the bf16 gate's margin at that scale.
+TOL = {torch.bfloat16: 2e-2, torch.float16: 5e-3, torch.float32: 1e-5}
 
 
 def assert_parity(got_out, got_lse, ref_out, ref_lse, dtype, what="", rows=None):

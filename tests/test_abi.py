@@ -99,6 +99,9 @@ def test_workspace_size(lib):
     assert n == ((slots * 128 * 4 + 255) // 256 + (slots * 4 + 255) // 256) * 256
     assert lib.attn_decode_paged_workspace_size(1, -1, 8, 2, 128, 16, 160, 2) == 0
     assert lib.attn_decode_paged_workspace_size(9, 4, 8, 2, 128, 16, 160, 2) == 0
+    # f16 uses the bf16 plan
+    assert (lib.attn_decode_paged_workspace_size(2, 4, 8, 2, 128, 16, 160, 2) ==
+            lib.attn_decode_paged_workspace_size(1, 4, 8, 2, 128, 16, 160, 2))
 
 
 def _prefill(lib, **kw):

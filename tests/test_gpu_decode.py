@@ -181,3 +181,23 @@ def test_many_requests(gpu, dtype):
         out, lse = _run(case, gpu, split)
         ro, rl = _oracle(case)
         assert_parity(out, lse, ro, rl, dtype, f"B150 {dtype} split{split}")
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 8, 8), (256, 16, 2)])
+@pytest.mark.parametrize("split_pages", [0, 2])
+def test_small_paged_fp16(gpu, D, Hq, Hkv, split_pages):
+    lens = [1, 15, 16, 17, 300, 64, 1000, 3, 0]
+    case = workloads.make_decode(B=len(lens), Hq=Hq, Hkv=Hkv, D=D, page_size=16, kv_lens=lens,
+                                 dtype=torch.float16, seed=430 + D + Hq, extra_pages=5)
+    out, lse = _run(case, gpu, split_pages)
+    ro, rl = _oracle(case)
+    assert_parity(out, lse, ro, rl, torch.float16, f"fp16 D{D} Hq{Hq} Hkv{Hkv} split{split_pages}")
+
+
+def test_paged_config_fp16(gpu):
+    """The batched paged GQA decode workload with fp16 inputs."""
+    case = workloads.make_decode(B=64, Hq=32, Hkv=8, D=128, page_size=16, len_range=(512, 4096),
+                                 dtype=torch.float16, seed=2, num_pages=20000)
+    out, lse = _run(case, gpu)
+    ro, rl = _oracle(case)
+    assert_parity(out, lse, ro, rl, torch.float16, "fp16 paged decode B64")

@@ -236,3 +236,34 @@ def test_paged_bad_page_is_nan(gpu):
     n0 = int(case.cu_seqlens_q[1])
     assert_parity(out[:n0], lse[:n0], ro[:n0], rl[:n0], torch.bfloat16, "good request")
     assert torch.isnan(out[n0:].float()).all() and torch.isnan(lse[n0:]).all()
+
+
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("causal", [True, False])
+def test_small_varlen_fp16(gpu, D, causal):
+    lens = [1, 17, 128, 129, 300, 64, 255]
+    case = workloads.make_prefill(B=len(lens), Hq=8, Hkv=2, D=D, lens_q=lens, dtype=torch.float16,
+                                  seed=340 + D, causal=causal)
+    out, lse = _varlen(case, gpu)
+    ro, rl = _ref(case)
+    assert_parity(out, lse, ro, rl, torch.float16, f"fp16 varlen D{D} causal={causal}")
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_small_paged_fp16(gpu, D):
+    case = workloads.make_paged_prefill(B=3, Hq=4, Hkv=2, D=D, page_size=16, chunk=70, cached=200,
+                                        shared_prefix=64, dtype=torch.float16, seed=350 + D)
+    out, lse = _paged(case, gpu)
+    ro, rl = oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, case.pool_k, case.pool_v,
+                                      case.page_table, case.kv_lens, True, case.scale)
+    assert_parity(out, lse, ro, rl, torch.float16, f"fp16 paged D{D}")
+
+
+def test_ragged_config_fp16_sampled(gpu):
+    """The ragged causal prefill workload (B 8, L in [1024, 4096], Hq 64, Hkv 8, D 128) in fp16."""
+    case = workloads.make_prefill(B=8, Hq=64, Hkv=8, D=128, len_range=(1024, 4096), dtype=torch.float16,
+                                  seed=3, causal=True)
+    out, lse = _varlen(case, gpu)
+    rows = _sample_rows(case.cu_seqlens_q, 64, 33)
+    ro, rl = _ref(case, rows=rows)
+    assert_parity(out, lse, ro, rl, torch.float16, "fp16 ragged (sampled rows)", rows=rows)
