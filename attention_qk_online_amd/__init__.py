@@ -15,6 +15,11 @@ Entry points (names follow the C ABI):
   with the argument list of ``varlen_fwd`` in "FlashAttention-3 内核在最新大模型
   推理中的集成实践" section 二.
 * :func:`prefill_paged` -- chunked prefill over a paged KV cache (same page).
+* :func:`prefill_paged_cascade` -- the same result when every request starts
+  with the same pages: the shared prefix is attended once for the whole batch
+  and merged into each request's own part (shared-prefix reuse in
+  "FlashInfer内核库深度解析").
+* :func:`merge_states` -- log-sum-exp merge of two partial attention states.
 
 The softmax scale defaults to 1/sqrt(head_dim) (same page, section 二).
 """
@@ -28,6 +33,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["decode_paged", "decode_paged_workspace_size", "prefill_varlen", "prefill_paged",
+           "prefill_paged_cascade", "prefill_paged_cascade_workspace_size", "merge_states",
            "timing_begin", "timing_end", "library_path", "load_library", "AttnError",
            "KERNEL_KINDS"]
 
@@ -36,7 +42,8 @@ _LIB_PATH = os.path.join(_HERE, "libattn.so")
 _lib = None
 
 ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
-KERNEL_KINDS = ("decode_split", "decode_combine", "prefill", "prefill_paged")
+KERNEL_KINDS = ("decode_split", "decode_combine", "prefill", "prefill_paged", "merge",
+                "cascade_prefix", "cascade_suffix")
 _STATUS = {0: "ok", 1: "null", 2: "shape", 3: "dtype", 4: "unsupported", 5: "value",
            6: "workspace", 7: "hip"}
 
@@ -76,6 +83,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_prefill_paged.argtypes = [c_int, vp, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int,
                                        c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_float,
                                        vp, vp, vp]
+    lib.attn_prefill_paged_cascade_workspace_size.restype = c_size
+    lib.attn_prefill_paged_cascade_workspace_size.argtypes = [c_int] * 4
+    lib.attn_prefill_paged_cascade.restype = c_int
+    lib.attn_prefill_paged_cascade.argtypes = [c_int, vp, vp, vp, vp, vp, vp] + [c_int] * 12 + [
+        c_float, vp, vp, vp, c_size, vp]
+    lib.attn_merge_states.restype = c_int
+    lib.attn_merge_states.argtypes = [c_int, vp, vp, vp, vp, c_int, c_int, vp, vp, vp]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [c_int]
     lib.attn_last_error.restype = ctypes.c_char_p
@@ -265,6 +279,91 @@ def prefill_paged(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_pages: torch.Te
                                   int(max_kv_len), int(bool(causal)), s, out.data_ptr(),
                                   lse.data_ptr(), _stream(q.device)))
     return out, lse
+
+
+def prefill_paged_cascade_workspace_size(dtype: torch.dtype, total_q: int, Hq: int, D: int) -> int:
+    code = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}.get(dtype)
+    if code is None:
+        raise ValueError(f"unsupported dtype {dtype} (float32, bfloat16 or float16)")
+    return int(load_library().attn_prefill_paged_cascade_workspace_size(code, int(total_q), int(Hq),
+                                                                        int(D)))
+
+
+def prefill_paged_cascade(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_pages: torch.Tensor,
+                          v_pages: torch.Tensor, page_table: torch.Tensor, kv_lens: torch.Tensor,
+                          max_seqlen_q: int, max_kv_len: int, shared_prefix_len: int,
+                          causal: bool = True, scale: Optional[float] = None,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None
+                          ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """:func:`prefill_paged` for a batch whose page-table rows all begin with the
+    same ``shared_prefix_len / page_size`` pages: the prefix is attended once
+    for every query row, then merged into each request's pass over its own
+    keys.  ``workspace`` (uint8, on the device) is allocated when not given."""
+    lib = load_library()
+    dt = _dtype_code(q)
+    pq = _dev(q, "q", dim=3)
+    pcq = _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    pk = _dev(k_pages, "k_pages", q.dtype, 4)
+    pv = _dev(v_pages, "v_pages", q.dtype, 4)
+    pt = _dev(page_table, "page_table", torch.int32, 2)
+    pl = _dev(kv_lens, "kv_lens", torch.int32, 1)
+    Tq, Hq, D = q.shape
+    num_pages, page_size, Hkv, Dk = k_pages.shape
+    if tuple(v_pages.shape) != tuple(k_pages.shape) or Dk != D:
+        raise ValueError("k_pages / v_pages do not match q")
+    B = cu_seqlens_q.shape[0] - 1
+    if page_table.shape[0] != B or kv_lens.shape[0] != B:
+        raise ValueError("page_table and kv_lens need one row per request")
+    s = _scale(scale, D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Tq, Hq), dtype=torch.float32, device=q.device)
+    _dev(out, "out", q.dtype, 3)
+    _dev(lse, "lse", torch.float32, 2)
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (Tq, Hq):
+        raise ValueError("out/lse have the wrong shape")
+    need = lib.attn_prefill_paged_cascade_workspace_size(dt, Tq, Hq, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    pw = _dev(workspace, "workspace", torch.uint8, 1)
+    _check(lib.attn_prefill_paged_cascade(dt, pq, pcq, pk, pv, pt, pl, B, Hq, Hkv, D, Tq,
+                                          page_size, num_pages, page_table.shape[1],
+                                          int(max_seqlen_q), int(max_kv_len),
+                                          int(shared_prefix_len), int(bool(causal)), s,
+                                          out.data_ptr(), lse.data_ptr(), pw, workspace.numel(),
+                                          _stream(q.device)))
+    return out, lse
+
+
+def merge_states(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: torch.Tensor,
+                 out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None
+                 ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Merge two attention states (o [..., D], lse [...]) over disjoint keys.
+    ``out`` / ``lse_out`` may be the a or b inputs (in place)."""
+    lib = load_library()
+    dt = _dtype_code(o_a)
+    D = o_a.shape[-1]
+    if tuple(o_b.shape) != tuple(o_a.shape) or o_b.dtype != o_a.dtype:
+        raise ValueError("o_a and o_b differ in shape or dtype")
+    if tuple(lse_a.shape) != tuple(o_a.shape[:-1]) or tuple(lse_b.shape) != tuple(lse_a.shape):
+        raise ValueError("lse_a / lse_b must have the shape of o without its last dim")
+    pa, pb = _dev(o_a, "o_a"), _dev(o_b, "o_b")
+    pla = _dev(lse_a, "lse_a", torch.float32)
+    plb = _dev(lse_b, "lse_b", torch.float32)
+    if out is None:
+        out = torch.empty_like(o_a)
+    if lse_out is None:
+        lse_out = torch.empty_like(lse_a)
+    _dev(out, "out", o_a.dtype)
+    _dev(lse_out, "lse_out", torch.float32)
+    if tuple(out.shape) != tuple(o_a.shape) or tuple(lse_out.shape) != tuple(lse_a.shape):
+        raise ValueError("out/lse_out have the wrong shape")
+    rows = lse_a.numel()
+    _check(lib.attn_merge_states(dt, pa, pla, pb, plb, rows, D, out.data_ptr(),
+                                 lse_out.data_ptr(), _stream(o_a.device)))
+    return out, lse_out
 
 
 def timing_begin(capacity: int = 4096) -> None:

@@ -156,6 +156,9 @@ const char* attn_kernel_name(attn_kernel_kind kind) {
     case ATTN_KERNEL_DECODE_COMBINE: return "decode_combine";
     case ATTN_KERNEL_PREFILL: return "prefill";
     case ATTN_KERNEL_PREFILL_PAGED: return "prefill_paged";
+    case ATTN_KERNEL_MERGE: return "merge";
+    case ATTN_KERNEL_CASCADE_PREFIX: return "cascade_prefix";
+    case ATTN_KERNEL_CASCADE_SUFFIX: return "cascade_suffix";
     default: return "unknown";
   }
 }
@@ -286,13 +289,16 @@ attn_status attn_prefill_varlen(attn_dtype dtype, const void* q, const void* k, 
   return ATTN_OK;
 }
 
-attn_status attn_prefill_paged(attn_dtype dtype, const void* q, const int32_t* cu_seqlens_q,
-                               const void* k_pages, const void* v_pages,
-                               const int32_t* page_table, const int32_t* kv_lens, int B, int Hq,
-                               int Hkv, int D, int total_q, int page_size, int num_pages,
-                               int max_pages_per_req, int max_seqlen_q, int max_kv_len,
-                               int causal, float scale, void* out, float* lse, void* stream) {
-  g_last_error[0] = 0;
+// Checks shared by the paged prefill entry points; on ATTN_OK, `p` holds the
+// launch parameters of the plain paged call and `empty` says there is no work.
+static attn_status paged_prefill_params(attn_dtype dtype, const void* q,
+                                        const int32_t* cu_seqlens_q, const void* k_pages,
+                                        const void* v_pages, const int32_t* page_table,
+                                        const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                                        int total_q, int page_size, int num_pages,
+                                        int max_pages_per_req, int max_seqlen_q, int max_kv_len,
+                                        int causal, float scale, void* out, float* lse,
+                                        attn::PrefillParams& p, bool& empty) {
   attn_status st = check_prefill_common(dtype, B, Hq, Hkv, D, total_q, max_seqlen_q, causal, scale);
   if (st != ATTN_OK) return st;
   if (page_size <= 0 || num_pages < 0 || max_pages_per_req < 0 || max_kv_len < 0)
@@ -304,26 +310,145 @@ attn_status attn_prefill_paged(attn_dtype dtype, const void* q, const int32_t* c
   if ((long)max_kv_len > (long)max_pages_per_req * page_size)
     return fail(ATTN_E_SHAPE, "max_kv_len=%d exceeds max_pages_per_req*page_size=%ld", max_kv_len,
                 (long)max_pages_per_req * page_size);
-  if (B == 0 || max_seqlen_q == 0 || total_q == 0) return ATTN_OK;
+  empty = B == 0 || max_seqlen_q == 0 || total_q == 0;
+  if (empty) return ATTN_OK;
   if (!q || !k_pages || !v_pages || !cu_seqlens_q || !page_table || !kv_lens || !out || !lse)
     return fail(ATTN_E_NULL, "a required pointer is NULL");
   if (num_pages == 0 && max_kv_len > 0)
     return fail(ATTN_E_SHAPE, "num_pages is 0 but max_kv_len=%d", max_kv_len);
   if (((uintptr_t)q | (uintptr_t)k_pages | (uintptr_t)v_pages | (uintptr_t)out) % 16 != 0)
     return fail(ATTN_E_UNSUPPORTED, "q, k_pages, v_pages and out must be 16-byte aligned");
-  attn::PrefillParams p{};
+  p = attn::PrefillParams{};
   p.q = q; p.k = k_pages; p.v = v_pages; p.cu_q = cu_seqlens_q;
   p.page_table = page_table; p.kv_lens = kv_lens;
   p.out = out; p.lse = lse;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.total_q = total_q; p.total_k = 0;
   p.max_seqlen_q = max_seqlen_q; p.max_seqlen_k = max_kv_len;
   p.num_pages = num_pages; p.max_pages = max_pages_per_req; p.causal = causal;
+  p.table_stride = max_pages_per_req; p.kv_offset = 0; p.kv_len_fixed = -1;
   p.q_tiles = (max_seqlen_q + attn::kPrefillBM - 1) / attn::kPrefillBM;
   p.scale_log2 = scale * kLog2e;
+  return ATTN_OK;
+}
+
+attn_status attn_prefill_paged(attn_dtype dtype, const void* q, const int32_t* cu_seqlens_q,
+                               const void* k_pages, const void* v_pages,
+                               const int32_t* page_table, const int32_t* kv_lens, int B, int Hq,
+                               int Hkv, int D, int total_q, int page_size, int num_pages,
+                               int max_pages_per_req, int max_seqlen_q, int max_kv_len,
+                               int causal, float scale, void* out, float* lse, void* stream) {
+  g_last_error[0] = 0;
+  attn::PrefillParams p;
+  bool empty = false;
+  attn_status st = paged_prefill_params(dtype, q, cu_seqlens_q, k_pages, v_pages, page_table,
+                                        kv_lens, B, Hq, Hkv, D, total_q, page_size, num_pages,
+                                        max_pages_per_req, max_seqlen_q, max_kv_len, causal, scale,
+                                        out, lse, p, empty);
+  if (st != ATTN_OK || empty) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e =
       timed(ATTN_KERNEL_PREFILL_PAGED, s, [&] { return attn::launch_prefill(p, (int)dtype, D, true, s); });
   if (e != hipSuccess) return fail(ATTN_E_HIP, "prefill_paged launch: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+static size_t elem_bytes(attn_dtype dtype) { return dtype == ATTN_F32 ? 4 : 2; }
+static size_t round256(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
+
+size_t attn_prefill_paged_cascade_workspace_size(attn_dtype dtype, int total_q, int Hq, int D) {
+  if (!dtype_ok(dtype) || total_q < 0 || Hq <= 0 || D <= 0) return 0;
+  const size_t rows = (size_t)total_q * Hq;
+  return round256(rows * D * elem_bytes(dtype)) + round256(rows * sizeof(float));
+}
+
+attn_status attn_prefill_paged_cascade(attn_dtype dtype, const void* q,
+                                       const int32_t* cu_seqlens_q, const void* k_pages,
+                                       const void* v_pages, const int32_t* page_table,
+                                       const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                                       int total_q, int page_size, int num_pages,
+                                       int max_pages_per_req, int max_seqlen_q, int max_kv_len,
+                                       int shared_prefix_len, int causal, float scale, void* out,
+                                       float* lse, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  g_last_error[0] = 0;
+  attn::PrefillParams p;
+  bool empty = false;
+  attn_status st = paged_prefill_params(dtype, q, cu_seqlens_q, k_pages, v_pages, page_table,
+                                        kv_lens, B, Hq, Hkv, D, total_q, page_size, num_pages,
+                                        max_pages_per_req, max_seqlen_q, max_kv_len, causal, scale,
+                                        out, lse, p, empty);
+  if (st != ATTN_OK) return st;
+  if (shared_prefix_len < 0 || shared_prefix_len % page_size != 0)
+    return fail(ATTN_E_SHAPE, "shared_prefix_len=%d is not a non-negative multiple of "
+                "page_size=%d", shared_prefix_len, page_size);
+  if (shared_prefix_len > max_kv_len)
+    return fail(ATTN_E_SHAPE, "shared_prefix_len=%d exceeds max_kv_len=%d", shared_prefix_len,
+                max_kv_len);
+  if (empty) return ATTN_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (shared_prefix_len == 0) {
+    hipError_t e = timed(ATTN_KERNEL_PREFILL_PAGED, s,
+                         [&] { return attn::launch_prefill(p, (int)dtype, D, true, s); });
+    if (e != hipSuccess) return fail(ATTN_E_HIP, "prefill_paged launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
+  }
+  // The shared-prefix pass runs every query row as one sequence.
+  const long long items =
+      (long long)Hq * ((total_q + attn::kPrefillBM - 1) / attn::kPrefillBM);
+  if (items > INT_MAX - 8)
+    return fail(ATTN_E_SHAPE, "Hq x ceil(total_q / %d) = %lld work items exceeds %d",
+                attn::kPrefillBM, items, INT_MAX - 8);
+  const size_t need = attn_prefill_paged_cascade_workspace_size(dtype, total_q, Hq, D);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace_bytes);
+  if ((uintptr_t)workspace % 256 != 0)
+    return fail(ATTN_E_UNSUPPORTED, "workspace must be 256-byte aligned");
+  void* pre_o = workspace;
+  float* pre_lse = reinterpret_cast<float*>(
+      reinterpret_cast<char*>(workspace) +
+      round256((size_t)total_q * Hq * D * elem_bytes(dtype)));
+
+  attn::PrefillParams pre = p;
+  pre.B = 1;
+  pre.causal = 0;
+  pre.kv_len_fixed = shared_prefix_len;
+  pre.max_seqlen_q = total_q;
+  pre.q_tiles = (total_q + attn::kPrefillBM - 1) / attn::kPrefillBM;
+  pre.out = pre_o;
+  pre.lse = pre_lse;
+  hipError_t e = timed(ATTN_KERNEL_CASCADE_PREFIX, s,
+                       [&] { return attn::launch_prefill(pre, (int)dtype, D, true, s); });
+  if (e != hipSuccess) return fail(ATTN_E_HIP, "cascade prefix launch: %s", hipGetErrorString(e));
+
+  attn::PrefillParams suf = p;
+  suf.kv_offset = shared_prefix_len;
+  suf.merge_o = pre_o;
+  suf.merge_lse = pre_lse;
+  e = timed(ATTN_KERNEL_CASCADE_SUFFIX, s,
+            [&] { return attn::launch_prefill(suf, (int)dtype, D, true, s); });
+  if (e != hipSuccess) return fail(ATTN_E_HIP, "cascade suffix launch: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+attn_status attn_merge_states(attn_dtype dtype, const void* o_a, const float* lse_a,
+                              const void* o_b, const float* lse_b, int rows, int D, void* out,
+                              float* lse_out, void* stream) {
+  g_last_error[0] = 0;
+  if (!dtype_ok(dtype)) return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32/ATTN_BF16/ATTN_F16", dtype);
+  if (rows < 0 || D <= 0) return fail(ATTN_E_SHAPE, "rows=%d D=%d", rows, D);
+  if (!attn::merge_supported((int)dtype, D))
+    return fail(ATTN_E_UNSUPPORTED, "merge_states: D=%d not built (64, 128, 256)", D);
+  if (rows == 0) return ATTN_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !out || !lse_out)
+    return fail(ATTN_E_NULL, "a required pointer is NULL");
+  if (((uintptr_t)o_a | (uintptr_t)o_b | (uintptr_t)out) % 16 != 0)
+    return fail(ATTN_E_UNSUPPORTED, "o_a, o_b and out must be 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = timed(ATTN_KERNEL_MERGE, s, [&] {
+    return attn::launch_merge_states(o_a, lse_a, o_b, lse_b, out, lse_out, rows, (int)dtype, D, s);
+  });
+  if (e != hipSuccess) return fail(ATTN_E_HIP, "merge_states launch: %s", hipGetErrorString(e));
   return ATTN_OK;
 }
 

@@ -47,6 +47,17 @@ struct PrefillParams {
   int num_pages, max_pages;
   int causal;
   int q_tiles;             // ceil(max_seqlen_q / BM)
+  // Paged only.  Request b's keys start at column kv_offset / 16 of row b
+  // (row stride table_stride) and number kv_lens[b] - kv_offset; with
+  // kv_offset > 0 and causal, a request with fewer keys than queries is
+  // invalid (its rows become NaN).  When kv_len_fixed >= 0 the launch is
+  // instead one sequence of all total_q query rows attending to the first
+  // kv_len_fixed keys of page-table row 0 (cu_q, kv_lens unused).
+  int table_stride, kv_offset, kv_len_fixed;
+  // When merge_lse is set, the state (merge_o, merge_lse) -- laid out like
+  // out / lse -- is merged into each written row before it is stored.
+  const void* merge_o;
+  const float* merge_lse;
   float scale_log2;
 };
 
@@ -59,6 +70,13 @@ hipError_t launch_decode_combine(const DecodeParams& p, int dtype, int D, int G,
 #define ATTN_DECODE_GROUPS_PER_CU 1
 #endif
 constexpr int kDecodeGroupsPerCU = ATTN_DECODE_GROUPS_PER_CU;
+
+// Log-sum-exp merge of two states over `rows` (token, head) rows of D elements;
+// out / lse may alias the b side (each element is read before it is written
+// by the same thread).
+bool merge_supported(int dtype, int D);
+hipError_t launch_merge_states(const void* oa, const float* la, const void* ob, const float* lb,
+                               void* out, float* lse, long rows, int dtype, int D, hipStream_t s);
 
 // Query rows per workgroup of the prefill kernels (grid sizing on the host).
 constexpr int kPrefillBM = 128;

@@ -160,8 +160,9 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
   }
 
   // Sequence extents, clamped so every access stays inside the tensors.
-  const int q_start = min(max(p.cu_q[b], 0), p.total_q);
-  const int q_end = min(max(p.cu_q[b + 1], q_start), p.total_q);
+  const bool fixed = PAGED && p.kv_len_fixed >= 0;   // all rows, one key range
+  const int q_start = fixed ? 0 : min(max(p.cu_q[b], 0), p.total_q);
+  const int q_end = fixed ? p.total_q : min(max(p.cu_q[b + 1], q_start), p.total_q);
   const int Lq = q_end - q_start;
   const int r0 = tile * BM;
   if (r0 >= Lq) return;
@@ -169,9 +170,15 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
   int k_start = 0, Lk;
   const int32_t* table = nullptr;
   if constexpr (PAGED) {
-    Lk = p.kv_lens[b];
-    if (Lk < 0 || Lk > p.max_pages * kPage) { bad = true; Lk = 0; }
-    table = page_table + (size_t)b * p.max_pages;
+    if (fixed) {
+      Lk = p.kv_len_fixed;
+      table = page_table;
+    } else {
+      Lk = p.kv_lens[b] - p.kv_offset;
+      if (Lk < 0 || Lk > p.max_pages * kPage - p.kv_offset) { bad = true; Lk = 0; }
+      if (p.kv_offset > 0 && p.causal && Lk < Lq) bad = true;
+      table = page_table + (size_t)b * p.table_stride + p.kv_offset / kPage;
+    }
   } else {
     k_start = min(max(p.cu_k[b], 0), p.total_k);
     const int k_end = min(max(p.cu_k[b + 1], k_start), p.total_k);
@@ -591,14 +598,54 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
   if (!row_ok) return;
   const size_t orow = (size_t)(q_start + my_row) * p.Hq + head;
   elem* og = reinterpret_cast<elem*>(p.out) + orow * D;
+  if (p.merge_lse != nullptr) {
+    // Merge with another state over disjoint keys: with x = log2 of each
+    // normaliser and mx their max, the weights are 2^(x - mx).  Here the
+    // accumulator is unnormalised, so its weight per unit is 2^(m - mx).
+    // An empty state (lse -inf) contributes nothing; a NaN on either side,
+    // or an invalid request, gives NaN.
+    const float lp = p.merge_lse[orow] * kLog2e;
+    const float ls = ltot > 0.f ? m + log2_fast(ltot) : kNegInf;
+    const float mx = fmaxf(lp, ls);
+    float wo = 0.f, wp = 0.f;
+    if (any_bad || lp != lp) {
+      wo = __builtin_nanf("");
+      lse_v = wo;
+    } else if (mx == kNegInf) {
+      lse_v = kNegInf;
+    } else {
+      wp = exp2_fast(lp - mx);
+      const float ws = ltot > 0.f ? exp2_fast(m - mx) : 0.f;
+      const float den = wp + ws * ltot;
+      const float r = 1.f / den;
+      wo = ws * r;
+      wp *= r;
+      lse_v = (mx + log2_fast(den)) * kLn2;
+    }
+    const elem* pg = reinterpret_cast<const elem*>(p.merge_o) + orow * D;
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
+    for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      typename H::v4 v;
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d0 = db * 32 + a4 * 8 + hl * 4;
+        typename H::v4 v;
+        typename H::v4 w{};
+        if (wp != 0.f) w = *reinterpret_cast<const typename H::v4*>(pg + d0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = (elem)(o[db][a4 * 4 + j] * inv);
-      *reinterpret_cast<typename H::v4*>(og + db * 32 + a4 * 8 + hl * 4) = v;
+        for (int j = 0; j < 4; ++j) v[j] = (elem)(o[db][a4 * 4 + j] * wo + (float)w[j] * wp);
+        *reinterpret_cast<typename H::v4*>(og + d0) = v;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        typename H::v4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = (elem)(o[db][a4 * 4 + j] * inv);
+        *reinterpret_cast<typename H::v4*>(og + db * 32 + a4 * 8 + hl * 4) = v;
+      }
     }
   }
   if (hl == 0) p.lse[orow] = lse_v;

@@ -177,6 +177,68 @@ attn_status attn_prefill_paged(attn_dtype dtype, const void* q, const int32_t* c
                                int causal, float scale, void* out, float* lse, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Chunked prefill over a paged KV cache whose first shared_prefix_len tokens
+ * are the same pages for every request (shared-prefix reuse of the batch
+ * processing layer in "FlashInfer内核库深度解析"), computed as a cascade:
+ *   1. every query row of every request attends, without a mask, to the
+ *      shared prefix, read through the first shared_prefix_len / 16 entries
+ *      of page_table row 0 -- one pass over the prefix K/V for the whole
+ *      batch instead of one per request;
+ *   2. each request's rows attend to its own keys after the prefix (causal
+ *      or not, as in attn_prefill_paged) and, before being stored, are
+ *      merged with the result of pass 1 by the log-sum-exp rule of the
+ *      online softmax ("FlashAttention-3 ..." section 一).
+ * The result is that of attn_prefill_paged with the same arguments, up to
+ * rounding, provided that:
+ *   - every row of page_table starts with the same shared_prefix_len / 16
+ *     page ids (row 0's are the ones read);
+ *   - shared_prefix_len is a multiple of page_size and at most max_kv_len;
+ *   - kv_lens[b] >= shared_prefix_len, and with causal also
+ *     kv_lens[b] - shared_prefix_len >= Lq_b, i.e. every query of request b
+ *     sees the whole prefix.  Rows of a request that breaks this are NaN.
+ * shared_prefix_len = 0 is exactly attn_prefill_paged (no workspace used).
+ *
+ *  workspace  device memory of at least
+ *             attn_prefill_paged_cascade_workspace_size(dtype, total_q, Hq, D)
+ *             bytes, 256-byte aligned, owned by the caller; it holds the
+ *             pass-1 state (a [total_q, Hq, D] array of the input type and a
+ *             [total_q, Hq] float array); contents on entry do not matter.
+ *             Two calls sharing a workspace must not overlap.
+ * Other arguments, supported shapes and NaN rules as attn_prefill_paged;
+ * pass 1 also needs Hq * ceil(total_q / 128) below 2^31 - 8 (ATTN_E_SHAPE).
+ */
+size_t attn_prefill_paged_cascade_workspace_size(attn_dtype dtype, int total_q, int Hq, int D);
+attn_status attn_prefill_paged_cascade(attn_dtype dtype, const void* q,
+                                       const int32_t* cu_seqlens_q, const void* k_pages,
+                                       const void* v_pages, const int32_t* page_table,
+                                       const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                                       int total_q, int page_size, int num_pages,
+                                       int max_pages_per_req, int max_seqlen_q, int max_kv_len,
+                                       int shared_prefix_len, int causal, float scale, void* out,
+                                       float* lse, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Merge of two attention states over disjoint key sets of the same query
+ * rows: the aggregation step of the online softmax ("FlashAttention-3 ..."
+ * section 一) applied to finished partial results.  A state is (o, lse): o
+ * normalised over its keys, lse the natural log of its normaliser.  With
+ * mx = max(lse_a, lse_b) and w = exp(lse - mx) per side,
+ *   out = (w_a o_a + w_b o_b) / (w_a + w_b),  lse_out = mx + log(w_a + w_b).
+ * An empty side (lse = -inf) has weight 0 and its o is not read; both empty
+ * gives out = 0, lse_out = -inf; a NaN lse on either side gives NaN.
+ *
+ *  o_a, o_b, out       [rows, D] of dtype (F32, BF16 or F16), 16-byte aligned
+ *  lse_a, lse_b, lse_out  [rows] float
+ *  rows  number of (token, head) pairs;  D in {64, 128, 256}
+ * out may be o_a or o_b and lse_out may be lse_a or lse_b (in place); other
+ * overlaps are not allowed.  fp32 arithmetic, one rounding to dtype.
+ */
+attn_status attn_merge_states(attn_dtype dtype, const void* o_a, const float* lse_a,
+                              const void* o_b, const float* lse_b, int rows, int D, void* out,
+                              float* lse_out, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Status text (static strings) and the detail of the calling thread's last
  * failing call (valid until that thread's next call into the library). */
 const char* attn_status_string(attn_status s);
@@ -194,7 +256,10 @@ typedef enum {
   ATTN_KERNEL_DECODE_COMBINE = 1,
   ATTN_KERNEL_PREFILL = 2,
   ATTN_KERNEL_PREFILL_PAGED = 3,
-  ATTN_KERNEL_KINDS = 4
+  ATTN_KERNEL_MERGE = 4,
+  ATTN_KERNEL_CASCADE_PREFIX = 5,
+  ATTN_KERNEL_CASCADE_SUFFIX = 6,
+  ATTN_KERNEL_KINDS = 7
 } attn_kernel_kind;
 
 attn_status attn_timing_begin(int capacity);

@@ -151,6 +151,57 @@ def test_prefill_paged_rejects(lib):
     assert call(B=0, q=None) == OK
 
 
+def _cascade(lib, **kw):
+    a = dict(dtype=1, q=16, cq=16, k=16, v=16, t=16, lens=16, B=2, Hq=4, Hkv=4, D=256, Tq=10,
+             P=16, num_pages=10, max_pages=4, mq=5, mkv=64, prefix=32, causal=1, scale=0.1,
+             out=16, lse=16, ws=256, ws_bytes=1 << 20)
+    a.update(kw)
+    return lib.attn_prefill_paged_cascade(
+        a["dtype"], a["q"], a["cq"], a["k"], a["v"], a["t"], a["lens"], a["B"], a["Hq"], a["Hkv"],
+        a["D"], a["Tq"], a["P"], a["num_pages"], a["max_pages"], a["mq"], a["mkv"], a["prefix"],
+        a["causal"], a["scale"], a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+def test_cascade_rejects(lib):
+    assert _cascade(lib, prefix=8) == E_SHAPE           # not a whole number of pages
+    assert _cascade(lib, prefix=-16) == E_SHAPE
+    assert _cascade(lib, prefix=80) == E_SHAPE          # beyond max_kv_len
+    assert _cascade(lib, ws=None) == E_WS
+    need = lib.attn_prefill_paged_cascade_workspace_size(1, 10, 4, 256)
+    assert _cascade(lib, ws_bytes=need - 1) == E_WS
+    assert _cascade(lib, ws=512 + 16) == E_UNSUP        # workspace not 256-byte aligned
+    assert _cascade(lib, P=8) == E_UNSUP                # checks of attn_prefill_paged apply
+    assert _cascade(lib, t=None) == E_NULL
+    assert _cascade(lib, D=64) == E_UNSUP
+    # the prefix pass runs Hq x ceil(total_q / 128) work items: 2^14 x 2^17 overflows
+    assert _cascade(lib, B=1, Hq=1 << 14, Hkv=1 << 14, Tq=1 << 24, mq=16) == E_SHAPE
+    assert _cascade(lib, B=0, q=None, ws=None) == OK
+
+
+def test_cascade_workspace_size(lib):
+    # [total_q, Hq, D] of the input type + [total_q, Hq] float, each rounded up to 256 bytes
+    assert lib.attn_prefill_paged_cascade_workspace_size(1, 10, 4, 256) == 20480 + 256
+    assert lib.attn_prefill_paged_cascade_workspace_size(2, 8192, 16, 256) == (64 << 20) + (512 << 10)
+    assert lib.attn_prefill_paged_cascade_workspace_size(0, 3, 1, 64) == 768 + 256
+    assert lib.attn_prefill_paged_cascade_workspace_size(9, 3, 1, 64) == 0
+    assert lib.attn_prefill_paged_cascade_workspace_size(1, -1, 1, 64) == 0
+
+
+def test_merge_rejects(lib):
+    def call(**kw):
+        a = dict(dtype=1, oa=16, la=16, ob=16, lb=16, rows=10, D=128, out=16, lo=16)
+        a.update(kw)
+        return lib.attn_merge_states(a["dtype"], a["oa"], a["la"], a["ob"], a["lb"], a["rows"],
+                                     a["D"], a["out"], a["lo"], None)
+    assert call(dtype=3) == E_DTYPE
+    assert call(D=100) == E_UNSUP
+    assert call(D=0) == E_SHAPE
+    assert call(rows=-1) == E_SHAPE
+    assert call(lb=None) == E_NULL
+    assert call(out=24) == E_UNSUP
+    assert call(rows=0, oa=None) == OK
+
+
 def test_binding_rejects_host_tensors():
     import attention_qk_online_amd as A
     q = torch.zeros(2, 4, 128, dtype=torch.bfloat16)
