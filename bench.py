@@ -19,8 +19,9 @@ in HBM but not in the MALL or the L2s.  Call times come from one event
 pair per segment of the timed steps (mean, median and minimum); per-kernel
 durations (the roofline figures) from a second pass in which the library
 records HIP events around each of its launches on the launch stream.  Also
-reported: the launch-bound fp32 single-sequence decode and the 1K-32K
-single-sequence causal prefill sweep.  The CPU oracle is timed on the host
+reported: the chunked workload through the shared-prefix cascade, the
+launch-bound fp32 single-sequence decode and the 1K-32K single-sequence
+causal prefill sweep.  The CPU oracle is timed on the host
 cores over the whole decode workload (repeated to at least ~10 s), as a
 reported baseline.
 
@@ -221,6 +222,44 @@ def main():
             "roofline": roofline_mfma(pg_flops, paged_ms, "prefill_paged"),
         },
     }
+
+    # The chunked workload again through the shared-prefix cascade: one pass
+    # of every query row over the 4096 shared tokens, then each request over
+    # its own keys with the merge fused into the store.  Same flops as the
+    # direct call (the work is split, not skipped).
+    prefix_len = pg.shared_pages * pg.page_size
+    c_ws = torch.empty(A.prefill_paged_cascade_workspace_size(pg.dtype, g_q.shape[0], pg.Hq, pg.D),
+                       dtype=torch.uint8, device=dev)
+
+    def cascade():
+        A.prefill_paged_cascade(g_q, g_cq, g_kp, g_vp, g_table, g_lens, pg.max_seqlen_q,
+                                pg.max_kv_len, prefix_len, causal=True, scale=pg.scale, out=g_out,
+                                lse=g_lse, workspace=c_ws)
+    for _ in range(2):
+        cascade()
+    torch.cuda.synchronize()
+    c_ms = []
+    for i in range(K):
+        flush()
+        ev[i][0].record(stream)
+        cascade()
+        ev_end[i][0].record(stream)
+    torch.cuda.synchronize()
+    c_ms = sorted(ev[i][0].elapsed_time(ev_end[i][0]) for i in range(K))
+    A.timing_begin(2 * K + 4)
+    for i in range(K):
+        flush()
+        cascade()
+    kc = A.timing_end()
+    c_mean = sum(c_ms) / K
+    res["prefill_paged"]["cascade"] = {
+        "shared_prefix_len": prefix_len,
+        "value": round(pg_flops / (c_mean * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "call_ms": round(c_mean, 4), "call_ms_stats": stats(c_ms),
+        "prefix_kernel_ms": round(kc["cascade_prefix"][0] / kc["cascade_prefix"][1], 4),
+        "suffix_kernel_ms": round(kc["cascade_suffix"][0] / kc["cascade_suffix"][1], 4),
+        "speedup_vs_direct": round(ms_paged / c_mean, 4)}
+    log("bench: cascade", res["prefill_paged"]["cascade"])
 
     # Single-sequence fp32 decode (1 query token, 4 heads, head_dim 64, 256
     # contiguous keys as an identity-paged NHD view): launch-latency bound.
