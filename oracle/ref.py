@@ -17,7 +17,10 @@ Sources:
   a ``causal`` flag and the default scale 1/sqrt(head_dim).  Section 四: the
   rescaling must stay, i.e. results must survive large logits.
 * "FlashInfer内核库深度解析" (bxzpzcl.cn), PageAttention paragraph: the KV
-  cache is cut into fixed-size pages addressed through a table.
+  cache is cut into fixed-size pages addressed through a table; precision
+  support: FP8 besides FP16/BF16.  FA-3 page section 一: with FP8 the
+  quantisation scale joins the softmax's exponent scaling.  The FP8 cache is
+  read as E4M3 bytes with one scale per K and V tensor.
 
 Readings where the pages are silent:
 * LSE is the natural log of the sum of exp of the *scaled* visible logits.
@@ -119,6 +122,58 @@ def ref_decode_paged(q, k_pages, v_pages, page_table, kv_lens, scale,
         L = int(kv_lens[b])
         k = gather_pages(k_pages, page_table[b], L)
         v = gather_pages(v_pages, page_table[b], L)
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            o, l = softmax_attend(q[b, h:h + 1], k[:, g], v[:, g], scale)
+            out[b, h] = o[0]
+            lse[b, h] = l[0]
+    return out, lse
+
+
+def fp8_e4m3_to_float(b: torch.Tensor) -> torch.Tensor:
+    """Value of each byte read as an OCP 8-bit float E4M3 (the variant without
+    infinities), as float64.
+
+    Bit 7 is the sign, bits 6..3 the exponent e (bias 7), bits 2..0 the
+    mantissa m.  e = 0 is subnormal: m/8 * 2^-6.  Otherwise the value is
+    (1 + m/8) * 2^(e-7), including e = 15 with m < 7 (up to 448); only
+    S.1111.111 is NaN.  The pages name FP8 tensor-core arithmetic
+    ("FlashInfer内核库深度解析", precision support) without fixing the
+    encoding; E4M3 is the format read here.
+    """
+    x = b.to(torch.int64) & 0xFF
+    sign = (x >> 7) & 1
+    e = (x >> 3) & 0xF
+    m = (x & 7).to(F64)
+    sub = m / 8.0 * 2.0 ** -6
+    norm = (1.0 + m / 8.0) * torch.pow(torch.full_like(m, 2.0), (e - 7).to(F64))
+    mag = torch.where(e == 0, sub, norm)
+    val = torch.where(sign == 1, -mag, mag)
+    return torch.where((e == 15) & ((x & 7) == 7), torch.full_like(val, float("nan")), val)
+
+
+def ref_decode_paged_fp8(q, k_pages, v_pages, k_scale: float, v_scale: float, page_table, kv_lens,
+                         scale, requests: Optional[Iterable[int]] = None):
+    """Decode over a KV cache stored as E4M3 bytes with one scale per tensor:
+    each key is k_scale times the value of its bytes, each value vector
+    v_scale times the value of its bytes; then plain decode attention.  (In
+    "FlashAttention-3 内核在最新大模型推理中的集成实践" section 一 the FP8
+    scale is folded into the softmax's exponent scaling; mathematically that
+    is this product.)
+
+    k_pages / v_pages: uint8 [num_pages, P, Hkv, D]; other arguments and the
+    result as :func:`ref_decode_paged`.  Only the tokens a request uses are
+    decoded.
+    """
+    B, Hq, D = q.shape
+    Hkv = k_pages.shape[2]
+    _check_heads(Hq, Hkv)
+    out = torch.full((B, Hq, v_pages.shape[3]), float("nan"), dtype=F64)
+    lse = torch.full((B, Hq), float("nan"), dtype=F64)
+    for b in (range(B) if requests is None else requests):
+        L = int(kv_lens[b])
+        k = fp8_e4m3_to_float(gather_pages(k_pages, page_table[b], L)) * float(k_scale)
+        v = fp8_e4m3_to_float(gather_pages(v_pages, page_table[b], L)) * float(v_scale)
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
             o, l = softmax_attend(q[b, h:h + 1], k[:, g], v[:, g], scale)

@@ -26,6 +26,8 @@ F64 = torch.float64
 
 def _ev(x):
     env = {"log": math.log, "sqrt": math.sqrt, "nan": math.nan, "inf": math.inf}
+    if isinstance(x, str) and x.strip() == "-0":
+        return -0.0
     return float(eval(x, {"__builtins__": {}}, env)) if isinstance(x, str) else float(x)
 
 
@@ -57,6 +59,21 @@ def pin_golden(R):
             o, l = R.ref_prefill_varlen(_tensor(g["q"]), _tensor(g["k"]), _tensor(g["v"]),
                                         g["cu_seqlens_q"], g["cu_seqlens_k"], g["causal"],
                                         _ev(g["scale"]))
+        elif g["kind"] == "fp8_e4m3":
+            got = R.fp8_e4m3_to_float(torch.tensor([b for b, _ in g["values"]], dtype=torch.uint8))
+            want = torch.tensor([_ev(v) for _, v in g["values"]], dtype=F64)
+            assert torch.equal(torch.isnan(got), torch.isnan(want)), fn
+            ok = ~torch.isnan(want)
+            assert torch.equal(got[ok], want[ok]), fn
+            assert torch.equal(torch.signbit(got[ok]), torch.signbit(want[ok])), fn
+            continue
+        elif g["kind"] == "decode_fp8":
+            o, l = R.ref_decode_paged_fp8(_tensor(g["q"]),
+                                          torch.tensor(g["k_pages"], dtype=torch.uint8),
+                                          torch.tensor(g["v_pages"], dtype=torch.uint8),
+                                          _ev(g["k_scale"]), _ev(g["v_scale"]),
+                                          torch.tensor(g["page_table"]), torch.tensor(g["kv_lens"]),
+                                          _ev(g["scale"]))
         elif g["kind"] == "decode":
             o, l = R.ref_decode_paged(_tensor(g["q"]), _tensor(g["k_pages"]), _tensor(g["v_pages"]),
                                       torch.tensor(g["page_table"]), torch.tensor(g["kv_lens"]),
@@ -300,10 +317,41 @@ def pin_rows_subset(R):
     assert torch.isnan(o2[1]).all()
 
 
+def pin_fp8_decoder_library(R):
+    """Every byte decodes as torch's float8_e4m3fn reads it."""
+    b = torch.arange(256, dtype=torch.int64).to(torch.uint8)
+    got = R.fp8_e4m3_to_float(b)
+    want = b.view(torch.float8_e4m3fn).to(F64)
+    assert torch.equal(torch.isnan(got), torch.isnan(want))
+    ok = ~torch.isnan(want)
+    assert torch.equal(got[ok], want[ok])
+
+
+def pin_fp8_decode_equals_dequantised(R):
+    """Decode over E4M3 bytes equals plain decode over the same cache decoded by
+    torch and scaled (k_scale on K, v_scale on V), including subnormal bytes."""
+    c = workloads.make_decode(B=3, Hq=4, Hkv=2, D=8, page_size=4, kv_lens=[5, 9, 1], dtype=F64,
+                              seed=30)
+    kb, vb, ks, vs = c.fp8_pools()
+    kb = kb.clone()
+    kb[c.page_table[1, 0], 1, 0, :4] = torch.tensor([1, 3, 0x81, 0x87], dtype=torch.uint8)
+    kf = kb.view(torch.float8_e4m3fn).to(F64) * ks
+    vf = vb.view(torch.float8_e4m3fn).to(F64) * vs
+    o, l = R.ref_decode_paged_fp8(c.q, kb, vb, ks, vs, c.page_table, c.kv_lens, c.scale)
+    o2, l2 = R.ref_decode_paged(c.q, kf, vf, c.page_table, c.kv_lens, c.scale)
+    _close(o, o2, 1e-13)
+    _close(l, l2, 1e-13)
+    # the scales are where they belong: k_scale * scale is one factor, v_scale is linear
+    o3, l3 = R.ref_decode_paged_fp8(c.q, kb, vb, 2 * ks, 3 * vs, c.page_table, c.kv_lens,
+                                    c.scale / 2)
+    _close(o3, 3 * o, 1e-12)
+    _close(l3, l, 1e-12)
+
+
 PINS = [pin_golden, pin_brute_force, pin_sdpa_library, pin_single_key, pin_constant_v,
         pin_scale_zero_mean, pin_shift_invariance, pin_paging, pin_gqa_equals_repeated_mha,
         pin_causal_rows, pin_chunked_equals_full, pin_merge_partition, pin_empty_rows,
-        pin_rows_subset]
+        pin_rows_subset, pin_fp8_decoder_library, pin_fp8_decode_equals_dequantised]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -324,6 +372,10 @@ MUTANTS = {
     "merge_linear_weights": ("w = torch.exp(lses - mx.unsqueeze(0))",
                              "w = torch.softmax(lses, dim=0) + 0 * mx"),
     "mask_strict": ("<= (rows.long().unsqueeze(1) + offset)", "< (rows.long().unsqueeze(1) + offset)"),
+    "fp8_exponent_bias": ("(e - 7).to(F64)", "(e - 8).to(F64)"),
+    "fp8_subnormal_as_normal": ("mag = torch.where(e == 0, sub, norm)", "mag = norm"),
+    "fp8_nan_on_exponent_15": ("(e == 15) & ((x & 7) == 7)", "(e == 15)"),
+    "fp8_k_scale_on_values": ("* float(v_scale)", "* float(k_scale)"),
     "softmax_no_exp_shift": ("p = torch.exp(s - torch.where(empty, torch.zeros_like(lse), lse).unsqueeze(1))",
                              "p = torch.exp(s - torch.where(empty, torch.zeros_like(m), m).unsqueeze(1))"),
 }

@@ -102,6 +102,33 @@ class DecodeCase:
     def kv_bytes(self) -> int:
         return decode_kv_bytes(self.kv_lens, self.Hkv, self.D, self.dtype)
 
+    def fp8_pools(self, device="cpu"):
+        """The same cache stored as 8-bit floats E4M3 with one scale per tensor.
+
+        Each of K and V is divided by amax/448 (448 = the largest E4M3
+        value) and rounded to E4M3 by torch's float8_e4m3fn conversion; the
+        pools hold the raw bytes (uint8), unreferenced slots 0x7F (NaN) when
+        the case is poisoned.  Returns (k_pages, v_pages, k_scale, v_scale):
+        token t's key is k_scale * E4M3(k_pages[...]).
+        """
+        shape = (self.num_pages, self.page_size, self.Hkv, self.D)
+        idx = self.slot_index.to(device)
+        out = []
+        for tok in (self.k_tok, self.v_tok):
+            x = tok.float()
+            amax = float(x.abs().max()) if x.numel() else 0.0
+            sc = amax / 448.0 if amax > 0 else 1.0
+            q8 = (x / sc).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+            pool = torch.full(shape, 0x7F if self.poison else 0, dtype=torch.uint8, device=device)
+            flat = pool.view(self.num_pages * self.page_size, self.Hkv, self.D)
+            flat.index_copy_(0, idx, q8.to(device))
+            out += [pool, sc]
+        return out[0], out[2], out[1], out[3]
+
+    def fp8_kv_bytes(self) -> int:
+        """Algorithmic K+V bytes of the E4M3 cache: 2*Hkv*D*sum(kv_len)."""
+        return int(2 * self.Hkv * self.D * int(self.kv_lens.long().sum().item()))
+
 
 def decode_kv_bytes(kv_lens, Hkv, D, dtype) -> int:
     """Algorithmic K+V bytes a decode call must stream: 2*Hkv*D*esize*sum(kv_len)."""
