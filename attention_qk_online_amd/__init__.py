@@ -11,6 +11,8 @@ Entry points (names follow the C ABI):
 * :func:`decode_paged` -- batched decode over a paged KV cache (split-KV +
   log-sum-exp merge), the analogue of FlashInfer's single/batch decode calls
   described in "FlashInfer内核库深度解析".
+* :func:`decode_paged_fp8` -- the same over a cache of 8-bit E4M3 floats with
+  one scale per K / V tensor (half the bytes streamed).
 * :func:`prefill_varlen` -- ragged (causal) prefill addressed by cu_seqlens,
   with the argument list of ``varlen_fwd`` in "FlashAttention-3 内核在最新大模型
   推理中的集成实践" section 二.
@@ -32,7 +34,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["decode_paged", "decode_paged_workspace_size", "prefill_varlen", "prefill_paged",
+__all__ = ["decode_paged", "decode_paged_fp8", "decode_paged_workspace_size", "prefill_varlen", "prefill_paged",
            "prefill_paged_cascade", "prefill_paged_cascade_workspace_size", "merge_states",
            "timing_begin", "timing_end", "library_path", "load_library", "AttnError",
            "KERNEL_KINDS"]
@@ -76,6 +78,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_decode_paged.restype = c_int
     lib.attn_decode_paged.argtypes = [c_int, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int,
                                       c_int, c_int, c_int, c_int, c_float, vp, vp, vp, c_size, vp]
+    lib.attn_decode_paged_fp8.restype = c_int
+    lib.attn_decode_paged_fp8.argtypes = [c_int, vp, vp, vp, vp, vp] + [c_int] * 9 + [
+        c_float, c_float, c_float, vp, vp, vp, c_size, vp]
     lib.attn_prefill_varlen.restype = c_int
     lib.attn_prefill_varlen.argtypes = [c_int, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int,
                                         c_int, c_int, c_int, c_int, c_float, vp, vp, vp]
@@ -156,23 +161,14 @@ def decode_paged_workspace_size(dtype: torch.dtype, B: int, Hq: int, Hkv: int, D
                                                                max_kv_len, split_pages))
 
 
-def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
-                 page_table: torch.Tensor, kv_lens: torch.Tensor, scale: Optional[float] = None,
-                 max_kv_len: Optional[int] = None, split_pages: int = 0,
-                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Batched decode over a paged KV cache.
-
-    q [B, Hq, D]; k_pages, v_pages [num_pages, page_size, Hkv, D] (NHD);
-    page_table [B, max_pages] int32; kv_lens [B] int32.  ``max_kv_len`` is a
-    host bound on every kv_len; when omitted it is read from ``kv_lens`` with
-    one device-to-host copy.  Returns (out [B, Hq, D], lse [B, Hq] float32).
-    """
+def _decode(q, k_pages, v_pages, page_table, kv_lens, scale, max_kv_len, split_pages, out, lse,
+            workspace, fp8_scales=None):
     lib = load_library()
     dt = _dtype_code(q)
+    kv_dtype = q.dtype if fp8_scales is None else torch.uint8
     pq = _dev(q, "q", dim=3)
-    pk = _dev(k_pages, "k_pages", q.dtype, 4)
-    pv = _dev(v_pages, "v_pages", q.dtype, 4)
+    pk = _dev(k_pages, "k_pages", kv_dtype, 4)
+    pv = _dev(v_pages, "v_pages", kv_dtype, 4)
     pt = _dev(page_table, "page_table", torch.int32, 2)
     pl = _dev(kv_lens, "kv_lens", torch.int32, 1)
     B, Hq, D = q.shape
@@ -198,11 +194,45 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
     if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     pw = _dev(workspace, "workspace")
-    _check(lib.attn_decode_paged(dt, pq, pk, pv, pt, pl, B, Hq, Hkv, D, page_size, num_pages,
-                                 page_table.shape[1], max_kv_len, split_pages, s, out.data_ptr(),
-                                 lse.data_ptr(), pw, workspace.numel() * workspace.element_size(),
-                                 _stream(q.device)))
+    args = (pq, pk, pv, pt, pl, B, Hq, Hkv, D, page_size, num_pages, page_table.shape[1],
+            max_kv_len, split_pages, s)
+    tail = (out.data_ptr(), lse.data_ptr(), pw, workspace.numel() * workspace.element_size(),
+            _stream(q.device))
+    if fp8_scales is None:
+        _check(lib.attn_decode_paged(dt, *args, *tail))
+    else:
+        _check(lib.attn_decode_paged_fp8(dt, *args, float(fp8_scales[0]), float(fp8_scales[1]),
+                                         *tail))
     return out, lse
+
+
+def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                 page_table: torch.Tensor, kv_lens: torch.Tensor, scale: Optional[float] = None,
+                 max_kv_len: Optional[int] = None, split_pages: int = 0,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Batched decode over a paged KV cache.
+
+    q [B, Hq, D]; k_pages, v_pages [num_pages, page_size, Hkv, D] (NHD);
+    page_table [B, max_pages] int32; kv_lens [B] int32.  ``max_kv_len`` is a
+    host bound on every kv_len; when omitted it is read from ``kv_lens`` with
+    one device-to-host copy.  Returns (out [B, Hq, D], lse [B, Hq] float32).
+    """
+    return _decode(q, k_pages, v_pages, page_table, kv_lens, scale, max_kv_len, split_pages, out,
+                   lse, workspace)
+
+
+def decode_paged_fp8(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                     page_table: torch.Tensor, kv_lens: torch.Tensor, k_scale: float,
+                     v_scale: float, scale: Optional[float] = None,
+                     max_kv_len: Optional[int] = None, split_pages: int = 0,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """:func:`decode_paged` over a cache of E4M3 bytes (uint8 pools): token t's
+    key is ``k_scale * E4M3(k_pages[...])`` and its value ``v_scale * E4M3(...)``.
+    q and out are bf16 or fp16."""
+    return _decode(q, k_pages, v_pages, page_table, kv_lens, scale, max_kv_len, split_pages, out,
+                   lse, workspace, fp8_scales=(k_scale, v_scale))
 
 
 def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,

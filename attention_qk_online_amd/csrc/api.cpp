@@ -171,15 +171,21 @@ size_t attn_decode_paged_workspace_size(attn_dtype dtype, int B, int Hq, int Hkv
   return plan_decode((int)dtype, B, Hq, Hkv, D, page_size, max_kv_len, split_pages).bytes;
 }
 
-attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pages,
-                              const void* v_pages, const int32_t* page_table,
-                              const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
-                              int page_size, int num_pages, int max_pages_per_req,
-                              int max_kv_len, int split_pages, float scale, void* out,
-                              float* lse, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+// Both decode entry points; fp8_kv: the pages hold E4M3 bytes with scales
+// k_scale / v_scale.
+static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, const void* q, const void* k_pages,
+                               const void* v_pages, const int32_t* page_table,
+                               const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                               int page_size, int num_pages, int max_pages_per_req,
+                               int max_kv_len, int split_pages, float scale, float k_scale,
+                               float v_scale, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
   if (!dtype_ok(dtype)) return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32/ATTN_BF16/ATTN_F16", dtype);
+  if (fp8_kv && dtype == ATTN_F32)
+    return fail(ATTN_E_UNSUPPORTED, "decode_paged_fp8: queries must be ATTN_BF16 or ATTN_F16");
+  if (fp8_kv && (!std::isfinite(k_scale) || !std::isfinite(v_scale)))
+    return fail(ATTN_E_VALUE, "k_scale / v_scale not finite");
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || num_pages < 0 ||
       max_pages_per_req < 0 || max_kv_len < 0 || split_pages < 0)
     return fail(ATTN_E_SHAPE,
@@ -224,11 +230,12 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pag
   p.hw = Hkv < 8 ? Hkv : 8;
   p.nhg = (Hkv + p.hw - 1) / p.hw;
   p.n_groups = attn::kDecodeGroupsPerCU * device_cus();
-  p.scale_log2 = scale * kLog2e;
+  p.scale_log2 = fp8_kv ? scale * k_scale * kLog2e : scale * kLog2e;
+  p.v_scale = fp8_kv ? v_scale : 1.f;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = timed(ATTN_KERNEL_DECODE_SPLIT, s,
-                       [&] { return attn::launch_decode_split(p, (int)dtype, D, G, s); });
+                       [&] { return attn::launch_decode_split(p, (int)dtype, D, G, fp8_kv, s); });
   if (e != hipSuccess)
     return fail(ATTN_E_HIP, "decode_split launch: %s", hipGetErrorString(e));
   if (dtype != ATTN_F32 || pl.n_splits > 1) {
@@ -238,6 +245,30 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pag
       return fail(ATTN_E_HIP, "decode_combine launch: %s", hipGetErrorString(e));
   }
   return ATTN_OK;
+}
+
+attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pages,
+                              const void* v_pages, const int32_t* page_table,
+                              const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                              int page_size, int num_pages, int max_pages_per_req,
+                              int max_kv_len, int split_pages, float scale, void* out,
+                              float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return decode_impl(dtype, false, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
+                     page_size, num_pages, max_pages_per_req, max_kv_len, split_pages, scale, 1.f,
+                     1.f, out, lse, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_paged_fp8(attn_dtype dtype, const void* q, const void* k_pages,
+                                  const void* v_pages, const int32_t* page_table,
+                                  const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                                  int page_size, int num_pages, int max_pages_per_req,
+                                  int max_kv_len, int split_pages, float scale, float k_scale,
+                                  float v_scale, void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return decode_impl(dtype, true, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
+                     page_size, num_pages, max_pages_per_req, max_kv_len, split_pages, scale,
+                     k_scale, v_scale, out, lse, workspace, workspace_bytes, stream);
 }
 
 static attn_status check_prefill_common(attn_dtype dtype, int B, int Hq, int Hkv, int D,

@@ -29,8 +29,10 @@ struct f16_t {
 };
 
 // The two 16-bit input formats on the matrix cores: operand vectors, the
-// element type (float -> element conversion rounds to nearest even) and the
-// MFMA shapes and dot product the kernels use, all with fp32 accumulation.
+// element type (float -> element conversion rounds to nearest even), the
+// MFMA shapes and dot product the kernels use, all with fp32 accumulation,
+// and the conversion from 8-bit E4M3 floats (exact in both formats: E4M3
+// spans 2^-9 .. 448 with 3 mantissa bits).
 template <typename E>
 struct Half16;
 template <>
@@ -51,6 +53,11 @@ struct Half16<bf16_t> {
   static __device__ __forceinline__ float dot2(v2 a, v2 b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
   }
+  // Two E4M3 bytes (the low or high half of w) -> two elements, exactly.
+  template <bool HI>
+  static __device__ __forceinline__ v2 from_fp8x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+  }
 };
 template <>
 struct Half16<f16_t> {
@@ -69,6 +76,10 @@ struct Half16<f16_t> {
   }
   static __device__ __forceinline__ float dot2(v2 a, v2 b, float c) {
     return __builtin_amdgcn_fdot2(a, b, c, false);
+  }
+  template <bool HI>
+  static __device__ __forceinline__ v2 from_fp8x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
   }
 };
 

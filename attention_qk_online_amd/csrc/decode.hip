@@ -309,6 +309,16 @@ __global__ __launch_bounds__(kNW * 64) void decode_split_kernel(DecodeParams p) 
 //        fragments via ds_read_b64_tr_b16; P^T is the S^T accumulator as is)
 // so per page only a few dozen vector instructions remain and the kernel is
 // bound by HBM.  Pages are loaded in batches of NB per wave.
+//
+// With an 8-bit E4M3 cache (F8) the same schedule streams half the bytes:
+// each lane loads 16-byte chunks of K (two k-steps' worth; the head
+// dimension is permuted identically in Q and K so that a chunk is
+// contiguous in memory) and of V, and converts them exactly to the 16-bit
+// type in registers (v_cvt_scalef32_pk_{bf16,f16}_fp8) before the MFMAs and
+// the LDS transpose.  The key scale is folded into the softmax exponent's
+// scale on the host and the value scale into the final normalisation
+// ("FlashAttention-3 ..." section 一: with FP8 the quantisation scale joins
+// the exponent scaling instead of costing a separate pass).
 template <int D>
 struct MfmaDecodeCfg {
   static constexpr int KS = D / 32;          // 16x16x32 k-steps for Q.K
@@ -372,14 +382,26 @@ __device__ __forceinline__ char* decode_vbuf(int wave) {
   return vbuf[wave];
 }
 
+// Eight E4M3 bytes (two words) -> eight 16-bit elements, exactly.
+template <typename H>
+__device__ __forceinline__ typename H::v8 fp8x8(uint32_t w0, uint32_t w1) {
+  const typename H::v2 a = H::template from_fp8x2<false>(w0), b = H::template from_fp8x2<true>(w0);
+  const typename H::v2 c = H::template from_fp8x2<false>(w1), d = H::template from_fp8x2<true>(w1);
+  return typename H::v8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // One run [u0, u1) of the balanced schedule.  A unit is one page of one
 // group of hw KV heads; wave w of the workgroup folds KV head hg * hw + w of
 // every unit, so a workgroup reads whole pages (all heads of a token are
 // adjacent in the NHD layout).
-template <typename E, int D, int G, int NB>
+template <typename E, int D, int G, int NB, bool F8>
 __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1, int W, int lane,
                                            int wave) {
   using C = MfmaDecodeCfg<D>;
+  constexpr int GROWB = F8 ? D : 2 * D;                  // bytes of one K/V row in the cache
+  constexpr int NK = F8 ? C::KS / 2 : C::KS;             // 16-byte K loads per lane per page
+  constexpr int NV = F8 ? C::LV / 2 : C::LV;             // 16-byte V loads per lane per page
+  constexpr int CHG = GROWB / 16;                        // 16-byte chunks per cache row
   using H = Half16<E>;
   using elem = typename H::elem;
   const int l16 = lane & 15, gq = lane >> 4;
@@ -404,12 +426,12 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
   char* myv = decode_vbuf<D>(wave);
   const char* kbase = reinterpret_cast<const char*>(p.k_pages);
   const char* vbase = reinterpret_cast<const char*>(p.v_pages);
-  const size_t tok_b = (size_t)p.Hkv * C::ROWB;           // bytes between tokens
+  const size_t tok_b = (size_t)p.Hkv * GROWB;            // bytes between tokens
   const float c = p.scale_log2;
   const float qnan = __builtin_nanf("");
 
   struct Page {
-    u32x4 k[C::KS], v[C::LV];
+    u32x4 k[NK], v[NV];
     bool ok;
   };
 
@@ -432,14 +454,16 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
     const bool whole = start_pair / W == (start_pair + np - 1) / W;
     const int len = min(p.kv_lens[b], np * kPage);     // valid tokens (clamped, >= 1 page)
 
-    // Q^T fragments: lane (head l16, k-group gq) holds q[head][32 ks + 8 gq .. +8].
+    // Q^T fragments: lane (head l16, k-group gq) holds q[head][32 ks + 8 gq .. +8]
+    // (F8: q[head][64 (ks/2) + 16 gq + 8 (ks%2) .. +8], the order of its K chunks).
     typename H::v8 qf[C::KS];
     {
       const elem* qh = reinterpret_cast<const elem*>(p.q) +
-                         ((size_t)b * p.Hq + (size_t)kvh * G + (l16 < G ? l16 : 0)) * D + 8 * gq;
+                         ((size_t)b * p.Hq + (size_t)kvh * G + (l16 < G ? l16 : 0)) * D;
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const typename H::v8 v = *reinterpret_cast<const typename H::v8*>(qh + 32 * ks);
+        const int d0 = F8 ? 64 * (ks / 2) + 16 * gq + 8 * (ks % 2) : 32 * ks + 8 * gq;
+        const typename H::v8 v = *reinterpret_cast<const typename H::v8*>(qh + d0);
         qf[ks] = l16 < G ? v : typename H::v8{};
       }
     }
@@ -448,8 +472,8 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
     for (int i = 0; i < C::DB; ++i) o[i] = f32x4{};
     float m = kNegInf, lsum = 0.f;
     bool bad = false;
-    const char* kh = kbase + (size_t)kvh * C::ROWB;
-    const char* vh = vbase + (size_t)kvh * C::ROWB;
+    const char* kh = kbase + (size_t)kvh * GROWB;
+    const char* vh = vbase + (size_t)kvh * GROWB;
     const int32_t* table = p.page_table + (size_t)b * p.max_pages + pg0;
 
     for (int c0 = 0; c0 < n; c0 += 64) {
@@ -462,12 +486,14 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
         const char* kp = kh + (size_t)pid * kPage * tok_b;
         const char* vp = vh + (size_t)pid * kPage * tok_b;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-          pg.k[ks] = *reinterpret_cast<const u32x4*>(kp + l16 * tok_b + (32 * ks + 8 * gq) * 2);
+        for (int j = 0; j < NK; ++j) {
+          const int off = F8 ? 64 * j + 16 * gq : (32 * j + 8 * gq) * 2;
+          pg.k[j] = *reinterpret_cast<const u32x4*>(kp + l16 * tok_b + off);
+        }
 #pragma unroll
-        for (int j = 0; j < C::LV; ++j) {
+        for (int j = 0; j < NV; ++j) {
           const int ci = lane + 64 * j;
-          pg.v[j] = *reinterpret_cast<const u32x4*>(vp + (ci / C::CHV) * tok_b + (ci % C::CHV) * 16);
+          pg.v[j] = *reinterpret_cast<const u32x4*>(vp + (ci / CHG) * tok_b + (ci % CHG) * 16);
         }
       };
       auto fold = [&](int i, Page& pg) {
@@ -478,16 +504,30 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
         const int nval = len - (pg0 + c0 + i) * kPage;   // valid tokens in this page
         // V rows to LDS (rows past the end zeroed: poisoned slots must not reach O)
 #pragma unroll
-        for (int j = 0; j < C::LV; ++j) {
+        for (int j = 0; j < NV; ++j) {
           const int ci = lane + 64 * j;
-          const int t = ci / C::CHV, ch = ci % C::CHV;
+          const int t = ci / CHG, ch = ci % CHG;
           const u32x4 v = t < nval ? pg.v[j] : u32x4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(myv + vpage_off<D>(t, ch * 8)) = v;
+          if constexpr (F8) {
+            // 16 bytes -> 16 elements, one 32-byte unit of the LDS row
+            char* dst = myv + vpage_off<D>(t, ch * 16);
+            *reinterpret_cast<typename H::v8*>(dst) = fp8x8<H>(v[0], v[1]);
+            *reinterpret_cast<typename H::v8*>(dst + 16) = fp8x8<H>(v[2], v[3]);
+          } else {
+            *reinterpret_cast<u32x4*>(myv + vpage_off<D>(t, ch * 8)) = v;
+          }
         }
         f32x4 s = {};
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-          s = H::mfma16x16x32(__builtin_bit_cast(typename H::v8, pg.k[ks]), qf[ks], s);
+        for (int ks = 0; ks < C::KS; ++ks) {
+          typename H::v8 kf;
+          if constexpr (F8)
+            kf = ks % 2 == 0 ? fp8x8<H>(pg.k[ks / 2][0], pg.k[ks / 2][1])
+                             : fp8x8<H>(pg.k[ks / 2][2], pg.k[ks / 2][3]);
+          else
+            kf = __builtin_bit_cast(typename H::v8, pg.k[ks]);
+          s = H::mfma16x16x32(kf, qf[ks], s);
+        }
         float mx = kNegInf;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -536,7 +576,7 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
 
     // Finish the piece: lane (head l16, group gq) holds d = 16 db + 4 gq + rr.
     const float ltot = sum_halves(lsum + shfl_xor_f32(lsum, 16));
-    float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    float inv = ltot > 0.f ? (F8 ? p.v_scale : 1.f) / ltot : 0.f;
     float lse_nat = ltot > 0.f ? (m + log2_fast(ltot)) * kLn2 : kNegInf;
     if (bad) { inv = qnan; lse_nat = qnan; }
     if (l16 < G) {
@@ -568,7 +608,7 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
   }
 }
 
-template <typename E, int D, int G, int NB>
+template <typename E, int D, int G, int NB, bool F8>
 __global__ __launch_bounds__(kMaxGroupWaves * 64, D == 256 ? 1 : 2) void decode_mfma_kernel(DecodeParams p) {
   static_assert(G >= 1 && G <= 16, "one 16-column MFMA tile holds the query heads");
   const int lane = threadIdx.x & 63;
@@ -577,7 +617,7 @@ __global__ __launch_bounds__(kMaxGroupWaves * 64, D == 256 ? 1 : 2) void decode_
   const int U = total_units(p);
   const int W = run_length(p, U);
   for (int run = blockIdx.x; (long)run * W < U; run += gridDim.x) {
-    decode_run<E, D, G, NB>(p, run * W, min(run * W + W, U), W, lane, wave);
+    decode_run<E, D, G, NB, F8>(p, run * W, min(run * W + W, U), W, lane, wave);
   }
 }
 
@@ -697,10 +737,14 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
 }
 
 template <typename T, int D, int G>
-hipError_t launch_split_t(const DecodeParams& p, hipStream_t s) {
+hipError_t launch_split_t(const DecodeParams& p, bool fp8, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, (D == 256 ? 1 : kMfmaBatch)>),
-                       dim3(p.n_groups), dim3(p.hw * 64), 0, s, p);
+    if (fp8)
+      hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, (D == 256 ? 1 : kMfmaBatch), true>),
+                         dim3(p.n_groups), dim3(p.hw * 64), 0, s, p);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, (D == 256 ? 1 : kMfmaBatch), false>),
+                         dim3(p.n_groups), dim3(p.hw * 64), 0, s, p);
   } else {
     hipLaunchKernelGGL((decode_split_kernel<T, D, G, kBatch>), dim3(p.n_splits, p.Hkv, p.B),
                        dim3(kNW * 64), 0, s, p);
@@ -709,23 +753,23 @@ hipError_t launch_split_t(const DecodeParams& p, hipStream_t s) {
 }
 
 template <typename T, int D>
-hipError_t launch_split_g(const DecodeParams& p, int G, hipStream_t s) {
+hipError_t launch_split_g(const DecodeParams& p, int G, bool fp8, hipStream_t s) {
   switch (G) {
-    case 1: return launch_split_t<T, D, 1>(p, s);
-    case 2: return launch_split_t<T, D, 2>(p, s);
-    case 4: return launch_split_t<T, D, 4>(p, s);
-    case 8: return launch_split_t<T, D, 8>(p, s);
+    case 1: return launch_split_t<T, D, 1>(p, fp8, s);
+    case 2: return launch_split_t<T, D, 2>(p, fp8, s);
+    case 4: return launch_split_t<T, D, 4>(p, fp8, s);
+    case 8: return launch_split_t<T, D, 8>(p, fp8, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
-hipError_t launch_split_d(const DecodeParams& p, int D, int G, hipStream_t s) {
+hipError_t launch_split_d(const DecodeParams& p, int D, int G, bool fp8, hipStream_t s) {
   switch (D) {
-    case 64: return launch_split_g<T, 64>(p, G, s);
-    case 128: return launch_split_g<T, 128>(p, G, s);
+    case 64: return launch_split_g<T, 64>(p, G, fp8, s);
+    case 128: return launch_split_g<T, 128>(p, G, fp8, s);
     case 256:
-      if constexpr (sizeof(T) == 2) return launch_split_g<T, 256>(p, G, s);
+      if constexpr (sizeof(T) == 2) return launch_split_g<T, 256>(p, G, fp8, s);
       break;
   }
   return hipErrorInvalidValue;
@@ -760,9 +804,11 @@ bool decode_supported(int dtype, int D, int G, int page_size) {
   return d_ok && (G == 1 || G == 2 || G == 4 || G == 8) && page_size == kPage;
 }
 
-hipError_t launch_decode_split(const DecodeParams& p, int dtype, int D, int G, hipStream_t s) {
-  if (dtype == 0) return launch_split_d<float>(p, D, G, s);
-  return dtype == 1 ? launch_split_d<bf16_t>(p, D, G, s) : launch_split_d<f16_t>(p, D, G, s);
+hipError_t launch_decode_split(const DecodeParams& p, int dtype, int D, int G, bool fp8_kv,
+                               hipStream_t s) {
+  if (dtype == 0) return fp8_kv ? hipErrorInvalidValue : launch_split_d<float>(p, D, G, false, s);
+  return dtype == 1 ? launch_split_d<bf16_t>(p, D, G, fp8_kv, s)
+                    : launch_split_d<f16_t>(p, D, G, fp8_kv, s);
 }
 
 hipError_t launch_decode_combine(const DecodeParams& p, int dtype, int D, int G, hipStream_t s) {

@@ -30,7 +30,8 @@ struct DecodeParams {
   //   spans at most max_segs runs;
   //   part_o [B, Hkv, max_segs, G, D], part_lse [B, Hkv, max_segs, G].
   int hw, nhg, n_groups, min_run, max_segs;
-  float scale_log2;        // softmax scale * log2(e)
+  float scale_log2;        // softmax scale * log2(e) (E4M3 cache: times the key scale)
+  float v_scale;           // E4M3 cache only: scale of the values
 };
 
 struct PrefillParams {
@@ -63,7 +64,9 @@ struct PrefillParams {
 
 // dtype: 0 = f32, 1 = bf16, 2 = f16 (values of attn_dtype).
 bool decode_supported(int dtype, int D, int G, int page_size);
-hipError_t launch_decode_split(const DecodeParams& p, int dtype, int D, int G, hipStream_t s);
+// fp8_kv: K/V pages are E4M3 bytes (16-bit dtype only).
+hipError_t launch_decode_split(const DecodeParams& p, int dtype, int D, int G, bool fp8_kv,
+                               hipStream_t s);
 hipError_t launch_decode_combine(const DecodeParams& p, int dtype, int D, int G, hipStream_t s);
 // Workgroups (of up to 8 waves, one per KV head) per CU in the balanced bf16 grid.
 #ifndef ATTN_DECODE_GROUPS_PER_CU

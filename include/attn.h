@@ -126,6 +126,34 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pag
                               void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Batched decode over a paged KV cache stored as 8-bit floats E4M3 (FP8 of
+ * "FlashInfer内核库深度解析", precision support), one scale per tensor:
+ * token t's key is k_scale * E4M3(k byte), its value v_scale * E4M3(v byte).
+ * The key scale is folded into the softmax exponent's scale and the value
+ * scale into the output normalisation ("FlashAttention-3 ..." section 一), so
+ * the result equals attn_decode_paged on the dequantised cache up to
+ * rounding, while half the K/V bytes are read.
+ *
+ *  dtype       type of q and out: ATTN_BF16 or ATTN_F16 (ATTN_F32 ->
+ *              ATTN_E_UNSUPPORTED); the E4M3 bytes are converted to it
+ *              exactly before the matrix-core products
+ *  k_pages, v_pages  [num_pages, page_size, Hkv, D] uint8 (E4M3 bytes;
+ *              0x7F / 0xFF are NaN)
+ *  k_scale, v_scale  finite floats (else ATTN_E_VALUE)
+ *  workspace   attn_decode_paged_workspace_size(dtype, ...) bytes, as for
+ *              attn_decode_paged with the same dtype
+ * Everything else, the supported shapes and the NaN rules are those of
+ * attn_decode_paged with a 16-bit dtype.
+ */
+attn_status attn_decode_paged_fp8(attn_dtype dtype, const void* q, const void* k_pages,
+                                  const void* v_pages, const int32_t* page_table,
+                                  const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                                  int page_size, int num_pages, int max_pages_per_req,
+                                  int max_kv_len, int split_pages, float scale, float k_scale,
+                                  float v_scale, void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Ragged prefill addressed by cu_seqlens ("FlashAttention-3 ..." section 二:
  * packed [total_tokens, heads, head_dim] tensors, prefix offsets of length
  * batch+1, max_seqlen_q / max_seqlen_k, softmax_scale and causal).

@@ -104,6 +104,28 @@ def test_workspace_size(lib):
             lib.attn_decode_paged_workspace_size(1, 4, 8, 2, 128, 16, 160, 2))
 
 
+def test_decode_fp8_rejects(lib):
+    def call(**kw):
+        a = dict(dtype=1, q=16, k=16, v=16, t=16, lens=16, B=2, Hq=8, Hkv=2, D=128, P=16,
+                 num_pages=10, max_pages=4, mkv=64, split=0, scale=0.1, ks=1.0, vs=1.0, out=16,
+                 lse=16, ws=256, ws_bytes=1 << 20)
+        a.update(kw)
+        return lib.attn_decode_paged_fp8(a["dtype"], a["q"], a["k"], a["v"], a["t"], a["lens"],
+                                         a["B"], a["Hq"], a["Hkv"], a["D"], a["P"], a["num_pages"],
+                                         a["max_pages"], a["mkv"], a["split"], a["scale"], a["ks"],
+                                         a["vs"], a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+    assert call(dtype=0) == E_UNSUP                     # fp32 queries with an E4M3 cache
+    assert call(dtype=3) == E_DTYPE
+    assert call(ks=float("inf")) == E_VALUE
+    assert call(vs=float("nan")) == E_VALUE
+    assert call(D=96) == E_UNSUP
+    assert call(P=8, mkv=32) == E_UNSUP
+    assert call(Hq=8, Hkv=3) == E_SHAPE
+    assert call(ws=None) == E_WS
+    assert call(t=None) == E_NULL
+    assert call(B=0, q=None) == OK
+
+
 def _prefill(lib, **kw):
     a = dict(dtype=1, q=16, k=16, v=16, cq=16, ck=16, B=2, Hq=8, Hkv=2, D=128, Tq=100, Tk=100,
              mq=64, mk=64, causal=1, scale=0.1, out=16, lse=16, stream=None)
