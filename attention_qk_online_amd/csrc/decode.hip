@@ -36,6 +36,10 @@ constexpr int kBatch = ATTN_DECODE_BATCH;  // pages whose loads are issued toget
 #define ATTN_DECODE_MFMA_BATCH 1
 #endif
 constexpr int kMfmaBatch = ATTN_DECODE_MFMA_BATCH;
+#ifndef ATTN_DECODE_FP8_BATCH
+#define ATTN_DECODE_FP8_BATCH 1
+#endif
+constexpr int kFp8Batch = ATTN_DECODE_FP8_BATCH;  // pages per batch with an E4M3 cache
 
 template <typename T, int D>
 struct Slice {
@@ -563,14 +567,35 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
           o[db] = H::mfma16x16x16(__builtin_bit_cast(typename H::v4, a), pb, o[db]);
         }
       };
-      Page bufs[NB];
       const int last = nc - 1;
-      for (int i = 0; i < nc; i += NB) {
+      if constexpr (F8) {
+        // Software pipeline (an E4M3 page is half the bytes, so one page in
+        // flight per wave leaves HBM idle): the loads of the next NB pages
+        // are in flight while a page is folded.  Past the last page the
+        // fetch repeats it (an L2 hit), so the count of loads in flight is
+        // the same on every path.
+        constexpr int DEP = NB + 1;
+        Page ring[DEP];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) fetch(min(i + j, last), bufs[j]);
+        for (int j = 0; j < DEP - 1; ++j) fetch(min(j, last), ring[j]);
+        for (int i = 0; i < nc; i += DEP) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
-          if (j == 0 || i + j < nc) fold(i + j, bufs[j]);
+          for (int j = 0; j < DEP; ++j) {
+            if (j == 0 || i + j < nc) {
+              fetch(min(i + j + DEP - 1, last), ring[(j + DEP - 1) % DEP]);
+              fold(i + j, ring[j]);
+            }
+          }
+        }
+      } else {
+        Page bufs[NB];
+        for (int i = 0; i < nc; i += NB) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) fetch(min(i + j, last), bufs[j]);
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            if (j == 0 || i + j < nc) fold(i + j, bufs[j]);
+        }
       }
     }
 
@@ -740,7 +765,7 @@ template <typename T, int D, int G>
 hipError_t launch_split_t(const DecodeParams& p, bool fp8, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     if (fp8)
-      hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, (D == 256 ? 1 : kMfmaBatch), true>),
+      hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, (D == 256 ? 1 : kFp8Batch), true>),
                          dim3(p.n_groups), dim3(p.hw * 64), 0, s, p);
     else
       hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, (D == 256 ? 1 : kMfmaBatch), false>),

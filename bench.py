@@ -19,14 +19,15 @@ in HBM but not in the MALL or the L2s.  Call times come from one event
 pair per segment of the timed steps (mean, median and minimum); per-kernel
 durations (the roofline figures) from a second pass in which the library
 records HIP events around each of its launches on the launch stream.  Also
-reported: the chunked workload through the shared-prefix cascade, the
-launch-bound fp32 single-sequence decode and the 1K-32K single-sequence
+reported: the decode workload over an E4M3 (fp8) copy of its cache, the
+chunked workload through the shared-prefix cascade, the launch-bound fp32
+single-sequence decode and the 1K-32K single-sequence
 causal prefill sweep.  The CPU oracle is timed on the host
 cores over the whole decode workload (repeated to at least ~10 s), as a
 reported baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-flush]
-                       [--no-cpu-baseline] [--calibrate-copy MIB]
+                       [--no-cpu-baseline] [--no-cascade] [--no-fp8] [--calibrate-copy MIB]
 Prints one JSON line.
 """
 import argparse
@@ -57,6 +58,10 @@ def main():
     ap.add_argument("--no-flush", action="store_true",
                     help="do not read a 1 GiB scratch buffer before each timed segment")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cascade", action="store_true",
+                    help="skip the shared-prefix cascade timing (its kernels share a name with "
+                         "the direct paged prefill, so profiles of the latter skip it)")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the E4M3-cache decode timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="finish with three plain device-to-device copies of MIB MiB, the "
@@ -223,43 +228,82 @@ def main():
         },
     }
 
+    # The decode workload over an E4M3 copy of its cache (one scale per K / V
+    # tensor): half the bytes through the same schedule.
+    if not args.no_fp8:
+        f_kp, f_vp, f_ks, f_vs = dec.fp8_pools(dev)
+        f_bytes = dec.fp8_kv_bytes()
+
+        def decode_fp8():
+            A.decode_paged_fp8(d_q, f_kp, f_vp, d_table, d_lens, f_ks, f_vs, scale=dec.scale,
+                               max_kv_len=dec.max_kv_len, out=d_out, lse=d_lse, workspace=d_ws)
+        for _ in range(3):
+            decode_fp8()
+        torch.cuda.synchronize()
+        for i in range(K):
+            flush()
+            ev[i][0].record(stream)
+            decode_fp8()
+            ev_end[i][0].record(stream)
+        torch.cuda.synchronize()
+        f_ms = sorted(ev[i][0].elapsed_time(ev_end[i][0]) for i in range(K))
+        A.timing_begin(2 * K + 4)
+        for i in range(K):
+            flush()
+            decode_fp8()
+        kf = A.timing_end()
+        f_mean = sum(f_ms) / K
+        f_split = kf["decode_split"][0] / kf["decode_split"][1]
+        res["decode_fp8"] = {
+            "metric": "decode KV GB/s over an E4M3 cache", "unit": "GB/s",
+            "value": round(f_bytes / (f_mean * 1e-3) / 1e9, 1), "kv_bytes": f_bytes,
+            "call_ms": round(f_mean, 5), "call_ms_stats": stats(f_ms),
+            "split_kernel_ms": round(f_split, 5),
+            "combine_kernel_ms": round(kf["decode_combine"][0] / kf["decode_combine"][1], 5),
+            "speedup_vs_bf16_call": round(ms_decode / f_mean, 4),
+            "roofline": roofline_hbm(f_bytes, f_split, "decode_fp8")}
+        log("bench: fp8 decode", res["decode_fp8"])
+        del f_kp, f_vp
+
     # The chunked workload again through the shared-prefix cascade: one pass
     # of every query row over the 4096 shared tokens, then each request over
     # its own keys with the merge fused into the store.  Same flops as the
     # direct call (the work is split, not skipped).
-    prefix_len = pg.shared_pages * pg.page_size
-    c_ws = torch.empty(A.prefill_paged_cascade_workspace_size(pg.dtype, g_q.shape[0], pg.Hq, pg.D),
-                       dtype=torch.uint8, device=dev)
+    if not args.no_cascade:
+        prefix_len = pg.shared_pages * pg.page_size
+        c_ws = torch.empty(A.prefill_paged_cascade_workspace_size(pg.dtype, g_q.shape[0], pg.Hq,
+                                                                  pg.D),
+                           dtype=torch.uint8, device=dev)
 
-    def cascade():
-        A.prefill_paged_cascade(g_q, g_cq, g_kp, g_vp, g_table, g_lens, pg.max_seqlen_q,
-                                pg.max_kv_len, prefix_len, causal=True, scale=pg.scale, out=g_out,
-                                lse=g_lse, workspace=c_ws)
-    for _ in range(2):
-        cascade()
-    torch.cuda.synchronize()
-    c_ms = []
-    for i in range(K):
-        flush()
-        ev[i][0].record(stream)
-        cascade()
-        ev_end[i][0].record(stream)
-    torch.cuda.synchronize()
-    c_ms = sorted(ev[i][0].elapsed_time(ev_end[i][0]) for i in range(K))
-    A.timing_begin(2 * K + 4)
-    for i in range(K):
-        flush()
-        cascade()
-    kc = A.timing_end()
-    c_mean = sum(c_ms) / K
-    res["prefill_paged"]["cascade"] = {
-        "shared_prefix_len": prefix_len,
-        "value": round(pg_flops / (c_mean * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-        "call_ms": round(c_mean, 4), "call_ms_stats": stats(c_ms),
-        "prefix_kernel_ms": round(kc["cascade_prefix"][0] / kc["cascade_prefix"][1], 4),
-        "suffix_kernel_ms": round(kc["cascade_suffix"][0] / kc["cascade_suffix"][1], 4),
-        "speedup_vs_direct": round(ms_paged / c_mean, 4)}
-    log("bench: cascade", res["prefill_paged"]["cascade"])
+        def cascade():
+            A.prefill_paged_cascade(g_q, g_cq, g_kp, g_vp, g_table, g_lens, pg.max_seqlen_q,
+                                    pg.max_kv_len, prefix_len, causal=True, scale=pg.scale,
+                                    out=g_out, lse=g_lse, workspace=c_ws)
+        for _ in range(2):
+            cascade()
+        torch.cuda.synchronize()
+        for i in range(K):
+            flush()
+            ev[i][0].record(stream)
+            cascade()
+            ev_end[i][0].record(stream)
+        torch.cuda.synchronize()
+        c_ms = sorted(ev[i][0].elapsed_time(ev_end[i][0]) for i in range(K))
+        A.timing_begin(2 * K + 4)
+        for i in range(K):
+            flush()
+            cascade()
+        kc = A.timing_end()
+        c_mean = sum(c_ms) / K
+        res["prefill_paged"]["cascade"] = {
+            "shared_prefix_len": prefix_len,
+            "value": round(pg_flops / (c_mean * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "call_ms": round(c_mean, 4), "call_ms_stats": stats(c_ms),
+            "prefix_kernel_ms": round(kc["cascade_prefix"][0] / kc["cascade_prefix"][1], 4),
+            "suffix_kernel_ms": round(kc["cascade_suffix"][0] / kc["cascade_suffix"][1], 4),
+            "speedup_vs_direct": round(ms_paged / c_mean, 4)}
+        log("bench: cascade", res["prefill_paged"]["cascade"])
+        del c_ws
 
     # Single-sequence fp32 decode (1 query token, 4 heads, head_dim 64, 256
     # contiguous keys as an identity-paged NHD view): launch-latency bound.
@@ -364,11 +408,13 @@ def main():
 # measured on; it is reported only while those sources are unchanged.
 TRAFFIC_FILES = {
     "decode_split": "profiles/traffic__decode_split__paged_decode_b64_hq32_hkv8_d128.md",
+    "decode_fp8": "profiles/traffic__decode_split_fp8__paged_decode_e4m3_b64_hq32_hkv8_d128.md",
     "prefill": "profiles/traffic__prefill__ragged_causal_b8_hq64_hkv8_d128.md",
     "prefill_paged": "profiles/traffic__prefill_paged__chunked_b16_q512_kv8704_h16_d256.md",
 }
 KERNEL_SOURCES = {
     "decode_split": ["decode.hip"],
+    "decode_fp8": ["decode.hip"],
     "prefill": ["prefill.hip"],
     "prefill_paged": ["prefill.hip"],
 }
