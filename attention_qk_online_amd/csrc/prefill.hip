@@ -1,14 +1,14 @@
-// Ragged causal prefill for gfx950 on bf16 / fp16 MFMA with fp32 accumulation.
+// Ragged causal prefill for gfx950 on bf16 / fp16 MFMA with fp32 accumulation,
+// head_dim 128 (head_dim 256: prefill16.hip).
 //
 // One workgroup = one (query tile of BM = 128 rows, query head) of one
-// sequence; four waves own 32 query rows each.  Key tiles have BN keys (64
-// for head_dim 128, 32 for head_dim 256).  Head_dim 128 runs two workgroups
-// per CU, so one wave's matrix work overlaps another's vector work; head_dim
-// 256 needs the whole register file and runs one.
+// sequence; four waves own 32 query rows each.  Key tiles have BN = 64 keys.
+// Two workgroups run per CU, so one wave's matrix work overlaps another's
+// vector work.
 //
 // Data movement: K and V tiles go from HBM straight into LDS with
-// buffer_load_dwordx4 ... lds (no register staging), into rings of R slots
-// (2 for head_dim 128, 4 for head_dim 256): while tile j is processed, the
+// buffer_load_dwordx4 ... lds (no register staging), into rings of R = 2
+// slots: while tile j is processed, the
 // DMA for K(j+R) and V(j+R-1) is in flight; one wait and one barrier per
 // tile.  Each lane loads the 16-byte chunk that belongs at its LDS position
 // under an XOR swizzle (K: chunk XOR row mod 16; V: 64-byte block XOR row mod
@@ -35,8 +35,8 @@
 // 推理中的集成实践" (section 一: Q/K/V blocks in on-chip memory, online softmax
 // accumulated in place, asynchronous global-to-shared copies overlapped with
 // tensor-core work by double buffering; section 二: varlen packing by
-// cu_seqlens, causal, paged blocks; section 四: keep the rescaling, and keep
-// tiles within the on-chip budget for head_dim 256) and the three-stage QK^T /
+// cu_seqlens, causal, paged blocks; section 四: keep the rescaling) and the
+// three-stage QK^T /
 // softmax / PV pipeline of "FlashInfer Attention Kernel技术解析" section 1.3
 // (bank-conflict avoidance: section 4), re-tiled for 64-wide waves, 32x32
 // MFMA tiles and a 160 KiB LDS.
@@ -56,7 +56,8 @@ constexpr int kBufferWord3 = 0x00020000;   // buffer descriptor word 3 for gfx95
 
 template <int D>
 struct Cfg {
-  static constexpr int BN = D == 128 ? 64 : 32;      // keys per tile
+  static_assert(D == 128, "head_dim 256 has its own kernel");
+  static constexpr int BN = 64;                       // keys per tile
   static constexpr int ROWB = D * 2;                  // bytes of one K/V row
   static constexpr int TILEB = BN * ROWB;             // bytes of one K or V tile
   static constexpr int CH = D / 8;                    // 16-byte chunks per row
@@ -66,15 +67,12 @@ struct Cfg {
   static constexpr int DB = D / 32;                   // 32-row blocks of D in O^T
   static constexpr int KB = BN / 32;                  // 32-key blocks per tile
   static constexpr int PS = BN / 16;                  // 16-key k-steps of P.V
-  static constexpr int VALU_PER_QK = D == 128 ? 6 : 3;  // vector work issued per S^T MFMA
-  // Ring slots per operand: two for head_dim 128 (two workgroups share a CU),
-  // four for head_dim 256 (one workgroup per CU; tiles arrive three steps early).
-  static constexpr int R = D == 128 ? 2 : 4;
+  static constexpr int VALU_PER_QK = 6;               // vector work issued per S^T MFMA
+  static constexpr int R = 2;                         // ring slots per operand
   static constexpr int LDSB = 2 * R * TILEB;
   static_assert(TILEB % (1024 * NWAVE) == 0, "tile split into 1 KiB DMA instructions");
   static_assert(WROWS <= kPage && kPage % WROWS == 0, "a wave's rows stay inside one page");
-  static_assert(D != 128 || LDSB <= 80 * 1024, "two workgroups per CU");
-  static_assert(LDSB <= 160 * 1024, "LDS per CU");
+  static_assert(LDSB <= 80 * 1024, "two workgroups per CU");
 };
 
 
@@ -98,7 +96,7 @@ constexpr int kWaitLgkm0 = 0xc07f;
 // The page table comes as its own restrict-qualified argument so that its
 // wave-uniform reads compile to scalar loads.
 template <typename E, int D, bool PAGED>
-__global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
+__global__ __launch_bounds__(NT, 2) void prefill_kernel(
     PrefillParams p, const int32_t* __restrict__ page_table) {
   using C = Cfg<D>;
   using H = Half16<E>;            // bf16 or fp16 inputs
@@ -108,28 +106,18 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
   auto mfma32 = [](v8 a, v8 b, f32x16 c) { return H::mfma32x32x16(a, b, c); };
   // One array per ring slot (not one array): the compiler can then tell that a
   // DMA into one slot does not alias operand reads from another, and does not
-  // stall those reads on the DMA's completion.  Slots past R are unused.
+  // stall those reads on the DMA's completion.
   __shared__ __attribute__((aligned(1024))) char k_ring0[C::TILEB];
   __shared__ __attribute__((aligned(1024))) char k_ring1[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) char k_ring2[C::R > 2 ? C::TILEB : 1];
-  __shared__ __attribute__((aligned(1024))) char k_ring3[C::R > 3 ? C::TILEB : 1];
   __shared__ __attribute__((aligned(1024))) char v_ring0[C::TILEB];
   __shared__ __attribute__((aligned(1024))) char v_ring1[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) char v_ring2[C::R > 2 ? C::TILEB : 1];
-  __shared__ __attribute__((aligned(1024))) char v_ring3[C::R > 3 ? C::TILEB : 1];
   auto kslot = [&](auto i) -> char* {
-    constexpr int S = decltype(i)::value % C::R;
-    if constexpr (S == 0) return k_ring0;
-    else if constexpr (S == 1) return k_ring1;
-    else if constexpr (S == 2) return k_ring2;
-    else return k_ring3;
+    if constexpr (decltype(i)::value % C::R == 0) return k_ring0;
+    else return k_ring1;
   };
   auto vslot = [&](auto i) -> char* {
-    constexpr int S = decltype(i)::value % C::R;
-    if constexpr (S == 0) return v_ring0;
-    else if constexpr (S == 1) return v_ring1;
-    else if constexpr (S == 2) return v_ring2;
-    else return v_ring3;
+    if constexpr (decltype(i)::value % C::R == 0) return v_ring0;
+    else return v_ring1;
   };
 
   const int tid = threadIdx.x;
@@ -401,69 +389,6 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
     }
   };
 
-  // Steady-state body written in issue order: the S^T(kt+1) MFMAs, each with
-  // the next K fragment read PF ahead and a share of tile kt's exponentials,
-  // then the O^T MFMAs with V^T fragments read PF ahead.  Used for head_dim
-  // 256, whose one wave per SIMD leaves the compiler no room to reorder.
-  auto fused = [&](const char* kbuf, const char* vbuf, f32x16 (&scur)[C::KB],
-                   f32x16 (&snext)[C::KB], v8 (&pb)[C::PS]) {
-    constexpr int NQ = C::KB * C::QK;       // S^T MFMAs
-    constexpr int NE = C::KB * 16;          // weights per lane
-    constexpr int EPM = NE / NQ;            // weights per S^T MFMA
-    constexpr int PF = 2;                   // fragments in flight (measured best)
-    const float nm = -m;
-    const v2 one = {(elem)1.f, (elem)1.f};
-    auto kfrag = [&](int i) {
-      const int kb = i / C::QK, ks = i % C::QK;
-      return *reinterpret_cast<const v8*>(kbuf + kb * 32 * C::ROWB + (ks >> 3) * 256 + kro[ks & 7]);
-    };
-    v8 kf[PF];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) kf[i] = kfrag(i);
-    f32x16 acc[C::KB];
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) acc[kb] = f32x16{};
-    float psum = 0.f;
-    v8 w;
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int kb = i / C::QK, ks = i % C::QK;
-      acc[kb] = mfma32(kf[i % PF], qf[ks], acc[kb]);
-      if (i + PF < NQ) kf[i % PF] = kfrag(i + PF);
-#pragma unroll
-      for (int e = 0; e < EPM; ++e) {
-        const int idx = i * EPM + e;
-        w[idx % 8] = (elem)exp2_fast(__builtin_fmaf(scur[idx / 16][idx % 16], c, nm));
-        if (idx % 8 == 7) {
-#pragma unroll
-          for (int t = 0; t < 8; t += 2)
-            psum = H::dot2(v2{w[t], w[t + 1]}, one, psum);
-          pb[idx / 8] = w;
-        }
-      }
-    }
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) snext[kb] = acc[kb];
-    lsum += psum;
-    constexpr int NP = C::DB * C::PS;       // O^T MFMAs
-    auto vfrag = [&](int j) {
-      const int db = j / C::PS, ps = j % C::PS;
-      const int ro = ps * 16 * C::ROWB + (db >> 2) * 256 + vro[db & 3];
-      v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_char*)vbuf + ro));
-      v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_char*)vbuf + ro + 8 * C::ROWB));
-      return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    v8 vf[PF];
-#pragma unroll
-    for (int j = 0; j < PF; ++j) vf[j] = vfrag(j);
-#pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      const int db = j / C::PS, ps = j % C::PS;
-      o[db] = mfma32(vf[j % PF], pb[ps], o[db]);
-      if (j + PF < NP) vf[j % PF] = vfrag(j + PF);
-    }
-  };
-
   // One tile step.  SLOT = kt % R picks the ring slots at compile time: K(kt+1)
   // is in slot kt+1, V(kt) in slot kt; this step starts the DMA of V(kt+R-1)
   // into slot kt-1 and of K(kt+R) into slot kt, both last read in the step
@@ -482,10 +407,7 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
     if (kt + C::R - 1 < n_kt) dma(kt + C::R - 1, VDST, true, pid_v);
     if (kt + C::R < n_kt) dma(kt + C::R, KDST, false, pid_k);
     v8 pb[C::PS];
-    if constexpr (FAST && D == 256) {
-      update_max(scur);
-      fused(KNXT, VCUR, scur, snext, pb);
-    } else if constexpr (FAST) {
+    if constexpr (FAST) {
       // One block in which the S^T(kt+1) MFMAs hide the exponentials of tile kt.
       update_max(scur);
       qk(KNXT, snext);
@@ -524,12 +446,8 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
       pid_v = pid_k;
       if (kt + C::R + 1 < n_kt) pid_k = load_pid(kt + C::R + 1);
     }
-    // Next step reads K(kt+2) and V(kt+1), issued R-2 steps before this one;
-    // the DMAs of the R-2 steps since (two tiles each) may stay in flight.
-    if (C::R > 2 && kt + C::R < n_kt)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::R - 2) * 2 * C::DMA));
-    else
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    // The next step reads K(kt+2) and V(kt+1), whose DMAs this step issued.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wave's LDS reads (and page ids) are done
     // Every wave's DMA for the next step has landed and every read of the
     // slots refilled next has completed.  (A workgroup fence here would also
@@ -555,8 +473,8 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
   for (int t = 0; t < C::R; ++t) {
     if (t < n_kt) {
       const int pid = load_pid(t);
-      char* kd = t == 0 ? kslot(Idx<0>{}) : t == 1 ? kslot(Idx<1>{}) : t == 2 ? kslot(Idx<2>{}) : kslot(Idx<3>{});
-      char* vd = t == 0 ? vslot(Idx<0>{}) : t == 1 ? vslot(Idx<1>{}) : t == 2 ? vslot(Idx<2>{}) : vslot(Idx<3>{});
+      char* kd = t == 0 ? kslot(Idx<0>{}) : kslot(Idx<1>{});
+      char* vd = t == 0 ? vslot(Idx<0>{}) : vslot(Idx<1>{});
       dma(t, kd, false, pid);
       if (t + 1 < C::R) dma(t, vd, true, pid);
       else pid_v = pid;
@@ -571,18 +489,10 @@ __global__ __launch_bounds__(NT, D == 128 ? 2 : 1) void prefill_kernel(
   for (; kt < n_fast; kt += C::R) {
     step(Idx<0>{}, Idx<1>{}, kt, sa, sb);
     step(Idx<1>{}, Idx<1>{}, kt + 1, sb, sa);
-    if constexpr (C::R == 4) {
-      step(Idx<2>{}, Idx<1>{}, kt + 2, sa, sb);
-      step(Idx<3>{}, Idx<1>{}, kt + 3, sb, sa);
-    }
   }
   for (; kt < n_kt; kt += C::R) {
     step(Idx<0>{}, Idx<0>{}, kt, sa, sb);
     if (kt + 1 < n_kt) step(Idx<1>{}, Idx<0>{}, kt + 1, sb, sa);
-    if constexpr (C::R == 4) {
-      if (kt + 2 < n_kt) step(Idx<2>{}, Idx<0>{}, kt + 2, sa, sb);
-      if (kt + 3 < n_kt) step(Idx<3>{}, Idx<0>{}, kt + 3, sb, sa);
-    }
   }
 
   const bool any_bad = __syncthreads_or(bad);
@@ -664,15 +574,15 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t s) {
 bool prefill_supported(int dtype, int D) { return (dtype == 1 || dtype == 2) && (D == 128 || D == 256); }
 
 template <typename E>
-hipError_t launch_e(const PrefillParams& p, int D, bool paged, hipStream_t s) {
-  if (D == 128) return paged ? launch_t<E, 128, true>(p, s) : launch_t<E, 128, false>(p, s);
-  if (D == 256) return paged ? launch_t<E, 256, true>(p, s) : launch_t<E, 256, false>(p, s);
-  return hipErrorInvalidValue;
+hipError_t launch_e(const PrefillParams& p, bool paged, hipStream_t s) {
+  return paged ? launch_t<E, 128, true>(p, s) : launch_t<E, 128, false>(p, s);
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, bool paged, hipStream_t s) {
-  if (dtype == 1) return launch_e<bf16_t>(p, D, paged, s);
-  if (dtype == 2) return launch_e<f16_t>(p, D, paged, s);
+  if (D == 256) return launch_prefill_d256(p, dtype, paged, s);
+  if (D != 128) return hipErrorInvalidValue;
+  if (dtype == 1) return launch_e<bf16_t>(p, paged, s);
+  if (dtype == 2) return launch_e<f16_t>(p, paged, s);
   return hipErrorInvalidValue;
 }
 
