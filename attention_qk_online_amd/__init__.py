@@ -23,6 +23,10 @@ Entry points (names follow the C ABI):
   "FlashInfer内核库深度解析").
 * :func:`merge_states` -- log-sum-exp merge of two partial attention states.
 
+The paged calls take ``kv_layout="NHD"`` (pools [pages, page_size, Hkv, D])
+or ``"HND"`` ([pages, Hkv, page_size, D]), the two KV-cache layouts of
+"FlashInfer内核库深度解析".
+
 The softmax scale defaults to 1/sqrt(head_dim) (same page, section 二).
 """
 from __future__ import annotations
@@ -95,6 +99,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         c_float, vp, vp, vp, c_size, vp]
     lib.attn_merge_states.restype = c_int
     lib.attn_merge_states.argtypes = [c_int, vp, vp, vp, vp, c_int, c_int, vp, vp, vp]
+    # HND twins: same argument lists
+    for name in ("attn_decode_paged", "attn_decode_paged_fp8", "attn_prefill_paged",
+                 "attn_prefill_paged_cascade"):
+        f, g = getattr(lib, name), getattr(lib, name + "_hnd")
+        g.restype, g.argtypes = c_int, f.argtypes
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [c_int]
     lib.attn_last_error.restype = ctypes.c_char_p
@@ -141,6 +150,24 @@ def _dev(t: torch.Tensor, name: str, dtype=None, dim=None) -> int:
     return t.data_ptr()
 
 
+def _layout(kv_layout: str) -> str:
+    """C-function suffix for a page layout: NHD pools are [pages, page_size,
+    Hkv, D], HND pools [pages, Hkv, page_size, D]."""
+    if kv_layout == "NHD":
+        return ""
+    if kv_layout == "HND":
+        return "_hnd"
+    raise ValueError(f"kv_layout must be 'NHD' or 'HND', got {kv_layout!r}")
+
+
+def _pool_dims(pages: torch.Tensor, kv_layout: str):
+    """(num_pages, page_size, Hkv, D) of a pool in either layout."""
+    if kv_layout == "HND":
+        n, h, ps, d = pages.shape
+        return n, ps, h, d
+    return tuple(pages.shape)
+
+
 def _stream(dev: torch.device) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
@@ -162,8 +189,9 @@ def decode_paged_workspace_size(dtype: torch.dtype, B: int, Hq: int, Hkv: int, D
 
 
 def _decode(q, k_pages, v_pages, page_table, kv_lens, scale, max_kv_len, split_pages, out, lse,
-            workspace, fp8_scales=None):
+            workspace, fp8_scales=None, kv_layout="NHD"):
     lib = load_library()
+    suffix = _layout(kv_layout)
     dt = _dtype_code(q)
     kv_dtype = q.dtype if fp8_scales is None else torch.uint8
     pq = _dev(q, "q", dim=3)
@@ -172,7 +200,7 @@ def _decode(q, k_pages, v_pages, page_table, kv_lens, scale, max_kv_len, split_p
     pt = _dev(page_table, "page_table", torch.int32, 2)
     pl = _dev(kv_lens, "kv_lens", torch.int32, 1)
     B, Hq, D = q.shape
-    num_pages, page_size, Hkv, Dk = k_pages.shape
+    num_pages, page_size, Hkv, Dk = _pool_dims(k_pages, kv_layout)
     if tuple(v_pages.shape) != tuple(k_pages.shape) or Dk != D:
         raise ValueError(f"k_pages {tuple(k_pages.shape)} / v_pages {tuple(v_pages.shape)} do not "
                          f"match q {tuple(q.shape)}")
@@ -199,10 +227,10 @@ def _decode(q, k_pages, v_pages, page_table, kv_lens, scale, max_kv_len, split_p
     tail = (out.data_ptr(), lse.data_ptr(), pw, workspace.numel() * workspace.element_size(),
             _stream(q.device))
     if fp8_scales is None:
-        _check(lib.attn_decode_paged(dt, *args, *tail))
+        _check(getattr(lib, "attn_decode_paged" + suffix)(dt, *args, *tail))
     else:
-        _check(lib.attn_decode_paged_fp8(dt, *args, float(fp8_scales[0]), float(fp8_scales[1]),
-                                         *tail))
+        _check(getattr(lib, "attn_decode_paged_fp8" + suffix)(
+            dt, *args, float(fp8_scales[0]), float(fp8_scales[1]), *tail))
     return out, lse
 
 
@@ -210,16 +238,18 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
                  page_table: torch.Tensor, kv_lens: torch.Tensor, scale: Optional[float] = None,
                  max_kv_len: Optional[int] = None, split_pages: int = 0,
                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                 workspace: Optional[torch.Tensor] = None,
+                 kv_layout: str = "NHD") -> Tuple[torch.Tensor, torch.Tensor]:
     """Batched decode over a paged KV cache.
 
-    q [B, Hq, D]; k_pages, v_pages [num_pages, page_size, Hkv, D] (NHD);
-    page_table [B, max_pages] int32; kv_lens [B] int32.  ``max_kv_len`` is a
-    host bound on every kv_len; when omitted it is read from ``kv_lens`` with
-    one device-to-host copy.  Returns (out [B, Hq, D], lse [B, Hq] float32).
+    q [B, Hq, D]; k_pages, v_pages [num_pages, page_size, Hkv, D] (NHD) or
+    [num_pages, Hkv, page_size, D] (``kv_layout="HND"``); page_table
+    [B, max_pages] int32; kv_lens [B] int32.  ``max_kv_len`` is a host bound
+    on every kv_len; when omitted it is read from ``kv_lens`` with one
+    device-to-host copy.  Returns (out [B, Hq, D], lse [B, Hq] float32).
     """
     return _decode(q, k_pages, v_pages, page_table, kv_lens, scale, max_kv_len, split_pages, out,
-                   lse, workspace)
+                   lse, workspace, kv_layout=kv_layout)
 
 
 def decode_paged_fp8(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
@@ -227,12 +257,13 @@ def decode_paged_fp8(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tens
                      v_scale: float, scale: Optional[float] = None,
                      max_kv_len: Optional[int] = None, split_pages: int = 0,
                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                     workspace: Optional[torch.Tensor] = None,
+                     kv_layout: str = "NHD") -> Tuple[torch.Tensor, torch.Tensor]:
     """:func:`decode_paged` over a cache of E4M3 bytes (uint8 pools): token t's
     key is ``k_scale * E4M3(k_pages[...])`` and its value ``v_scale * E4M3(...)``.
     q and out are bf16 or fp16."""
     return _decode(q, k_pages, v_pages, page_table, kv_lens, scale, max_kv_len, split_pages, out,
-                   lse, workspace, fp8_scales=(k_scale, v_scale))
+                   lse, workspace, fp8_scales=(k_scale, v_scale), kv_layout=kv_layout)
 
 
 def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
@@ -277,10 +308,13 @@ def prefill_paged(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_pages: torch.Te
                   v_pages: torch.Tensor, page_table: torch.Tensor, kv_lens: torch.Tensor,
                   max_seqlen_q: int, max_kv_len: int, causal: bool = True,
                   scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                  lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                  lse: Optional[torch.Tensor] = None,
+                  kv_layout: str = "NHD") -> Tuple[torch.Tensor, torch.Tensor]:
     """Chunked prefill over a paged KV cache: request b's queries are the last
-    Lq_b of its kv_lens[b] cached tokens.  Returns (out, lse)."""
+    Lq_b of its kv_lens[b] cached tokens.  Pools are NHD or, with
+    ``kv_layout="HND"``, [num_pages, Hkv, page_size, D].  Returns (out, lse)."""
     lib = load_library()
+    suffix = _layout(kv_layout)
     dt = _dtype_code(q)
     pq = _dev(q, "q", dim=3)
     pcq = _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
@@ -289,7 +323,7 @@ def prefill_paged(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_pages: torch.Te
     pt = _dev(page_table, "page_table", torch.int32, 2)
     pl = _dev(kv_lens, "kv_lens", torch.int32, 1)
     Tq, Hq, D = q.shape
-    num_pages, page_size, Hkv, Dk = k_pages.shape
+    num_pages, page_size, Hkv, Dk = _pool_dims(k_pages, kv_layout)
     if tuple(v_pages.shape) != tuple(k_pages.shape) or Dk != D:
         raise ValueError("k_pages / v_pages do not match q")
     B = cu_seqlens_q.shape[0] - 1
@@ -304,7 +338,8 @@ def prefill_paged(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_pages: torch.Te
     _dev(lse, "lse", torch.float32, 2)
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (Tq, Hq):
         raise ValueError("out/lse have the wrong shape")
-    _check(lib.attn_prefill_paged(dt, pq, pcq, pk, pv, pt, pl, B, Hq, Hkv, D, Tq, page_size,
+    _check(getattr(lib, "attn_prefill_paged" + suffix)(
+        dt, pq, pcq, pk, pv, pt, pl, B, Hq, Hkv, D, Tq, page_size,
                                   num_pages, page_table.shape[1], int(max_seqlen_q),
                                   int(max_kv_len), int(bool(causal)), s, out.data_ptr(),
                                   lse.data_ptr(), _stream(q.device)))
@@ -324,13 +359,14 @@ def prefill_paged_cascade(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_pages: 
                           max_seqlen_q: int, max_kv_len: int, shared_prefix_len: int,
                           causal: bool = True, scale: Optional[float] = None,
                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                          workspace: Optional[torch.Tensor] = None
+                          workspace: Optional[torch.Tensor] = None, kv_layout: str = "NHD"
                           ) -> Tuple[torch.Tensor, torch.Tensor]:
     """:func:`prefill_paged` for a batch whose page-table rows all begin with the
     same ``shared_prefix_len / page_size`` pages: the prefix is attended once
     for every query row, then merged into each request's pass over its own
     keys.  ``workspace`` (uint8, on the device) is allocated when not given."""
     lib = load_library()
+    suffix = _layout(kv_layout)
     dt = _dtype_code(q)
     pq = _dev(q, "q", dim=3)
     pcq = _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
@@ -339,7 +375,7 @@ def prefill_paged_cascade(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_pages: 
     pt = _dev(page_table, "page_table", torch.int32, 2)
     pl = _dev(kv_lens, "kv_lens", torch.int32, 1)
     Tq, Hq, D = q.shape
-    num_pages, page_size, Hkv, Dk = k_pages.shape
+    num_pages, page_size, Hkv, Dk = _pool_dims(k_pages, kv_layout)
     if tuple(v_pages.shape) != tuple(k_pages.shape) or Dk != D:
         raise ValueError("k_pages / v_pages do not match q")
     B = cu_seqlens_q.shape[0] - 1
@@ -358,7 +394,8 @@ def prefill_paged_cascade(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_pages: 
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     pw = _dev(workspace, "workspace", torch.uint8, 1)
-    _check(lib.attn_prefill_paged_cascade(dt, pq, pcq, pk, pv, pt, pl, B, Hq, Hkv, D, Tq,
+    _check(getattr(lib, "attn_prefill_paged_cascade" + suffix)(
+        dt, pq, pcq, pk, pv, pt, pl, B, Hq, Hkv, D, Tq,
                                           page_size, num_pages, page_table.shape[1],
                                           int(max_seqlen_q), int(max_kv_len),
                                           int(shared_prefix_len), int(bool(causal)), s,

@@ -173,7 +173,8 @@ size_t attn_decode_paged_workspace_size(attn_dtype dtype, int B, int Hq, int Hkv
 
 // Both decode entry points; fp8_kv: the pages hold E4M3 bytes with scales
 // k_scale / v_scale.
-static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, const void* q, const void* k_pages,
+static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, const void* q,
+                               const void* k_pages,
                                const void* v_pages, const int32_t* page_table,
                                const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
                                int page_size, int num_pages, int max_pages_per_req,
@@ -232,6 +233,7 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, const void* q, con
   p.n_groups = attn::kDecodeGroupsPerCU * device_cus();
   p.scale_log2 = fp8_kv ? scale * k_scale * kLog2e : scale * kLog2e;
   p.v_scale = fp8_kv ? v_scale : 1.f;
+  p.kv_hnd = kv_hnd;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = timed(ATTN_KERNEL_DECODE_SPLIT, s,
@@ -254,7 +256,19 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pag
                               int max_kv_len, int split_pages, float scale, void* out,
                               float* lse, void* workspace, size_t workspace_bytes,
                               void* stream) {
-  return decode_impl(dtype, false, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
+  return decode_impl(dtype, false, 0, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
+                     page_size, num_pages, max_pages_per_req, max_kv_len, split_pages, scale, 1.f,
+                     1.f, out, lse, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_paged_hnd(attn_dtype dtype, const void* q, const void* k_pages,
+                                  const void* v_pages, const int32_t* page_table,
+                                  const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                                  int page_size, int num_pages, int max_pages_per_req,
+                                  int max_kv_len, int split_pages, float scale, void* out,
+                                  float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return decode_impl(dtype, false, 1, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
                      page_size, num_pages, max_pages_per_req, max_kv_len, split_pages, scale, 1.f,
                      1.f, out, lse, workspace, workspace_bytes, stream);
 }
@@ -266,7 +280,19 @@ attn_status attn_decode_paged_fp8(attn_dtype dtype, const void* q, const void* k
                                   int max_kv_len, int split_pages, float scale, float k_scale,
                                   float v_scale, void* out, float* lse, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  return decode_impl(dtype, true, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
+  return decode_impl(dtype, true, 0, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
+                     page_size, num_pages, max_pages_per_req, max_kv_len, split_pages, scale,
+                     k_scale, v_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_paged_fp8_hnd(attn_dtype dtype, const void* q, const void* k_pages,
+                                      const void* v_pages, const int32_t* page_table,
+                                      const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                                      int page_size, int num_pages, int max_pages_per_req,
+                                      int max_kv_len, int split_pages, float scale,
+                                      float k_scale, float v_scale, void* out, float* lse,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(dtype, true, 1, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
                      page_size, num_pages, max_pages_per_req, max_kv_len, split_pages, scale,
                      k_scale, v_scale, out, lse, workspace, workspace_bytes, stream);
 }
@@ -329,7 +355,7 @@ static attn_status paged_prefill_params(attn_dtype dtype, const void* q,
                                         int total_q, int page_size, int num_pages,
                                         int max_pages_per_req, int max_seqlen_q, int max_kv_len,
                                         int causal, float scale, void* out, float* lse,
-                                        attn::PrefillParams& p, bool& empty) {
+                                        int kv_hnd, attn::PrefillParams& p, bool& empty) {
   attn_status st = check_prefill_common(dtype, B, Hq, Hkv, D, total_q, max_seqlen_q, causal, scale);
   if (st != ATTN_OK) return st;
   if (page_size <= 0 || num_pages < 0 || max_pages_per_req < 0 || max_kv_len < 0)
@@ -357,8 +383,32 @@ static attn_status paged_prefill_params(attn_dtype dtype, const void* q,
   p.max_seqlen_q = max_seqlen_q; p.max_seqlen_k = max_kv_len;
   p.num_pages = num_pages; p.max_pages = max_pages_per_req; p.causal = causal;
   p.table_stride = max_pages_per_req; p.kv_offset = 0; p.kv_len_fixed = -1;
+  p.kv_hnd = kv_hnd;
   p.q_tiles = (max_seqlen_q + attn::kPrefillBM - 1) / attn::kPrefillBM;
   p.scale_log2 = scale * kLog2e;
+  return ATTN_OK;
+}
+
+static attn_status prefill_paged_impl(attn_dtype dtype, int kv_hnd, const void* q,
+                                      const int32_t* cu_seqlens_q, const void* k_pages,
+                                      const void* v_pages, const int32_t* page_table,
+                                      const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                                      int total_q, int page_size, int num_pages,
+                                      int max_pages_per_req, int max_seqlen_q, int max_kv_len,
+                                      int causal, float scale, void* out, float* lse,
+                                      void* stream) {
+  g_last_error[0] = 0;
+  attn::PrefillParams p;
+  bool empty = false;
+  attn_status st = paged_prefill_params(dtype, q, cu_seqlens_q, k_pages, v_pages, page_table,
+                                        kv_lens, B, Hq, Hkv, D, total_q, page_size, num_pages,
+                                        max_pages_per_req, max_seqlen_q, max_kv_len, causal, scale,
+                                        out, lse, kv_hnd, p, empty);
+  if (st != ATTN_OK || empty) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e =
+      timed(ATTN_KERNEL_PREFILL_PAGED, s, [&] { return attn::launch_prefill(p, (int)dtype, D, true, s); });
+  if (e != hipSuccess) return fail(ATTN_E_HIP, "prefill_paged launch: %s", hipGetErrorString(e));
   return ATTN_OK;
 }
 
@@ -368,19 +418,21 @@ attn_status attn_prefill_paged(attn_dtype dtype, const void* q, const int32_t* c
                                int Hkv, int D, int total_q, int page_size, int num_pages,
                                int max_pages_per_req, int max_seqlen_q, int max_kv_len,
                                int causal, float scale, void* out, float* lse, void* stream) {
-  g_last_error[0] = 0;
-  attn::PrefillParams p;
-  bool empty = false;
-  attn_status st = paged_prefill_params(dtype, q, cu_seqlens_q, k_pages, v_pages, page_table,
-                                        kv_lens, B, Hq, Hkv, D, total_q, page_size, num_pages,
-                                        max_pages_per_req, max_seqlen_q, max_kv_len, causal, scale,
-                                        out, lse, p, empty);
-  if (st != ATTN_OK || empty) return st;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e =
-      timed(ATTN_KERNEL_PREFILL_PAGED, s, [&] { return attn::launch_prefill(p, (int)dtype, D, true, s); });
-  if (e != hipSuccess) return fail(ATTN_E_HIP, "prefill_paged launch: %s", hipGetErrorString(e));
-  return ATTN_OK;
+  return prefill_paged_impl(dtype, 0, q, cu_seqlens_q, k_pages, v_pages, page_table, kv_lens, B,
+                            Hq, Hkv, D, total_q, page_size, num_pages, max_pages_per_req,
+                            max_seqlen_q, max_kv_len, causal, scale, out, lse, stream);
+}
+
+attn_status attn_prefill_paged_hnd(attn_dtype dtype, const void* q, const int32_t* cu_seqlens_q,
+                                   const void* k_pages, const void* v_pages,
+                                   const int32_t* page_table, const int32_t* kv_lens, int B,
+                                   int Hq, int Hkv, int D, int total_q, int page_size,
+                                   int num_pages, int max_pages_per_req, int max_seqlen_q,
+                                   int max_kv_len, int causal, float scale, void* out,
+                                   float* lse, void* stream) {
+  return prefill_paged_impl(dtype, 1, q, cu_seqlens_q, k_pages, v_pages, page_table, kv_lens, B,
+                            Hq, Hkv, D, total_q, page_size, num_pages, max_pages_per_req,
+                            max_seqlen_q, max_kv_len, causal, scale, out, lse, stream);
 }
 
 static size_t elem_bytes(attn_dtype dtype) { return dtype == ATTN_F32 ? 4 : 2; }
@@ -392,7 +444,7 @@ size_t attn_prefill_paged_cascade_workspace_size(attn_dtype dtype, int total_q, 
   return round256(rows * D * elem_bytes(dtype)) + round256(rows * sizeof(float));
 }
 
-attn_status attn_prefill_paged_cascade(attn_dtype dtype, const void* q,
+static attn_status cascade_impl(attn_dtype dtype, int kv_hnd, const void* q,
                                        const int32_t* cu_seqlens_q, const void* k_pages,
                                        const void* v_pages, const int32_t* page_table,
                                        const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
@@ -407,7 +459,7 @@ attn_status attn_prefill_paged_cascade(attn_dtype dtype, const void* q,
   attn_status st = paged_prefill_params(dtype, q, cu_seqlens_q, k_pages, v_pages, page_table,
                                         kv_lens, B, Hq, Hkv, D, total_q, page_size, num_pages,
                                         max_pages_per_req, max_seqlen_q, max_kv_len, causal, scale,
-                                        out, lse, p, empty);
+                                        out, lse, kv_hnd, p, empty);
   if (st != ATTN_OK) return st;
   if (shared_prefix_len < 0 || shared_prefix_len % page_size != 0)
     return fail(ATTN_E_SHAPE, "shared_prefix_len=%d is not a non-negative multiple of "
@@ -460,6 +512,36 @@ attn_status attn_prefill_paged_cascade(attn_dtype dtype, const void* q,
             [&] { return attn::launch_prefill(suf, (int)dtype, D, true, s); });
   if (e != hipSuccess) return fail(ATTN_E_HIP, "cascade suffix launch: %s", hipGetErrorString(e));
   return ATTN_OK;
+}
+
+attn_status attn_prefill_paged_cascade(attn_dtype dtype, const void* q,
+                                       const int32_t* cu_seqlens_q, const void* k_pages,
+                                       const void* v_pages, const int32_t* page_table,
+                                       const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                                       int total_q, int page_size, int num_pages,
+                                       int max_pages_per_req, int max_seqlen_q, int max_kv_len,
+                                       int shared_prefix_len, int causal, float scale, void* out,
+                                       float* lse, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  return cascade_impl(dtype, 0, q, cu_seqlens_q, k_pages, v_pages, page_table, kv_lens, B, Hq,
+                      Hkv, D, total_q, page_size, num_pages, max_pages_per_req, max_seqlen_q,
+                      max_kv_len, shared_prefix_len, causal, scale, out, lse, workspace,
+                      workspace_bytes, stream);
+}
+
+attn_status attn_prefill_paged_cascade_hnd(attn_dtype dtype, const void* q,
+                                           const int32_t* cu_seqlens_q, const void* k_pages,
+                                           const void* v_pages, const int32_t* page_table,
+                                           const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                                           int total_q, int page_size, int num_pages,
+                                           int max_pages_per_req, int max_seqlen_q,
+                                           int max_kv_len, int shared_prefix_len, int causal,
+                                           float scale, void* out, float* lse, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  return cascade_impl(dtype, 1, q, cu_seqlens_q, k_pages, v_pages, page_table, kv_lens, B, Hq,
+                      Hkv, D, total_q, page_size, num_pages, max_pages_per_req, max_seqlen_q,
+                      max_kv_len, shared_prefix_len, causal, scale, out, lse, workspace,
+                      workspace_bytes, stream);
 }
 
 attn_status attn_merge_states(attn_dtype dtype, const void* o_a, const float* lse_a,

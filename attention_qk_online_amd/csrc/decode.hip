@@ -148,8 +148,12 @@ __global__ __launch_bounds__(kNW * 64) void decode_split_kernel(DecodeParams p) 
 
   const T* kbase = reinterpret_cast<const T*>(p.k_pages);
   const T* vbase = reinterpret_cast<const T*>(p.v_pages);
-  const size_t row_stride = (size_t)p.Hkv * D;            // elements between tokens
-  const size_t lane_off = (size_t)kvh * D + gl * VPL;
+  // Elements between consecutive tokens of one head and from a page's start
+  // to this head's first row: NHD interleaves the heads of a token, HND keeps
+  // each head's 16 rows together.
+  const size_t row_stride = p.kv_hnd ? (size_t)D : (size_t)p.Hkv * D;
+  const size_t page_stride = (size_t)kPage * p.Hkv * D;
+  const size_t lane_off = (size_t)kvh * (p.kv_hnd ? kPage * D : D) + gl * VPL;
   const int32_t* table = p.page_table + (size_t)b * p.max_pages;
 
   // Pages of this wave: first, first + NW, first + 2 NW, ...  A split holds
@@ -173,7 +177,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_split_kernel(DecodeParams p) 
     pid = bf.ok ? pid : 0;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const size_t off = ((size_t)pid * kPage + grp * 4 + t) * row_stride + lane_off;
+      const size_t off = (size_t)pid * page_stride + (size_t)(grp * 4 + t) * row_stride + lane_off;
       bf.k[t].load(kbase + off);
       bf.v[t].load(vbase + off);
     }
@@ -430,7 +434,11 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
   char* myv = decode_vbuf<D>(wave);
   const char* kbase = reinterpret_cast<const char*>(p.k_pages);
   const char* vbase = reinterpret_cast<const char*>(p.v_pages);
-  const size_t tok_b = (size_t)p.Hkv * GROWB;            // bytes between tokens
+  // Bytes between consecutive tokens of one head, and per page (NHD
+  // interleaves the heads of a token, HND keeps each head's 16 rows together).
+  const size_t tok_b = p.kv_hnd ? (size_t)GROWB : (size_t)p.Hkv * GROWB;
+  const size_t page_b = (size_t)kPage * p.Hkv * GROWB;
+  const size_t head_b = p.kv_hnd ? (size_t)kPage * GROWB : (size_t)GROWB;
   const float c = p.scale_log2;
   const float qnan = __builtin_nanf("");
 
@@ -476,8 +484,8 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
     for (int i = 0; i < C::DB; ++i) o[i] = f32x4{};
     float m = kNegInf, lsum = 0.f;
     bool bad = false;
-    const char* kh = kbase + (size_t)kvh * GROWB;
-    const char* vh = vbase + (size_t)kvh * GROWB;
+    const char* kh = kbase + (size_t)kvh * head_b;
+    const char* vh = vbase + (size_t)kvh * head_b;
     const int32_t* table = p.page_table + (size_t)b * p.max_pages + pg0;
 
     for (int c0 = 0; c0 < n; c0 += 64) {
@@ -487,8 +495,8 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
         int pid = __builtin_amdgcn_readlane(ids, i);
         pg.ok = (unsigned)pid < (unsigned)p.num_pages;
         pid = pg.ok ? pid : 0;
-        const char* kp = kh + (size_t)pid * kPage * tok_b;
-        const char* vp = vh + (size_t)pid * kPage * tok_b;
+        const char* kp = kh + (size_t)pid * page_b;
+        const char* vp = vh + (size_t)pid * page_b;
 #pragma unroll
         for (int j = 0; j < NK; ++j) {
           const int off = F8 ? 64 * j + 16 * gq : (32 * j + 8 * gq) * 2;

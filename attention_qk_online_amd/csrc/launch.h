@@ -32,6 +32,8 @@ struct DecodeParams {
   int hw, nhg, n_groups, min_run, max_segs;
   float scale_log2;        // softmax scale * log2(e) (E4M3 cache: times the key scale)
   float v_scale;           // E4M3 cache only: scale of the values
+  // Page layout: 0 = NHD [page, slot, kv head, d], 1 = HND [page, kv head, slot, d].
+  int kv_hnd;
 };
 
 struct PrefillParams {
@@ -59,6 +61,8 @@ struct PrefillParams {
   // out / lse -- is merged into each written row before it is stored.
   const void* merge_o;
   const float* merge_lse;
+  // Paged only: page layout, 0 = NHD, 1 = HND (as DecodeParams::kv_hnd).
+  int kv_hnd;
   float scale_log2;
 };
 

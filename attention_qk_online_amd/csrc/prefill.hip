@@ -206,7 +206,11 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
   constexpr int RPI = 64 / C::CH;                      // rows per DMA instruction
   const char* kg = reinterpret_cast<const char*>(p.k);
   const char* vg = reinterpret_cast<const char*>(p.v);
-  const int kv_rowb = p.Hkv * C::ROWB;                 // bytes between consecutive tokens
+  // Bytes between consecutive keys of one head: NHD interleaves the heads of
+  // a token, HND (paged only) keeps each head's 16 rows of a page together.
+  const int kv_rowb = (PAGED && p.kv_hnd) ? C::ROWB : p.Hkv * C::ROWB;
+  const size_t page_b = (size_t)kPage * p.Hkv * C::ROWB;
+  const size_t head_b = (PAGED && p.kv_hnd) ? (size_t)kPage * C::ROWB : (size_t)C::ROWB;
   const int wrow0 = wave * C::WROWS;                   // first tile row of this wave
   const int lane_row = lane / C::CH, lane_q = lane % C::CH;
   const int lane_rowb = lane_row * kv_rowb;
@@ -242,7 +246,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
     const char* base;
     int nrec;
     if constexpr (PAGED) {
-      base = g + (size_t)pid * kPage * kv_rowb + (size_t)kvh * C::ROWB;
+      base = g + (size_t)pid * page_b + (size_t)kvh * head_b;
       nrec = (kPage - 1) * kv_rowb + C::ROWB;
     } else {
       base = g + ((size_t)(k_start + k0) * kv_rowb + (size_t)kvh * C::ROWB);

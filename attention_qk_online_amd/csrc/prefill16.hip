@@ -197,7 +197,11 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
   constexpr int RPI = 64 / CH;
   const char* kg = reinterpret_cast<const char*>(p.k);
   const char* vg = reinterpret_cast<const char*>(p.v);
-  const int kv_rowb = p.Hkv * ROWB;
+  // Bytes between consecutive keys of one head: NHD interleaves the heads of
+  // a token, HND (paged only) keeps each head's 16 rows of a page together.
+  const int kv_rowb = (PAGED && p.kv_hnd) ? ROWB : p.Hkv * ROWB;
+  const size_t page_b = (size_t)kPage * p.Hkv * ROWB;
+  const size_t head_b = (PAGED && p.kv_hnd) ? (size_t)kPage * ROWB : (size_t)ROWB;
   const int wrow0 = wave * WROWS;
   const int lane_row = lane / CH, lane_q = lane % CH;
   const int lane_rowb = lane_row * kv_rowb;
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
     const char* base;
     int nrec;
     if constexpr (PAGED) {
-      base = g + (size_t)pid * kPage * kv_rowb + (size_t)kvh * ROWB;
+      base = g + (size_t)pid * page_b + (size_t)kvh * head_b;
       nrec = (kPage - 1) * kv_rowb + ROWB;
     } else {
       base = g + ((size_t)(k_start + k0) * kv_rowb + (size_t)kvh * ROWB);

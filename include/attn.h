@@ -267,6 +267,47 @@ attn_status attn_merge_states(attn_dtype dtype, const void* o_a, const float* ls
                               float* lse_out, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* The paged entry points above read NHD pages: [num_pages, page_size, Hkv, D],
+ * the heads of one token adjacent.  Each has a twin for HND pages,
+ * [num_pages, Hkv, page_size, D], where one head's page_size rows are
+ * contiguous (the two layouts of "FlashInfer内核库深度解析", KV-cache
+ * layout choice: NHD for many heads in parallel, HND for long,
+ * bandwidth-bound sequences).  Arguments, results, workspace and errors are
+ * those of the NHD call; only the order of the pool's middle dimensions
+ * differs, so the same cache permuted gives the same result bit for bit.
+ */
+attn_status attn_decode_paged_hnd(attn_dtype dtype, const void* q, const void* k_pages,
+                                  const void* v_pages, const int32_t* page_table,
+                                  const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                                  int page_size, int num_pages, int max_pages_per_req,
+                                  int max_kv_len, int split_pages, float scale, void* out,
+                                  float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+attn_status attn_decode_paged_fp8_hnd(attn_dtype dtype, const void* q, const void* k_pages,
+                                      const void* v_pages, const int32_t* page_table,
+                                      const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                                      int page_size, int num_pages, int max_pages_per_req,
+                                      int max_kv_len, int split_pages, float scale,
+                                      float k_scale, float v_scale, void* out, float* lse,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+attn_status attn_prefill_paged_hnd(attn_dtype dtype, const void* q, const int32_t* cu_seqlens_q,
+                                   const void* k_pages, const void* v_pages,
+                                   const int32_t* page_table, const int32_t* kv_lens, int B,
+                                   int Hq, int Hkv, int D, int total_q, int page_size,
+                                   int num_pages, int max_pages_per_req, int max_seqlen_q,
+                                   int max_kv_len, int causal, float scale, void* out,
+                                   float* lse, void* stream);
+attn_status attn_prefill_paged_cascade_hnd(attn_dtype dtype, const void* q,
+                                           const int32_t* cu_seqlens_q, const void* k_pages,
+                                           const void* v_pages, const int32_t* page_table,
+                                           const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                                           int total_q, int page_size, int num_pages,
+                                           int max_pages_per_req, int max_seqlen_q,
+                                           int max_kv_len, int shared_prefix_len, int causal,
+                                           float scale, void* out, float* lse, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Status text (static strings) and the detail of the calling thread's last
  * failing call (valid until that thread's next call into the library). */
 const char* attn_status_string(attn_status s);

@@ -224,6 +224,13 @@ def test_merge_rejects(lib):
     assert call(rows=0, oa=None) == OK
 
 
+def test_binding_checks_layout_name():
+    import attention_qk_online_amd as A
+    assert A._layout("NHD") == "" and A._layout("HND") == "_hnd"
+    with pytest.raises(ValueError):
+        A._layout("nhd")
+
+
 def test_binding_rejects_host_tensors():
     import attention_qk_online_amd as A
     q = torch.zeros(2, 4, 128, dtype=torch.bfloat16)

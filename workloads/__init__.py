@@ -45,6 +45,15 @@ def _randn(g: torch.Generator, shape, dtype) -> torch.Tensor:
     return torch.randn(*shape, generator=g, dtype=torch.float32).to(dtype)
 
 
+def _to_layout(pool: torch.Tensor, layout: str) -> torch.Tensor:
+    """An NHD pool [pages, P, Hkv, D] as itself or as HND [pages, Hkv, P, D]."""
+    if layout == "NHD":
+        return pool
+    if layout == "HND":
+        return pool.transpose(1, 2).contiguous()
+    raise ValueError(f"layout must be NHD or HND, got {layout!r}")
+
+
 # ---------------------------------------------------------------------------
 # Paged decode
 # ---------------------------------------------------------------------------
@@ -86,8 +95,9 @@ class DecodeCase:
     def max_kv_len(self) -> int:
         return int(self.kv_lens.max().item()) if self.B > 0 else 0
 
-    def pools(self, device="cpu"):
-        """Materialise (k_pages, v_pages) [num_pages, P, Hkv, D] on ``device``."""
+    def pools(self, device="cpu", layout="NHD"):
+        """Materialise (k_pages, v_pages) on ``device``: [num_pages, P, Hkv, D]
+        (NHD) or, with ``layout="HND"``, the same cache as [num_pages, Hkv, P, D]."""
         shape = (self.num_pages, self.page_size, self.Hkv, self.D)
         fill = float("nan") if self.poison else 0.0
         out = []
@@ -96,13 +106,13 @@ class DecodeCase:
             pool = torch.full(shape, fill, dtype=self.dtype, device=device)
             flat = pool.view(self.num_pages * self.page_size, self.Hkv, self.D)
             flat.index_copy_(0, idx, tok.to(device))
-            out.append(pool)
+            out.append(_to_layout(pool, layout))
         return out[0], out[1]
 
     def kv_bytes(self) -> int:
         return decode_kv_bytes(self.kv_lens, self.Hkv, self.D, self.dtype)
 
-    def fp8_pools(self, device="cpu"):
+    def fp8_pools(self, device="cpu", layout="NHD"):
         """The same cache stored as 8-bit floats E4M3 with one scale per tensor.
 
         Each of K and V is divided by amax/448 (448 = the largest E4M3
@@ -122,7 +132,7 @@ class DecodeCase:
             pool = torch.full(shape, 0x7F if self.poison else 0, dtype=torch.uint8, device=device)
             flat = pool.view(self.num_pages * self.page_size, self.Hkv, self.D)
             flat.index_copy_(0, idx, q8.to(device))
-            out += [pool, sc]
+            out += [_to_layout(pool, layout), sc]
         return out[0], out[2], out[1], out[3]
 
     def fp8_kv_bytes(self) -> int:
@@ -353,8 +363,10 @@ class PagedPrefillCase:
     def max_pages(self) -> int:
         return int(self.page_table.shape[1])
 
-    def pools(self, device="cpu"):
-        return self.pool_k.to(device), self.pool_v.to(device)
+    def pools(self, device="cpu", layout="NHD"):
+        """(k_pages, v_pages) on ``device``, NHD or HND (see DecodeCase.pools)."""
+        return (_to_layout(self.pool_k.to(device), layout),
+                _to_layout(self.pool_v.to(device), layout))
 
     def flops(self) -> int:
         return prefill_flops(self.lens_q, self.kv_lens.tolist(), self.Hq, self.D, self.causal)
