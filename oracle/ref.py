@@ -83,6 +83,13 @@ def causal_visible(rows: torch.Tensor, n_keys: int, offset: int) -> torch.Tensor
     return torch.arange(n_keys).unsqueeze(0) <= (rows.long().unsqueeze(1) + offset)
 
 
+def window_visible(rows: torch.Tensor, n_keys: int, offset: int, left: int) -> torch.Tensor:
+    """Sliding window (left side, aligned like the causal mask): query row r
+    sees key j iff j >= r + offset - left ("FlashAttention-3 内核在最新大模型
+    推理中的集成实践" section 二, window_size of varlen_fwd)."""
+    return torch.arange(n_keys).unsqueeze(0) >= (rows.long().unsqueeze(1) + offset - left)
+
+
 def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
     """Grouped-query mapping: consecutive groups of Hq/Hkv query heads share one KV head."""
     return h // (Hq // Hkv)
@@ -183,8 +190,9 @@ def ref_decode_paged_fp8(q, k_pages, v_pages, k_scale: float, v_scale: float, pa
 
 
 def _prefill_one(qs, ks, vs, Hq, Hkv, scale, causal, rows: Optional[torch.Tensor],
-                 block: int = 1024):
-    """One sequence: qs [Lq, Hq, D], ks/vs [Lk, Hkv, D]; causal is bottom-right.
+                 block: int = 1024, window_left: int = -1):
+    """One sequence: qs [Lq, Hq, D], ks/vs [Lk, Hkv, D]; causal is bottom-right;
+    window_left >= 0 adds the sliding-window bound (-1: none).
 
     Rows go in blocks of at most ``block`` queries; under the causal mask a
     block only multiplies against the keys its last row can see, since every
@@ -199,6 +207,9 @@ def _prefill_one(qs, ks, vs, Hq, Hkv, scale, causal, rows: Optional[torch.Tensor
         r = idx[s0:s0 + block]
         kmax = Lk if not causal else max(0, min(Lk, int(r.max()) + off + 1))
         vis = causal_visible(r, kmax, off) if causal else None
+        if window_left >= 0:
+            w = window_visible(r, kmax, off, window_left)
+            vis = w if vis is None else vis & w
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
             o, l = softmax_attend(qs[r, h], ks[:kmax, g], vs[:kmax, g], scale, vis)
@@ -208,7 +219,7 @@ def _prefill_one(qs, ks, vs, Hq, Hkv, scale, causal, rows: Optional[torch.Tensor
 
 
 def ref_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale,
-                       rows: Optional[torch.Tensor] = None):
+                       rows: Optional[torch.Tensor] = None, window_left: int = -1):
     """Ragged prefill addressed by cu_seqlens (length B+1).
 
     q [Tq, Hq, D]; k, v [Tk, Hkv, D].  Returns out [Tq, Hq, D], lse [Tq, Hq]
@@ -232,7 +243,8 @@ def ref_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale,
             if sel.numel() == 0:
                 continue
             local = sel - q0
-        o, l = _prefill_one(q[q0:q1], k[k0:k1], v[k0:k1], Hq, Hkv, scale, causal, local)
+        o, l = _prefill_one(q[q0:q1], k[k0:k1], v[k0:k1], Hq, Hkv, scale, causal, local,
+                            window_left=window_left)
         tgt = torch.arange(q0, q1) if local is None else local + q0
         out[tgt] = o
         lse[tgt] = l
@@ -240,7 +252,7 @@ def ref_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale,
 
 
 def ref_prefill_paged(q, cu_seqlens_q, k_pages, v_pages, page_table, kv_lens, causal, scale,
-                      rows: Optional[torch.Tensor] = None):
+                      rows: Optional[torch.Tensor] = None, window_left: int = -1):
     """Chunked prefill over a paged cache: request b's queries are the last
     Lq_b of its kv_lens[b] tokens (bottom-right causal)."""
     B = len(cu_seqlens_q) - 1
@@ -253,7 +265,8 @@ def ref_prefill_paged(q, cu_seqlens_q, k_pages, v_pages, page_table, kv_lens, ca
     tail = tuple(k_pages.shape[2:])
     k = torch.cat(ks) if ks else k_pages.new_zeros((0,) + tail)
     v = torch.cat(vs) if vs else v_pages.new_zeros((0,) + tail)
-    return ref_prefill_varlen(q, k, v, cu_seqlens_q, torch.tensor(ck), causal, scale, rows=rows)
+    return ref_prefill_varlen(q, k, v, cu_seqlens_q, torch.tensor(ck), causal, scale, rows=rows,
+                              window_left=window_left)
 
 
 def merge_states(states: Sequence[Tuple[torch.Tensor, torch.Tensor]]):

@@ -58,7 +58,7 @@ def pin_golden(R):
         if g["kind"] == "prefill":
             o, l = R.ref_prefill_varlen(_tensor(g["q"]), _tensor(g["k"]), _tensor(g["v"]),
                                         g["cu_seqlens_q"], g["cu_seqlens_k"], g["causal"],
-                                        _ev(g["scale"]))
+                                        _ev(g["scale"]), window_left=g.get("window_left", -1))
         elif g["kind"] == "fp8_e4m3":
             got = R.fp8_e4m3_to_float(torch.tensor([b for b, _ in g["values"]], dtype=torch.uint8))
             want = torch.tensor([_ev(v) for _, v in g["values"]], dtype=F64)
@@ -348,10 +348,46 @@ def pin_fp8_decode_equals_dequantised(R):
     _close(l3, l, 1e-12)
 
 
+def pin_window_brute_force(R):
+    """Sliding window against explicit loops over (i, j, d), causal and not,
+    with Lq < Lk (bottom-right alignment), and its limits: a window as long
+    as the keys is no window; window 0 with causal leaves each row its own key."""
+    c = workloads.make_prefill(B=2, Hq=2, Hkv=1, D=3, lens_q=[4, 3], lens_k=[7, 3], dtype=F64,
+                               seed=40, causal=True)
+    for causal in (True, False):
+        for left in (0, 2, 5):
+            o, l = R.ref_prefill_varlen(c.q, c.k, c.v, c.cu_seqlens_q, c.cu_seqlens_k, causal,
+                                        c.scale, window_left=left)
+            cq, ck = c.cu_seqlens_q.tolist(), c.cu_seqlens_k.tolist()
+            for b in range(2):
+                Lq, Lk = cq[b + 1] - cq[b], ck[b + 1] - ck[b]
+                for i in range(Lq):
+                    for h in range(2):
+                        js = [j for j in range(Lk) if j >= i + Lk - Lq - left and
+                              (not causal or j <= i + Lk - Lq)]
+                        sc = [c.scale * sum(float(c.q[cq[b] + i, h, d]) * float(c.k[ck[b] + j, 0, d])
+                                            for d in range(3)) for j in js]
+                        mx = max(sc)
+                        w = [math.exp(x - mx) for x in sc]
+                        z = sum(w)
+                        for d in range(3):
+                            want = sum(wj * float(c.v[ck[b] + j, 0, d]) for wj, j in zip(w, js)) / z
+                            assert abs(float(o[cq[b] + i, h, d]) - want) < 1e-12
+                        assert abs(float(l[cq[b] + i, h]) - (mx + math.log(z))) < 1e-12
+    full = R.ref_prefill_varlen(c.q, c.k, c.v, c.cu_seqlens_q, c.cu_seqlens_k, True, c.scale)
+    wide = R.ref_prefill_varlen(c.q, c.k, c.v, c.cu_seqlens_q, c.cu_seqlens_k, True, c.scale,
+                                window_left=7)
+    _close(full[0], wide[0], 0.0)
+    o, l = R.ref_prefill_varlen(c.q, c.k, c.v, c.cu_seqlens_q, c.cu_seqlens_k, True, c.scale,
+                                window_left=0)
+    _close(o[3, 0], c.v[6, 0], 0.0)       # last row of sequence 0 sits on key 6
+
+
 PINS = [pin_golden, pin_brute_force, pin_sdpa_library, pin_single_key, pin_constant_v,
         pin_scale_zero_mean, pin_shift_invariance, pin_paging, pin_gqa_equals_repeated_mha,
         pin_causal_rows, pin_chunked_equals_full, pin_merge_partition, pin_empty_rows,
-        pin_rows_subset, pin_fp8_decoder_library, pin_fp8_decode_equals_dequantised]
+        pin_rows_subset, pin_fp8_decoder_library, pin_fp8_decode_equals_dequantised,
+        pin_window_brute_force]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -372,6 +408,9 @@ MUTANTS = {
     "merge_linear_weights": ("w = torch.exp(lses - mx.unsqueeze(0))",
                              "w = torch.softmax(lses, dim=0) + 0 * mx"),
     "mask_strict": ("<= (rows.long().unsqueeze(1) + offset)", "< (rows.long().unsqueeze(1) + offset)"),
+    "window_sign": ("(rows.long().unsqueeze(1) + offset - left)", "(rows.long().unsqueeze(1) - offset - left)"),
+    "window_strict": (">= (rows.long().unsqueeze(1) + offset - left)", "> (rows.long().unsqueeze(1) + offset - left)"),
+    "window_ignored": ("            vis = w if vis is None else vis & w", "            vis = vis"),
     "fp8_exponent_bias": ("(e - 7).to(F64)", "(e - 8).to(F64)"),
     "fp8_subnormal_as_normal": ("mag = torch.where(e == 0, sub, norm)", "mag = norm"),
     "fp8_nan_on_exponent_15": ("(e == 15) & ((x & 7) == 7)", "(e == 15)"),
