@@ -63,6 +63,9 @@ struct PrefillParams {
   const float* merge_lse;
   // Paged only: page layout, 0 = NHD, 1 = HND (as DecodeParams::kv_hnd).
   int kv_hnd;
+  // Sliding window: query i sees only keys >= i + (Lk - Lq) - window_left
+  // (bottom-right aligned like the causal mask); -1 = no window.
+  int window_left;
   float scale_log2;
 };
 

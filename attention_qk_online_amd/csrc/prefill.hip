@@ -172,10 +172,23 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
     const int k_end = min(max(p.cu_k[b + 1], k_start), p.total_k);
     Lk = k_end - k_start;
   }
-  const int off = Lk - Lq;                       // bottom-right causal offset
+  int off = Lk - Lq;                             // bottom-right causal offset
   const int r_last = min(r0 + BM, Lq) - 1;
   int kend = p.causal ? min(Lk, r_last + off + 1) : Lk;
   if (kend < 0) kend = 0;
+  // Sliding window: query i sees keys from i + off - window_left on.  Whole
+  // tiles before the first row's window are skipped by moving the key origin
+  // (tile-aligned, so paged tiles still start at a page).
+  const int win = p.window_left;
+  if (win >= 0) {
+    const int kt0 = min(max(0, r0 + off - win), kend) / C::BN;
+    const int sh = kt0 * C::BN;
+    if constexpr (PAGED) table += sh / kPage;
+    else k_start += sh;
+    Lk -= sh;
+    off -= sh;
+    kend -= sh;
+  }
   const int n_kt = (kend + C::BN - 1) / C::BN;
 
   // Scores are used as s * c with c > 0: a negative scale flips the sign of Q,
@@ -303,8 +316,10 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
   const int pos = my_row + off;   // last visible key index for this lane's query
   // Tiles this wave needs (keys up to its last row's diagonal), and the
   // leading ones in which every row of the wave sees every key (no mask).
-  int w_kt = 0, w_fast = 0;
+  int w_kt = 0, w_fast = 0, w_lead = 0;
   if (wave_rows) {
+    // tiles before w_lead hold keys left of some row's window
+    if (win >= 0) w_lead = max(0, w_last + off - win + C::BN - 1) / C::BN;
     const int wkend = p.causal ? max(0, min(Lk, w_last + off + 1)) : Lk;
     w_kt = min(n_kt, (wkend + C::BN - 1) / C::BN);
     int lim = t_full;
@@ -323,16 +338,18 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
     }
   };
 
-  // Scores past the end of the keys or right of this lane's diagonal -> -inf.
+  // Scores past the end of the keys, right of this lane's diagonal or left of
+  // its window -> -inf.
   auto mask = [&](int kt, f32x16 (&s)[C::KB]) {
     const int k0 = kt * C::BN;
     const int lim = p.causal ? min(pos, Lk - 1) : Lk - 1;
+    const int lo = win >= 0 ? pos - win : 0;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        s[kb][r] = key > lim ? kNegInf : s[kb][r];
+        s[kb][r] = (key > lim || key < lo) ? kNegInf : s[kb][r];
       }
   };
 
@@ -440,7 +457,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
       }
     } else if (kt < w_kt) {
-      if (kt >= w_fast) mask(kt, scur);
+      if (kt < w_lead || kt >= w_fast) mask(kt, scur);
       update_max(scur);
       if (kt + 1 < w_kt) qk(KNXT, snext);
       weights(scur, pb, m == kNegInf ? 0.f : -m);
@@ -471,6 +488,14 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
     n_fast = max(0, min(n_fast, w_kt0 - 1));
     n_fast -= n_fast % C::R;
   }
+  // Leading tiles that some row's window cuts (from the last row, whose
+  // window starts latest) run the masked step too; a multiple of R.
+  int n_lead = 0;
+  if (win >= 0) {
+    n_lead = min(n_kt, max(0, r_last + off - win + C::BN - 1) / C::BN);
+    n_lead += n_lead % C::R;
+  }
+  n_fast = max(n_fast, n_lead);
 
   // prologue: K(0 .. R-1) and V(0 .. R-2) in LDS, S^T(0) in registers
 #pragma unroll
@@ -490,6 +515,10 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
   if (n_kt > 0) qk(k_ring0, sa);
   __syncthreads();   // every wave is done with K(0) before step 0 refills its slot
   int kt = 0;
+  for (; kt < n_lead; kt += C::R) {
+    step(Idx<0>{}, Idx<0>{}, kt, sa, sb);
+    if (kt + 1 < n_kt) step(Idx<1>{}, Idx<0>{}, kt + 1, sb, sa);
+  }
   for (; kt < n_fast; kt += C::R) {
     step(Idx<0>{}, Idx<1>{}, kt, sa, sb);
     step(Idx<1>{}, Idx<1>{}, kt + 1, sb, sa);

@@ -166,10 +166,23 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
     const int k_end = min(max(p.cu_k[b + 1], k_start), p.total_k);
     Lk = k_end - k_start;
   }
-  const int off = Lk - Lq;                       // bottom-right causal offset
+  int off = Lk - Lq;                             // bottom-right causal offset
   const int r_last = min(r0 + BM, Lq) - 1;
   int kend = p.causal ? min(Lk, r_last + off + 1) : Lk;
   if (kend < 0) kend = 0;
+  // Sliding window: query i sees keys from i + off - window_left on.  Whole
+  // tiles before the first row's window are skipped by moving the key origin
+  // (tile-aligned, so paged tiles still start at a page).
+  const int win = p.window_left;
+  if (win >= 0) {
+    const int kt0 = min(max(0, r0 + off - win), kend) / BN;
+    const int sh = kt0 * BN;
+    if constexpr (PAGED) table += sh / kPage;
+    else k_start += sh;
+    Lk -= sh;
+    off -= sh;
+    kend -= sh;
+  }
   const int n_kt = (kend + BN - 1) / BN;
 
   float c = p.scale_log2;
@@ -279,8 +292,10 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
   const int w_last = min(w_first + RW - 1, Lq - 1);
   const bool wave_rows = w_first < Lq;
   const int pos = my_row + off;
-  int w_kt = 0, w_fast = 0;
+  int w_kt = 0, w_fast = 0, w_lead = 0;
   if (wave_rows) {
+    // tiles before w_lead hold keys left of some row's window
+    if (win >= 0) w_lead = max(0, w_last + off - win + BN - 1) / BN;
     const int wkend = p.causal ? max(0, min(Lk, w_last + off + 1)) : Lk;
     w_kt = min(n_kt, (wkend + BN - 1) / BN);
     int lim = t_full;
@@ -303,12 +318,13 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
   auto mask = [&](int kt, f32x4 (&s)[KB]) {
     const int k0 = kt * BN;
     const int lim = p.causal ? min(pos, Lk - 1) : Lk - 1;
+    const int lo = win >= 0 ? pos - win : 0;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = k0 + 16 * kb + 4 * grp + r;
-        s[kb][r] = key > lim ? kNegInf : s[kb][r];
+        s[kb][r] = (key > lim || key < lo) ? kNegInf : s[kb][r];
       }
   };
 
@@ -381,7 +397,7 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
       weights(scur, pb, -m);
       pv(VCUR, pb);
     } else if (kt < w_kt) {
-      if (kt >= w_fast) mask(kt, scur);
+      if (kt < w_lead || kt >= w_fast) mask(kt, scur);
       update_max(scur);
       if (kt + 1 < w_kt) qk(KNXT, snext);
       weights(scur, pb, m == kNegInf ? 0.f : -m);
@@ -404,6 +420,14 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
     n_fast = max(0, min(n_fast, w_kt0 - 1));
     n_fast -= n_fast % R;
   }
+  // Leading tiles that some row's window cuts (from the last row, whose
+  // window starts latest) run the masked step too; a multiple of R.
+  int n_lead = 0;
+  if (win >= 0) {
+    n_lead = min(n_kt, max(0, r_last + off - win + BN - 1) / BN);
+    n_lead += n_lead % R;
+  }
+  n_fast = max(n_fast, n_lead);
 
   // prologue: K(0 .. R-1) and V(0 .. R-2) in LDS, S^T(0) in registers
 #pragma unroll
@@ -423,6 +447,10 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
   if (n_kt > 0) qk(k_ring0, sa);
   __syncthreads();
   int kt = 0;
+  for (; kt < n_lead; kt += R) {
+    step(Idx<0>{}, Idx<0>{}, kt, sa, sb);
+    if (kt + 1 < n_kt) step(Idx<1>{}, Idx<0>{}, kt + 1, sb, sa);
+  }
   for (; kt < n_fast; kt += R) {
     step(Idx<0>{}, Idx<1>{}, kt, sa, sb);
     step(Idx<1>{}, Idx<1>{}, kt + 1, sb, sa);

@@ -1,0 +1,111 @@
+"""GPU parity of the sliding-window prefill (attn_prefill_varlen_window,
+attn_prefill_paged_window) against the oracle's window_left."""
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _varlen(case, gpu, window, causal=None):
+    import attention_qk_online_amd as A
+    causal = case.causal if causal is None else causal
+    out, lse = A.prefill_varlen(case.q.to(gpu), case.k.to(gpu), case.v.to(gpu),
+                                case.cu_seqlens_q.to(gpu), case.cu_seqlens_k.to(gpu),
+                                case.max_seqlen_q, case.max_seqlen_k, causal=causal,
+                                scale=case.scale, window_left=window)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _ref(case, window, causal=None, rows=None):
+    causal = case.causal if causal is None else causal
+    return oracle.ref_prefill_varlen(case.q, case.k, case.v, case.cu_seqlens_q, case.cu_seqlens_k,
+                                     causal, case.scale, rows=rows, window_left=window)
+
+
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("window", [0, 1, 63, 64, 100, 128, 500])
+def test_window_small(gpu, D, causal, window):
+    lens = [1, 17, 128, 129, 300, 64, 255]
+    case = workloads.make_prefill(B=len(lens), Hq=4, Hkv=2, D=D, lens_q=lens, dtype=torch.bfloat16,
+                                  seed=700 + D, causal=causal)
+    out, lse = _varlen(case, gpu, window)
+    ro, rl = _ref(case, window)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, f"window {window} D{D} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_window_q_shorter_than_k(gpu, causal):
+    """Lq < Lk: the window is aligned bottom-right like the causal mask."""
+    case = workloads.make_prefill(B=3, Hq=4, Hkv=4, D=128, lens_q=[50, 200, 7], lens_k=[400, 333, 900],
+                                  dtype=torch.bfloat16, seed=710, causal=causal)
+    for window in (10, 150, 600):
+        out, lse = _varlen(case, gpu, window)
+        ro, rl = _ref(case, window)
+        assert_parity(out, lse, ro, rl, torch.bfloat16, f"Lq<Lk window {window}")
+
+
+def test_window_wider_than_keys_is_no_window(gpu):
+    """A window covering every key gives the plain call's result bit for bit."""
+    case = workloads.make_prefill(B=2, Hq=8, Hkv=2, D=128, lens_q=[300, 129], dtype=torch.bfloat16,
+                                  seed=720, causal=True)
+    o1, l1 = _varlen(case, gpu, -1)
+    o2, l2 = _varlen(case, gpu, 300)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_window_paged(gpu, D, layout):
+    import attention_qk_online_amd as A
+    case = workloads.make_paged_prefill(B=3, Hq=4, Hkv=2, D=D, page_size=16, chunk=90, cached=250,
+                                        shared_prefix=64, dtype=torch.bfloat16, seed=730 + D)
+    kp, vp = case.pools(gpu, layout=layout)
+    for window in (0, 77, 200):
+        out, lse = A.prefill_paged(case.q.to(gpu), case.cu_seqlens_q.to(gpu), kp, vp,
+                                   case.page_table.to(gpu), case.kv_lens.to(gpu), case.max_seqlen_q,
+                                   case.max_kv_len, causal=True, scale=case.scale,
+                                   kv_layout=layout, window_left=window)
+        torch.cuda.synchronize()
+        ro, rl = oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, case.pool_k, case.pool_v,
+                                          case.page_table, case.kv_lens, True, case.scale,
+                                          window_left=window)
+        assert_parity(out, lse, ro, rl, torch.bfloat16, f"paged {layout} D{D} window {window}")
+
+
+def test_window_ragged_config_sampled(gpu):
+    """The ragged causal workload (B 8, L in [1024, 4096], Hq 64, Hkv 8, D 128) with a
+    1024-key window, sampled rows."""
+    case = workloads.make_config(3)
+    out, lse = _varlen(case, gpu, 1024)
+    cu = [int(x) for x in case.cu_seqlens_q]
+    g = torch.Generator().manual_seed(740)
+    rows = set(torch.randint(0, cu[-1], (64,), generator=g).tolist())
+    for a, b in zip(cu[:-1], cu[1:]):
+        rows.update(r for r in (a, a + 1023, a + 1024, a + 1025, b - 1) if a <= r < b)
+    rows = torch.tensor(sorted(rows))
+    ro, rl = _ref(case, 1024, rows=rows)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, "ragged window 1024 (sampled rows)", rows=rows)
+    assert torch.isfinite(out.float()).all()
+
+
+def test_window_chunked_paged_config_sampled(gpu):
+    """The chunked paged workload (16 x 512 queries over 8704 keys, D 256) with a 2048-key window."""
+    import attention_qk_online_amd as A
+    case = workloads.make_config(5)
+    kp, vp = case.pools(gpu)
+    out, lse = A.prefill_paged(case.q.to(gpu), case.cu_seqlens_q.to(gpu), kp, vp,
+                               case.page_table.to(gpu), case.kv_lens.to(gpu), case.max_seqlen_q,
+                               case.max_kv_len, causal=True, scale=case.scale, window_left=2048)
+    torch.cuda.synchronize()
+    cu = [int(x) for x in case.cu_seqlens_q]
+    rows = torch.tensor(sorted({r for a, b in zip(cu[:-1], cu[1:]) for r in (a, a + 200, b - 1)}))
+    ro, rl = oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, case.pool_k, case.pool_v,
+                                      case.page_table, case.kv_lens, True, case.scale, rows=rows,
+                                      window_left=2048)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, "chunked paged window 2048 (sampled)", rows=rows)
