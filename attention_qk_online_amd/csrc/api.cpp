@@ -173,7 +173,8 @@ size_t attn_decode_paged_workspace_size(attn_dtype dtype, int B, int Hq, int Hkv
 
 // Both decode entry points; fp8_kv: the pages hold E4M3 bytes with scales
 // k_scale / v_scale.
-static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, const void* q,
+static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int window_left,
+                               const void* q,
                                const void* k_pages,
                                const void* v_pages, const int32_t* page_table,
                                const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
@@ -187,6 +188,7 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, const 
     return fail(ATTN_E_UNSUPPORTED, "decode_paged_fp8: queries must be ATTN_BF16 or ATTN_F16");
   if (fp8_kv && (!std::isfinite(k_scale) || !std::isfinite(v_scale)))
     return fail(ATTN_E_VALUE, "k_scale / v_scale not finite");
+  if (window_left < -1) return fail(ATTN_E_VALUE, "window_left=%d (-1 = no window)", window_left);
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || num_pages < 0 ||
       max_pages_per_req < 0 || max_kv_len < 0 || split_pages < 0)
     return fail(ATTN_E_SHAPE,
@@ -234,6 +236,7 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, const 
   p.scale_log2 = fp8_kv ? scale * k_scale * kLog2e : scale * kLog2e;
   p.v_scale = fp8_kv ? v_scale : 1.f;
   p.kv_hnd = kv_hnd;
+  p.window_left = window_left;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = timed(ATTN_KERNEL_DECODE_SPLIT, s,
@@ -256,7 +259,7 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pag
                               int max_kv_len, int split_pages, float scale, void* out,
                               float* lse, void* workspace, size_t workspace_bytes,
                               void* stream) {
-  return decode_impl(dtype, false, 0, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
+  return decode_impl(dtype, false, 0, -1, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
                      page_size, num_pages, max_pages_per_req, max_kv_len, split_pages, scale, 1.f,
                      1.f, out, lse, workspace, workspace_bytes, stream);
 }
@@ -268,7 +271,7 @@ attn_status attn_decode_paged_hnd(attn_dtype dtype, const void* q, const void* k
                                   int max_kv_len, int split_pages, float scale, void* out,
                                   float* lse, void* workspace, size_t workspace_bytes,
                                   void* stream) {
-  return decode_impl(dtype, false, 1, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
+  return decode_impl(dtype, false, 1, -1, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
                      page_size, num_pages, max_pages_per_req, max_kv_len, split_pages, scale, 1.f,
                      1.f, out, lse, workspace, workspace_bytes, stream);
 }
@@ -280,9 +283,24 @@ attn_status attn_decode_paged_fp8(attn_dtype dtype, const void* q, const void* k
                                   int max_kv_len, int split_pages, float scale, float k_scale,
                                   float v_scale, void* out, float* lse, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  return decode_impl(dtype, true, 0, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
+  return decode_impl(dtype, true, 0, -1, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
                      page_size, num_pages, max_pages_per_req, max_kv_len, split_pages, scale,
                      k_scale, v_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_paged_window(attn_dtype dtype, int kv_layout, int window_left,
+                                     const void* q, const void* k_pages, const void* v_pages,
+                                     const int32_t* page_table, const int32_t* kv_lens, int B,
+                                     int Hq, int Hkv, int D, int page_size, int num_pages,
+                                     int max_pages_per_req, int max_kv_len, int split_pages,
+                                     float scale, void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (kv_layout != 0 && kv_layout != 1)
+    return fail(ATTN_E_VALUE, "kv_layout=%d (0 = NHD, 1 = HND)", kv_layout);
+  return decode_impl(dtype, false, kv_layout, window_left, q, k_pages, v_pages, page_table,
+                     kv_lens, B, Hq, Hkv, D, page_size, num_pages, max_pages_per_req, max_kv_len,
+                     split_pages, scale, 1.f, 1.f, out, lse, workspace, workspace_bytes, stream);
 }
 
 attn_status attn_decode_paged_fp8_hnd(attn_dtype dtype, const void* q, const void* k_pages,
@@ -292,7 +310,7 @@ attn_status attn_decode_paged_fp8_hnd(attn_dtype dtype, const void* q, const voi
                                       int max_kv_len, int split_pages, float scale,
                                       float k_scale, float v_scale, void* out, float* lse,
                                       void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_impl(dtype, true, 1, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
+  return decode_impl(dtype, true, 1, -1, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
                      page_size, num_pages, max_pages_per_req, max_kv_len, split_pages, scale,
                      k_scale, v_scale, out, lse, workspace, workspace_bytes, stream);
 }

@@ -155,6 +155,9 @@ __global__ __launch_bounds__(kNW * 64) void decode_split_kernel(DecodeParams p) 
   const size_t page_stride = (size_t)kPage * p.Hkv * D;
   const size_t lane_off = (size_t)kvh * (p.kv_hnd ? kPage * D : D) + gl * VPL;
   const int32_t* table = p.page_table + (size_t)b * p.max_pages;
+  // First key inside the sliding window (pages before it are still visited,
+  // their keys masked: the fp32 path serves short requests).
+  const int win_lo = p.window_left >= 0 ? len - 1 - p.window_left : 0;
 
   // Pages of this wave: first, first + NW, first + 2 NW, ...  A split holds
   // at most 64 * NW pages, so all of this wave's page ids fit in one VGPR
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_split_kernel(DecodeParams p) 
     float s[4][G];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const bool valid = tok0 + t < len;
+      const bool valid = tok0 + t < len && tok0 + t >= win_lo;
       if (!valid) bf.v[t].zero();   // poisoned tail slots must not reach o (0 * NaN)
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -350,10 +353,17 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) char lds_char;
 
+// First page holding a key inside the sliding window (0 without one).
+__device__ __forceinline__ int window_page0(const DecodeParams& p, int len) {
+  const int lo = p.window_left >= 0 ? len - 1 - p.window_left : 0;
+  return lo > 0 ? lo / kPage : 0;
+}
+
+// Pages of request b that hold keys the query sees (the schedule's units).
 __device__ __forceinline__ int pages_of(const DecodeParams& p, int b) {
   bool bad;
   const int len = request_len(p, b, bad);
-  return (len + kPage - 1) / kPage;
+  return (len + kPage - 1) / kPage - window_page0(p, len);
 }
 
 __device__ __forceinline__ int wave_incl_scan(int x) {
@@ -464,7 +474,14 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
       continue;
     }
     const bool whole = start_pair / W == (start_pair + np - 1) / W;
-    const int len = min(p.kv_lens[b], np * kPage);     // valid tokens (clamped, >= 1 page)
+    // Valid tokens (clamped) and the window: the piece's pages are counted
+    // from page p0, the first one the window reaches; keys before win_lo
+    // (relative to p0's first token) are masked.
+    bool bad_b;
+    const int len_b = request_len(p, b, bad_b);
+    const int p0 = window_page0(p, len_b);
+    const int len = min(p.kv_lens[b], (p0 + np) * kPage) - p0 * kPage;
+    const int win_lo = p.window_left >= 0 ? len_b - 1 - p.window_left - p0 * kPage : 0;
 
     // Q^T fragments: lane (head l16, k-group gq) holds q[head][32 ks + 8 gq .. +8]
     // (F8: q[head][64 (ks/2) + 16 gq + 8 (ks%2) .. +8], the order of its K chunks).
@@ -486,7 +503,7 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
     bool bad = false;
     const char* kh = kbase + (size_t)kvh * head_b;
     const char* vh = vbase + (size_t)kvh * head_b;
-    const int32_t* table = p.page_table + (size_t)b * p.max_pages + pg0;
+    const int32_t* table = p.page_table + (size_t)b * p.max_pages + p0 + pg0;
 
     for (int c0 = 0; c0 < n; c0 += 64) {
       const int nc = min(64, n - c0);
@@ -514,12 +531,13 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
           return;
         }
         const int nval = len - (pg0 + c0 + i) * kPage;   // valid tokens in this page
+        const int nlo = win_lo - (pg0 + c0 + i) * kPage;  // first one inside the window
         // V rows to LDS (rows past the end zeroed: poisoned slots must not reach O)
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
           const int ci = lane + 64 * j;
           const int t = ci / CHG, ch = ci % CHG;
-          const u32x4 v = t < nval ? pg.v[j] : u32x4{0u, 0u, 0u, 0u};
+          const u32x4 v = (t < nval && t >= nlo) ? pg.v[j] : u32x4{0u, 0u, 0u, 0u};
           if constexpr (F8) {
             // 16 bytes -> 16 elements, one 32-byte unit of the LDS row
             char* dst = myv + vpage_off<D>(t, ch * 16);
@@ -543,7 +561,7 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
         float mx = kNegInf;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const float v = 4 * gq + rr < nval ? s[rr] * c : kNegInf;
+          const float v = (4 * gq + rr < nval && 4 * gq + rr >= nlo) ? s[rr] * c : kNegInf;
           s[rr] = v;
           mx = fmaxf(mx, v);
         }

@@ -34,6 +34,9 @@ struct DecodeParams {
   float v_scale;           // E4M3 cache only: scale of the values
   // Page layout: 0 = NHD [page, slot, kv head, d], 1 = HND [page, kv head, slot, d].
   int kv_hnd;
+  // Sliding window: the query (the last token) sees keys kv_len-1-window_left
+  // .. kv_len-1; -1 = every key.
+  int window_left;
 };
 
 struct PrefillParams {

@@ -267,6 +267,22 @@ attn_status attn_merge_states(attn_dtype dtype, const void* o_a, const float* ls
                               float* lse_out, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Batched decode with a sliding window: the query (the request's last token)
+ * sees only keys kv_len-1-window_left .. kv_len-1 (window_left = -1: all,
+ * i.e. attn_decode_paged; other negative values return ATTN_E_VALUE).  With
+ * a 16-bit dtype the pages before the window are never read; with F32 their
+ * keys are masked.  kv_layout: 0 NHD, 1 HND pages.  Everything else, the
+ * workspace included, as attn_decode_paged.
+ */
+attn_status attn_decode_paged_window(attn_dtype dtype, int kv_layout, int window_left,
+                                     const void* q, const void* k_pages, const void* v_pages,
+                                     const int32_t* page_table, const int32_t* kv_lens, int B,
+                                     int Hq, int Hkv, int D, int page_size, int num_pages,
+                                     int max_pages_per_req, int max_kv_len, int split_pages,
+                                     float scale, void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Ragged and paged prefill with a sliding window (the window_size argument
  * of varlen_fwd in "FlashAttention-3 ..." section 二, left side): query i of
  * a sequence with Lq queries and Lk keys sees key j only if

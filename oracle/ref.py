@@ -113,12 +113,14 @@ def _check_heads(Hq: int, Hkv: int):
 
 
 def ref_decode_paged(q, k_pages, v_pages, page_table, kv_lens, scale,
-                     requests: Optional[Iterable[int]] = None):
+                     requests: Optional[Iterable[int]] = None, window_left: int = -1):
     """Decode: one query token per request over its paged KV (no mask).
 
     q [B, Hq, D]; pools [num_pages, P, Hkv, D]; page_table [B, max_pages];
     kv_lens [B].  Returns out [B, Hq, D] and lse [B, Hq] (float64).  With
-    ``requests`` only those rows are filled (the rest stay NaN).
+    ``requests`` only those rows are filled (the rest stay NaN).  With
+    window_left >= 0 the query (the last token, position kv_len - 1) sees only
+    keys kv_len - 1 - window_left .. kv_len - 1.
     """
     B, Hq, D = q.shape
     Hkv = k_pages.shape[2]
@@ -129,6 +131,9 @@ def ref_decode_paged(q, k_pages, v_pages, page_table, kv_lens, scale,
         L = int(kv_lens[b])
         k = gather_pages(k_pages, page_table[b], L)
         v = gather_pages(v_pages, page_table[b], L)
+        if window_left >= 0:
+            first = max(0, L - 1 - window_left)
+            k, v = k[first:], v[first:]
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
             o, l = softmax_attend(q[b, h:h + 1], k[:, g], v[:, g], scale)

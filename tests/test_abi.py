@@ -168,6 +168,23 @@ def test_window_rejects(lib):
                                          5, 64, 1, 3, 0.1, 16, 16, None) == E_VALUE   # layout 2
 
 
+def test_decode_window_rejects(lib):
+    def call(layout, w, **kw):
+        a = dict(dtype=1, q=16, k=16, v=16, t=16, lens=16, B=2, Hq=8, Hkv=2, D=128, P=16,
+                 num_pages=10, max_pages=4, mkv=64, split=0, scale=0.1, out=16, lse=16, ws=256,
+                 ws_bytes=1 << 20)
+        a.update(kw)
+        return lib.attn_decode_paged_window(a["dtype"], layout, w, a["q"], a["k"], a["v"], a["t"],
+                                            a["lens"], a["B"], a["Hq"], a["Hkv"], a["D"], a["P"],
+                                            a["num_pages"], a["max_pages"], a["mkv"], a["split"],
+                                            a["scale"], a["out"], a["lse"], a["ws"], a["ws_bytes"],
+                                            None)
+    assert call(0, -2) == E_VALUE
+    assert call(2, 5) == E_VALUE
+    assert call(0, 5, dtype=3) == E_DTYPE
+    assert call(0, 5, B=0, q=None) == OK
+
+
 def test_prefill_empty_is_noop(lib):
     assert _prefill(lib, B=0, q=None) == OK
     assert _prefill(lib, mq=0, q=None) == OK

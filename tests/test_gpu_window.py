@@ -109,3 +109,54 @@ def test_window_chunked_paged_config_sampled(gpu):
                                       case.page_table, case.kv_lens, True, case.scale, rows=rows,
                                       window_left=2048)
     assert_parity(out, lse, ro, rl, torch.bfloat16, "chunked paged window 2048 (sampled)", rows=rows)
+
+
+# ---------------------------------------------------------------- decode ---
+def _decode(case, gpu, window, layout="NHD", split_pages=0):
+    import attention_qk_online_amd as A
+    kp, vp = case.pools(gpu, layout=layout)
+    out, lse = A.decode_paged(case.q.to(gpu), kp, vp, case.page_table.to(gpu), case.kv_lens.to(gpu),
+                              scale=case.scale, max_kv_len=case.max_kv_len,
+                              split_pages=split_pages, kv_layout=layout, window_left=window)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv", [(torch.bfloat16, 128, 32, 8), (torch.bfloat16, 256, 16, 2),
+                                            (torch.float16, 64, 8, 8), (torch.float32, 128, 8, 2)])
+@pytest.mark.parametrize("split_pages", [0, 2])
+def test_decode_window(gpu, dtype, D, Hq, Hkv, split_pages):
+    lens = [1, 15, 16, 17, 300, 64, 1000, 0, 33]
+    case = workloads.make_decode(B=len(lens), Hq=Hq, Hkv=Hkv, D=D, page_size=16, kv_lens=lens,
+                                 dtype=dtype, seed=750 + D + Hq, extra_pages=4)
+    kp, vp = case.pools("cpu")
+    for window in (0, 5, 15, 16, 17, 100, 1000):
+        out, lse = _decode(case, gpu, window, split_pages=split_pages)
+        ro, rl = oracle.ref_decode_paged(case.q, kp, vp, case.page_table, case.kv_lens, case.scale,
+                                         window_left=window)
+        assert_parity(out, lse, ro, rl, dtype, f"decode {dtype} D{D} window {window}")
+
+
+def test_decode_window_hnd_and_wide(gpu):
+    """HND equals NHD bit for bit with a window; a window covering every key
+    equals the plain call bit for bit."""
+    case = workloads.make_decode(B=5, Hq=16, Hkv=4, D=128, page_size=16, kv_lens=[33, 400, 16, 1, 250],
+                                 dtype=torch.bfloat16, seed=760, extra_pages=3)
+    o1, l1 = _decode(case, gpu, 37, "NHD", 2)
+    o2, l2 = _decode(case, gpu, 37, "HND", 2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o3, l3 = _decode(case, gpu, -1, "NHD", 2)
+    o4, l4 = _decode(case, gpu, 400, "NHD", 2)
+    assert torch.equal(o3, o4) and torch.equal(l3, l4)
+
+
+def test_decode_window_paged_config(gpu):
+    """The batched paged GQA decode workload (B 64, Hq 32, Hkv 8, D 128) with a
+    1024-key window, every request against the oracle."""
+    case = workloads.make_decode(B=64, Hq=32, Hkv=8, D=128, page_size=16, len_range=(512, 4096),
+                                 dtype=torch.bfloat16, seed=2, num_pages=20000)
+    out, lse = _decode(case, gpu, 1024)
+    kp, vp = case.pools("cpu")
+    ro, rl = oracle.ref_decode_paged(case.q, kp, vp, case.page_table, case.kv_lens, case.scale,
+                                     window_left=1024)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, "paged decode window 1024")

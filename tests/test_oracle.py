@@ -383,11 +383,34 @@ def pin_window_brute_force(R):
     _close(o[3, 0], c.v[6, 0], 0.0)       # last row of sequence 0 sits on key 6
 
 
+def pin_decode_window(R):
+    """Decode with a window is the last row of a causal windowed prefill over the
+    same keys (one slices the keys, the other masks them), and a window of 0
+    returns the last value row."""
+    c = workloads.make_decode(B=3, Hq=4, Hkv=2, D=5, page_size=4, kv_lens=[9, 1, 6], dtype=F64,
+                              seed=41)
+    kp, vp = c.pools()
+    for left in (0, 3, 20):
+        o, l = R.ref_decode_paged(c.q, kp, vp, c.page_table, c.kv_lens, c.scale, window_left=left)
+        for b in range(3):
+            L = int(c.kv_lens[b])
+            kf = R.gather_pages(kp, c.page_table[b], L)
+            vf = R.gather_pages(vp, c.page_table[b], L)
+            qf = torch.zeros((L, 4, 5), dtype=F64)
+            qf[L - 1] = c.q[b]
+            of, lf = R.ref_prefill_varlen(qf, kf, vf, [0, L], [0, L], True, c.scale,
+                                          window_left=left)
+            _close(o[b], of[L - 1], 1e-13)
+            _close(l[b], lf[L - 1], 1e-13)
+            if left == 0:
+                _close(o[b, 0], vf[L - 1, 0], 0.0)
+
+
 PINS = [pin_golden, pin_brute_force, pin_sdpa_library, pin_single_key, pin_constant_v,
         pin_scale_zero_mean, pin_shift_invariance, pin_paging, pin_gqa_equals_repeated_mha,
         pin_causal_rows, pin_chunked_equals_full, pin_merge_partition, pin_empty_rows,
         pin_rows_subset, pin_fp8_decoder_library, pin_fp8_decode_equals_dequantised,
-        pin_window_brute_force]
+        pin_window_brute_force, pin_decode_window]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -410,6 +433,7 @@ MUTANTS = {
     "mask_strict": ("<= (rows.long().unsqueeze(1) + offset)", "< (rows.long().unsqueeze(1) + offset)"),
     "window_sign": ("(rows.long().unsqueeze(1) + offset - left)", "(rows.long().unsqueeze(1) - offset - left)"),
     "window_strict": (">= (rows.long().unsqueeze(1) + offset - left)", "> (rows.long().unsqueeze(1) + offset - left)"),
+    "decode_window_off_by_one": ("first = max(0, L - 1 - window_left)", "first = max(0, L - window_left)"),
     "window_ignored": ("            vis = w if vis is None else vis & w", "            vis = vis"),
     "fp8_exponent_bias": ("(e - 7).to(F64)", "(e - 8).to(F64)"),
     "fp8_subnormal_as_normal": ("mag = torch.where(e == 0, sub, norm)", "mag = norm"),
