@@ -416,7 +416,7 @@ KERNEL_SOURCES = {
     "decode_split": ["decode.hip"],
     "decode_fp8": ["decode.hip"],
     "prefill": ["prefill.hip"],
-    "prefill_paged": ["prefill.hip"],
+    "prefill_paged": ["prefill16.hip"],     # the chunked workload has head_dim 256
 }
 
 
