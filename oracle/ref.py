@@ -107,20 +107,41 @@ def gather_pages(pages: torch.Tensor, table_row: torch.Tensor, length: int) -> t
     return pages[ids, t % P]
 
 
+def rope_rotate(x: torch.Tensor, pos: torch.Tensor, theta: float, scale: float = 1.0) -> torch.Tensor:
+    """Rotary position embedding, rotate-half convention, in float64.
+
+    x [..., n, D] with positions pos [n]: pair (x_d, x_{d+D/2}), d < D/2, is
+    turned by the angle pos / scale * theta^(-2d/D).  ("FlashInfer内核库深度
+    解析" names dynamic RoPE in its single-request decode kernel without
+    fixing a convention; this is the rotate-half form.)
+    """
+    x = x.to(F64)
+    D = x.shape[-1]
+    h = D // 2
+    freq = torch.pow(torch.tensor(float(theta), dtype=F64), -2.0 * torch.arange(h, dtype=F64) / D)
+    ang = pos.to(F64).unsqueeze(-1) / scale * freq                     # [n, D/2]
+    c, s = torch.cos(ang), torch.sin(ang)
+    a, b = x[..., :h], x[..., h:]
+    return torch.cat([a * c - b * s, b * c + a * s], dim=-1)
+
+
 def _check_heads(Hq: int, Hkv: int):
     if Hkv <= 0 or Hq % Hkv != 0:
         raise ValueError(f"Hq={Hq} must be a positive multiple of Hkv={Hkv}")
 
 
 def ref_decode_paged(q, k_pages, v_pages, page_table, kv_lens, scale,
-                     requests: Optional[Iterable[int]] = None, window_left: int = -1):
+                     requests: Optional[Iterable[int]] = None, window_left: int = -1,
+                     rope: Optional[Tuple[float, float]] = None):
     """Decode: one query token per request over its paged KV (no mask).
 
     q [B, Hq, D]; pools [num_pages, P, Hkv, D]; page_table [B, max_pages];
     kv_lens [B].  Returns out [B, Hq, D] and lse [B, Hq] (float64).  With
     ``requests`` only those rows are filled (the rest stay NaN).  With
     window_left >= 0 the query (the last token, position kv_len - 1) sees only
-    keys kv_len - 1 - window_left .. kv_len - 1.
+    keys kv_len - 1 - window_left .. kv_len - 1.  With rope = (theta, scale)
+    the query (position kv_len - 1) and the keys (their token index) are
+    rotated by :func:`rope_rotate` first.
     """
     B, Hq, D = q.shape
     Hkv = k_pages.shape[2]
@@ -131,12 +152,16 @@ def ref_decode_paged(q, k_pages, v_pages, page_table, kv_lens, scale,
         L = int(kv_lens[b])
         k = gather_pages(k_pages, page_table[b], L)
         v = gather_pages(v_pages, page_table[b], L)
+        qb = q[b]
+        if rope is not None:
+            k = rope_rotate(k.transpose(0, 1), torch.arange(L), *rope).transpose(0, 1)
+            qb = rope_rotate(q[b].unsqueeze(1), torch.tensor([L - 1]), *rope).squeeze(1)
         if window_left >= 0:
             first = max(0, L - 1 - window_left)
             k, v = k[first:], v[first:]
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
-            o, l = softmax_attend(q[b, h:h + 1], k[:, g], v[:, g], scale)
+            o, l = softmax_attend(qb[h:h + 1], k[:, g], v[:, g], scale)
             out[b, h] = o[0]
             lse[b, h] = l[0]
     return out, lse

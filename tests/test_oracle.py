@@ -25,7 +25,8 @@ F64 = torch.float64
 
 
 def _ev(x):
-    env = {"log": math.log, "sqrt": math.sqrt, "nan": math.nan, "inf": math.inf}
+    env = {"log": math.log, "sqrt": math.sqrt, "nan": math.nan, "inf": math.inf,
+           "exp": math.exp, "cos": math.cos, "sin": math.sin}
     if isinstance(x, str) and x.strip() == "-0":
         return -0.0
     return float(eval(x, {"__builtins__": {}}, env)) if isinstance(x, str) else float(x)
@@ -74,6 +75,11 @@ def pin_golden(R):
                                           _ev(g["k_scale"]), _ev(g["v_scale"]),
                                           torch.tensor(g["page_table"]), torch.tensor(g["kv_lens"]),
                                           _ev(g["scale"]))
+        elif g["kind"] == "decode_rope":
+            o, l = R.ref_decode_paged(_tensor(g["q"]), _tensor(g["k_pages"]), _tensor(g["v_pages"]),
+                                      torch.tensor(g["page_table"]), torch.tensor(g["kv_lens"]),
+                                      _ev(g["scale"]),
+                                      rope=(_ev(g["rope_theta"]), _ev(g["rope_scale"])))
         elif g["kind"] == "decode":
             o, l = R.ref_decode_paged(_tensor(g["q"]), _tensor(g["k_pages"]), _tensor(g["v_pages"]),
                                       torch.tensor(g["page_table"]), torch.tensor(g["kv_lens"]),
@@ -406,11 +412,51 @@ def pin_decode_window(R):
                 _close(o[b, 0], vf[L - 1, 0], 0.0)
 
 
+def pin_rope(R):
+    """rope_rotate against complex multiplication (library complex128), its
+    relative-position property, norm preservation and position 0; decode with
+    rope equals plain decode on pre-rotated q and keys."""
+    g = torch.Generator().manual_seed(42)
+    x = torch.randn((3, 5, 8), generator=g, dtype=F64)
+    pos = torch.tensor([0.0, 1.0, 7.0, 100.0, 4095.0], dtype=F64)
+    theta, scale = 500.0, 2.0
+    y = R.rope_rotate(x, pos, theta, scale)
+    freq = theta ** (-2.0 * torch.arange(4, dtype=F64) / 8)
+    z = torch.complex(x[..., :4], x[..., 4:]) * torch.polar(torch.ones(5, 4, dtype=F64),
+                                                            pos.unsqueeze(1) / scale * freq)
+    _close(y, torch.cat([z.real, z.imag], dim=-1), 1e-12)
+    _close(y.norm(dim=-1), x.norm(dim=-1), 1e-12)
+    _close(y[:, 0], x[:, 0], 0.0)
+    q, k = x[0, :1], x[1, :1]
+    for m, n, dl in ((3.0, 1.0, 10.0), (50.0, 70.0, -20.0)):
+        a = (R.rope_rotate(q, torch.tensor([m]), theta) * R.rope_rotate(k, torch.tensor([n]), theta)).sum()
+        b = (R.rope_rotate(q, torch.tensor([m + dl]), theta) *
+             R.rope_rotate(k, torch.tensor([n + dl]), theta)).sum()
+        assert abs(float(a - b)) < 1e-12
+    c = workloads.make_decode(B=2, Hq=4, Hkv=2, D=8, page_size=4, kv_lens=[6, 3], dtype=F64, seed=43)
+    kp, vp = c.pools()
+    o, l = R.ref_decode_paged(c.q, kp, vp, c.page_table, c.kv_lens, c.scale, rope=(theta, scale))
+    for b in range(2):
+        L = int(c.kv_lens[b])
+        kf = R.gather_pages(kp, c.page_table[b], L)
+        vf = R.gather_pages(vp, c.page_table[b], L)
+        zk = torch.complex(kf[..., :4], kf[..., 4:]) * torch.polar(
+            torch.ones(L, 1, 4, dtype=F64), torch.arange(L, dtype=F64).view(L, 1, 1) / scale * freq)
+        zq = torch.complex(c.q[b][..., :4], c.q[b][..., 4:]) * torch.polar(
+            torch.ones(4, 4, dtype=F64), torch.full((4, 1), (L - 1) / scale, dtype=F64) * freq)
+        kr = torch.cat([zk.real, zk.imag], dim=-1)
+        qr = torch.cat([zq.real, zq.imag], dim=-1)
+        for h in range(4):
+            of, lf = R.softmax_attend(qr[h:h + 1], kr[:, h // 2], vf[:, h // 2], c.scale)
+            _close(o[b, h], of[0], 1e-12)
+            _close(l[b, h], lf[0], 1e-12)
+
+
 PINS = [pin_golden, pin_brute_force, pin_sdpa_library, pin_single_key, pin_constant_v,
         pin_scale_zero_mean, pin_shift_invariance, pin_paging, pin_gqa_equals_repeated_mha,
         pin_causal_rows, pin_chunked_equals_full, pin_merge_partition, pin_empty_rows,
         pin_rows_subset, pin_fp8_decoder_library, pin_fp8_decode_equals_dequantised,
-        pin_window_brute_force, pin_decode_window]
+        pin_window_brute_force, pin_decode_window, pin_rope]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -434,6 +480,10 @@ MUTANTS = {
     "window_sign": ("(rows.long().unsqueeze(1) + offset - left)", "(rows.long().unsqueeze(1) - offset - left)"),
     "window_strict": (">= (rows.long().unsqueeze(1) + offset - left)", "> (rows.long().unsqueeze(1) + offset - left)"),
     "decode_window_off_by_one": ("first = max(0, L - 1 - window_left)", "first = max(0, L - window_left)"),
+    "rope_turn_sign": ("return torch.cat([a * c - b * s, b * c + a * s], dim=-1)",
+                       "return torch.cat([a * c + b * s, b * c - a * s], dim=-1)"),
+    "rope_freq_exponent": ("-2.0 * torch.arange(h, dtype=F64) / D", "-1.0 * torch.arange(h, dtype=F64) / D"),
+    "rope_query_position": ("torch.tensor([L - 1]), *rope)", "torch.tensor([L]), *rope)"),
     "window_ignored": ("            vis = w if vis is None else vis & w", "            vis = vis"),
     "fp8_exponent_bias": ("(e - 7).to(F64)", "(e - 8).to(F64)"),
     "fp8_subnormal_as_normal": ("mag = torch.where(e == 0, sub, norm)", "mag = norm"),
