@@ -102,6 +102,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_decode_paged_window.restype = c_int
     lib.attn_decode_paged_window.argtypes = [c_int, c_int, c_int, vp, vp, vp, vp, vp] + [c_int] * 9 + [
         c_float, vp, vp, vp, c_size, vp]
+    lib.attn_decode_paged_rope.restype = c_int
+    lib.attn_decode_paged_rope.argtypes = [c_int, c_int, c_int, c_float, c_float, vp, vp, vp, vp,
+                                           vp] + [c_int] * 9 + [c_float, vp, vp, vp, c_size, vp]
     lib.attn_prefill_varlen_window.restype = c_int
     lib.attn_prefill_varlen_window.argtypes = [c_int, vp, vp, vp, vp, vp] + [c_int] * 10 + [
         c_float, vp, vp, vp]
@@ -198,7 +201,7 @@ def decode_paged_workspace_size(dtype: torch.dtype, B: int, Hq: int, Hkv: int, D
 
 
 def _decode(q, k_pages, v_pages, page_table, kv_lens, scale, max_kv_len, split_pages, out, lse,
-            workspace, fp8_scales=None, kv_layout="NHD", window_left=-1):
+            workspace, fp8_scales=None, kv_layout="NHD", window_left=-1, rope=None):
     lib = load_library()
     suffix = _layout(kv_layout)
     dt = _dtype_code(q)
@@ -235,7 +238,12 @@ def _decode(q, k_pages, v_pages, page_table, kv_lens, scale, max_kv_len, split_p
             max_kv_len, split_pages, s)
     tail = (out.data_ptr(), lse.data_ptr(), pw, workspace.numel() * workspace.element_size(),
             _stream(q.device))
-    if window_left != -1:
+    if rope is not None:
+        if fp8_scales is not None:
+            raise ValueError("the rotary embedding is not built for the E4M3 cache")
+        _check(lib.attn_decode_paged_rope(dt, 1 if suffix else 0, int(window_left),
+                                          float(rope[0]), float(rope[1]), *args, *tail))
+    elif window_left != -1:
         if fp8_scales is not None:
             raise ValueError("a sliding window is not built for the E4M3 cache")
         _check(lib.attn_decode_paged_window(dt, 1 if suffix else 0, int(window_left), *args,
@@ -253,9 +261,12 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
                  max_kv_len: Optional[int] = None, split_pages: int = 0,
                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None, kv_layout: str = "NHD",
-                 window_left: int = -1) -> Tuple[torch.Tensor, torch.Tensor]:
+                 window_left: int = -1, rope_theta: Optional[float] = None,
+                 rope_scale: float = 1.0) -> Tuple[torch.Tensor, torch.Tensor]:
     """Batched decode over a paged KV cache (``window_left`` >= 0: the query sees
-    only the last window_left + 1 keys).
+    only the last window_left + 1 keys; ``rope_theta``: rotate q (position
+    kv_len - 1) and the keys (their token index) in the kernel, rotate-half
+    convention, angle position / rope_scale * rope_theta^(-2d/D)).
 
     q [B, Hq, D]; k_pages, v_pages [num_pages, page_size, Hkv, D] (NHD) or
     [num_pages, Hkv, page_size, D] (``kv_layout="HND"``); page_table
@@ -264,7 +275,8 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
     device-to-host copy.  Returns (out [B, Hq, D], lse [B, Hq] float32).
     """
     return _decode(q, k_pages, v_pages, page_table, kv_lens, scale, max_kv_len, split_pages, out,
-                   lse, workspace, kv_layout=kv_layout, window_left=window_left)
+                   lse, workspace, kv_layout=kv_layout, window_left=window_left,
+                   rope=None if rope_theta is None else (rope_theta, rope_scale))
 
 
 def decode_paged_fp8(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,

@@ -174,7 +174,7 @@ size_t attn_decode_paged_workspace_size(attn_dtype dtype, int B, int Hq, int Hkv
 // Both decode entry points; fp8_kv: the pages hold E4M3 bytes with scales
 // k_scale / v_scale.
 static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int window_left,
-                               const void* q,
+                               bool rope, float rope_theta, float rope_scale, const void* q,
                                const void* k_pages,
                                const void* v_pages, const int32_t* page_table,
                                const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
@@ -189,6 +189,12 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int wi
   if (fp8_kv && (!std::isfinite(k_scale) || !std::isfinite(v_scale)))
     return fail(ATTN_E_VALUE, "k_scale / v_scale not finite");
   if (window_left < -1) return fail(ATTN_E_VALUE, "window_left=%d (-1 = no window)", window_left);
+  if (rope && !(std::isfinite(rope_theta) && rope_theta > 0.f && std::isfinite(rope_scale) &&
+                rope_scale > 0.f))
+    return fail(ATTN_E_VALUE, "rope_theta / rope_scale must be finite and positive");
+  if (rope && (dtype == ATTN_F32 || (D != 64 && D != 128)))
+    return fail(ATTN_E_UNSUPPORTED, "rotary decode: dtype=%d D=%d not built (bf16/f16, D 64 or 128)",
+                dtype, D);
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || num_pages < 0 ||
       max_pages_per_req < 0 || max_kv_len < 0 || split_pages < 0)
     return fail(ATTN_E_SHAPE,
@@ -237,10 +243,12 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int wi
   p.v_scale = fp8_kv ? v_scale : 1.f;
   p.kv_hnd = kv_hnd;
   p.window_left = window_left;
+  p.rope_log2_theta = rope ? std::log2(rope_theta) : 0.f;
+  p.rope_inv_scale = rope ? 1.f / rope_scale : 1.f;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = timed(ATTN_KERNEL_DECODE_SPLIT, s,
-                       [&] { return attn::launch_decode_split(p, (int)dtype, D, G, fp8_kv, s); });
+                       [&] { return attn::launch_decode_split(p, (int)dtype, D, G, fp8_kv, rope, s); });
   if (e != hipSuccess)
     return fail(ATTN_E_HIP, "decode_split launch: %s", hipGetErrorString(e));
   if (dtype != ATTN_F32 || pl.n_splits > 1) {
@@ -259,7 +267,8 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pag
                               int max_kv_len, int split_pages, float scale, void* out,
                               float* lse, void* workspace, size_t workspace_bytes,
                               void* stream) {
-  return decode_impl(dtype, false, 0, -1, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
+  return decode_impl(dtype, false, 0, -1, false, 0.f, 0.f, q, k_pages, v_pages, page_table,
+                     kv_lens, B, Hq, Hkv, D,
                      page_size, num_pages, max_pages_per_req, max_kv_len, split_pages, scale, 1.f,
                      1.f, out, lse, workspace, workspace_bytes, stream);
 }
@@ -271,7 +280,8 @@ attn_status attn_decode_paged_hnd(attn_dtype dtype, const void* q, const void* k
                                   int max_kv_len, int split_pages, float scale, void* out,
                                   float* lse, void* workspace, size_t workspace_bytes,
                                   void* stream) {
-  return decode_impl(dtype, false, 1, -1, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
+  return decode_impl(dtype, false, 1, -1, false, 0.f, 0.f, q, k_pages, v_pages, page_table,
+                     kv_lens, B, Hq, Hkv, D,
                      page_size, num_pages, max_pages_per_req, max_kv_len, split_pages, scale, 1.f,
                      1.f, out, lse, workspace, workspace_bytes, stream);
 }
@@ -283,7 +293,8 @@ attn_status attn_decode_paged_fp8(attn_dtype dtype, const void* q, const void* k
                                   int max_kv_len, int split_pages, float scale, float k_scale,
                                   float v_scale, void* out, float* lse, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  return decode_impl(dtype, true, 0, -1, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
+  return decode_impl(dtype, true, 0, -1, false, 0.f, 0.f, q, k_pages, v_pages, page_table,
+                     kv_lens, B, Hq, Hkv, D,
                      page_size, num_pages, max_pages_per_req, max_kv_len, split_pages, scale,
                      k_scale, v_scale, out, lse, workspace, workspace_bytes, stream);
 }
@@ -298,9 +309,27 @@ attn_status attn_decode_paged_window(attn_dtype dtype, int kv_layout, int window
   g_last_error[0] = 0;
   if (kv_layout != 0 && kv_layout != 1)
     return fail(ATTN_E_VALUE, "kv_layout=%d (0 = NHD, 1 = HND)", kv_layout);
-  return decode_impl(dtype, false, kv_layout, window_left, q, k_pages, v_pages, page_table,
+  return decode_impl(dtype, false, kv_layout, window_left, false, 0.f, 0.f, q, k_pages, v_pages,
+                     page_table,
                      kv_lens, B, Hq, Hkv, D, page_size, num_pages, max_pages_per_req, max_kv_len,
                      split_pages, scale, 1.f, 1.f, out, lse, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_paged_rope(attn_dtype dtype, int kv_layout, int window_left,
+                                   float rope_theta, float rope_scale, const void* q,
+                                   const void* k_pages, const void* v_pages,
+                                   const int32_t* page_table, const int32_t* kv_lens, int B, int Hq,
+                                   int Hkv, int D, int page_size, int num_pages,
+                                   int max_pages_per_req, int max_kv_len, int split_pages,
+                                   float scale, void* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (kv_layout != 0 && kv_layout != 1)
+    return fail(ATTN_E_VALUE, "kv_layout=%d (0 = NHD, 1 = HND)", kv_layout);
+  return decode_impl(dtype, false, kv_layout, window_left, true, rope_theta, rope_scale, q,
+                     k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D, page_size, num_pages,
+                     max_pages_per_req, max_kv_len, split_pages, scale, 1.f, 1.f, out, lse,
+                     workspace, workspace_bytes, stream);
 }
 
 attn_status attn_decode_paged_fp8_hnd(attn_dtype dtype, const void* q, const void* k_pages,
@@ -310,7 +339,8 @@ attn_status attn_decode_paged_fp8_hnd(attn_dtype dtype, const void* q, const voi
                                       int max_kv_len, int split_pages, float scale,
                                       float k_scale, float v_scale, void* out, float* lse,
                                       void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_impl(dtype, true, 1, -1, q, k_pages, v_pages, page_table, kv_lens, B, Hq, Hkv, D,
+  return decode_impl(dtype, true, 1, -1, false, 0.f, 0.f, q, k_pages, v_pages, page_table,
+                     kv_lens, B, Hq, Hkv, D,
                      page_size, num_pages, max_pages_per_req, max_kv_len, split_pages, scale,
                      k_scale, v_scale, out, lse, workspace, workspace_bytes, stream);
 }

@@ -412,9 +412,10 @@ __device__ __forceinline__ typename H::v8 fp8x8(uint32_t w0, uint32_t w1) {
 // group of hw KV heads; wave w of the workgroup folds KV head hg * hw + w of
 // every unit, so a workgroup reads whole pages (all heads of a token are
 // adjacent in the NHD layout).
-template <typename E, int D, int G, int NB, bool F8>
+template <typename E, int D, int G, int NB, bool F8, bool RP>
 __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1, int W, int lane,
                                            int wave) {
+  static_assert(!(RP && F8), "rotary embedding on the 16-bit cache only");
   using C = MfmaDecodeCfg<D>;
   constexpr int GROWB = F8 ? D : 2 * D;                  // bytes of one K/V row in the cache
   constexpr int NK = F8 ? C::KS / 2 : C::KS;             // 16-byte K loads per lane per page
@@ -496,6 +497,25 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
         qf[ks] = l16 < G ? v : typename H::v8{};
       }
     }
+    // Rotary embedding: lane pair j = (k-step j / 8 < KS/2, element j % 8)
+    // holds d = 32 (j / 8) + 8 gq + j % 8 in qf[j / 8] and d + D/2 in
+    // qf[j / 8 + KS/2] (likewise for K), so each lane turns its own pairs.
+    constexpr int NR = RP ? C::KS / 2 * 8 : 1;
+    float rf[NR], rc[NR], rs[NR], tc[NR], ts[NR];
+    if constexpr (RP) {
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        const int d = 32 * (j / 8) + 8 * gq + j % 8;
+        rf[j] = exp2f(-(float)(2 * d) / D * p.rope_log2_theta) * p.rope_inv_scale;
+        float sq, cq;
+        sincosf((float)(len_b - 1) * rf[j], &sq, &cq);
+        const int ks = j / 8, e = j % 8;
+        const float x = (float)qf[ks][e], y = (float)qf[ks + C::KS / 2][e];
+        qf[ks][e] = (elem)(x * cq - y * sq);
+        qf[ks + C::KS / 2][e] = (elem)(y * cq + x * sq);
+        sincosf(16.f * rf[j], &ts[j], &tc[j]);      // one page further on
+      }
+    }
     f32x4 o[C::DB];
 #pragma unroll
     for (int i = 0; i < C::DB; ++i) o[i] = f32x4{};
@@ -508,6 +528,13 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
     for (int c0 = 0; c0 < n; c0 += 64) {
       const int nc = min(64, n - c0);
       const int ids = lane < nc ? table[c0 + lane] : 0;
+      if constexpr (RP) {
+        // Angle of this lane's key (token l16 of the page) at the first page of
+        // the chunk, exact; later pages advance it by a 16-token rotation.
+        const float pos = (float)((p0 + pg0 + c0) * kPage + l16);
+#pragma unroll
+        for (int j = 0; j < NR; ++j) sincosf(pos * rf[j], &rs[j], &rc[j]);
+      }
       auto fetch = [&](int i, Page& pg) {
         int pid = __builtin_amdgcn_readlane(ids, i);
         pg.ok = (unsigned)pid < (unsigned)p.num_pages;
@@ -547,17 +574,30 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
             *reinterpret_cast<u32x4*>(myv + vpage_off<D>(t, ch * 8)) = v;
           }
         }
-        f32x4 s = {};
+        typename H::v8 kfr[C::KS];
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-          typename H::v8 kf;
           if constexpr (F8)
-            kf = ks % 2 == 0 ? fp8x8<H>(pg.k[ks / 2][0], pg.k[ks / 2][1])
-                             : fp8x8<H>(pg.k[ks / 2][2], pg.k[ks / 2][3]);
+            kfr[ks] = ks % 2 == 0 ? fp8x8<H>(pg.k[ks / 2][0], pg.k[ks / 2][1])
+                                  : fp8x8<H>(pg.k[ks / 2][2], pg.k[ks / 2][3]);
           else
-            kf = __builtin_bit_cast(typename H::v8, pg.k[ks]);
-          s = H::mfma16x16x32(kf, qf[ks], s);
+            kfr[ks] = __builtin_bit_cast(typename H::v8, pg.k[ks]);
         }
+        if constexpr (RP) {
+#pragma unroll
+          for (int j = 0; j < NR; ++j) {
+            const int ks = j / 8, e = j % 8;
+            const float x = (float)kfr[ks][e], y = (float)kfr[ks + C::KS / 2][e];
+            kfr[ks][e] = (elem)(x * rc[j] - y * rs[j]);
+            kfr[ks + C::KS / 2][e] = (elem)(y * rc[j] + x * rs[j]);
+            const float c2 = rc[j] * tc[j] - rs[j] * ts[j];
+            rs[j] = rs[j] * tc[j] + rc[j] * ts[j];
+            rc[j] = c2;
+          }
+        }
+        f32x4 s = {};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) s = H::mfma16x16x32(kfr[ks], qf[ks], s);
         float mx = kNegInf;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -659,7 +699,7 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
   }
 }
 
-template <typename E, int D, int G, int NB, bool F8>
+template <typename E, int D, int G, int NB, bool F8, bool RP>
 __global__ __launch_bounds__(kMaxGroupWaves * 64, D == 256 ? 1 : 2) void decode_mfma_kernel(DecodeParams p) {
   static_assert(G >= 1 && G <= 16, "one 16-column MFMA tile holds the query heads");
   const int lane = threadIdx.x & 63;
@@ -668,7 +708,7 @@ __global__ __launch_bounds__(kMaxGroupWaves * 64, D == 256 ? 1 : 2) void decode_
   const int U = total_units(p);
   const int W = run_length(p, U);
   for (int run = blockIdx.x; (long)run * W < U; run += gridDim.x) {
-    decode_run<E, D, G, NB, F8>(p, run * W, min(run * W + W, U), W, lane, wave);
+    decode_run<E, D, G, NB, F8, RP>(p, run * W, min(run * W + W, U), W, lane, wave);
   }
 }
 
@@ -788,15 +828,22 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
 }
 
 template <typename T, int D, int G>
-hipError_t launch_split_t(const DecodeParams& p, bool fp8, hipStream_t s) {
+hipError_t launch_split_t(const DecodeParams& p, bool fp8, bool rope, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     if (fp8)
-      hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, (D == 256 ? 1 : kFp8Batch), true>),
+      hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, (D == 256 ? 1 : kFp8Batch), true, false>),
                          dim3(p.n_groups), dim3(p.hw * 64), 0, s, p);
-    else
-      hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, (D == 256 ? 1 : kMfmaBatch), false>),
+    else if (rope) {
+      if constexpr (D <= 128)
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, kMfmaBatch, false, true>),
+                           dim3(p.n_groups), dim3(p.hw * 64), 0, s, p);
+      else
+        return hipErrorInvalidValue;
+    } else
+      hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, (D == 256 ? 1 : kMfmaBatch), false, false>),
                          dim3(p.n_groups), dim3(p.hw * 64), 0, s, p);
   } else {
+    if (fp8 || rope) return hipErrorInvalidValue;
     hipLaunchKernelGGL((decode_split_kernel<T, D, G, kBatch>), dim3(p.n_splits, p.Hkv, p.B),
                        dim3(kNW * 64), 0, s, p);
   }
@@ -804,23 +851,23 @@ hipError_t launch_split_t(const DecodeParams& p, bool fp8, hipStream_t s) {
 }
 
 template <typename T, int D>
-hipError_t launch_split_g(const DecodeParams& p, int G, bool fp8, hipStream_t s) {
+hipError_t launch_split_g(const DecodeParams& p, int G, bool fp8, bool rope, hipStream_t s) {
   switch (G) {
-    case 1: return launch_split_t<T, D, 1>(p, fp8, s);
-    case 2: return launch_split_t<T, D, 2>(p, fp8, s);
-    case 4: return launch_split_t<T, D, 4>(p, fp8, s);
-    case 8: return launch_split_t<T, D, 8>(p, fp8, s);
+    case 1: return launch_split_t<T, D, 1>(p, fp8, rope, s);
+    case 2: return launch_split_t<T, D, 2>(p, fp8, rope, s);
+    case 4: return launch_split_t<T, D, 4>(p, fp8, rope, s);
+    case 8: return launch_split_t<T, D, 8>(p, fp8, rope, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
-hipError_t launch_split_d(const DecodeParams& p, int D, int G, bool fp8, hipStream_t s) {
+hipError_t launch_split_d(const DecodeParams& p, int D, int G, bool fp8, bool rope, hipStream_t s) {
   switch (D) {
-    case 64: return launch_split_g<T, 64>(p, G, fp8, s);
-    case 128: return launch_split_g<T, 128>(p, G, fp8, s);
+    case 64: return launch_split_g<T, 64>(p, G, fp8, rope, s);
+    case 128: return launch_split_g<T, 128>(p, G, fp8, rope, s);
     case 256:
-      if constexpr (sizeof(T) == 2) return launch_split_g<T, 256>(p, G, fp8, s);
+      if constexpr (sizeof(T) == 2) return launch_split_g<T, 256>(p, G, fp8, rope, s);
       break;
   }
   return hipErrorInvalidValue;
@@ -856,10 +903,11 @@ bool decode_supported(int dtype, int D, int G, int page_size) {
 }
 
 hipError_t launch_decode_split(const DecodeParams& p, int dtype, int D, int G, bool fp8_kv,
-                               hipStream_t s) {
-  if (dtype == 0) return fp8_kv ? hipErrorInvalidValue : launch_split_d<float>(p, D, G, false, s);
-  return dtype == 1 ? launch_split_d<bf16_t>(p, D, G, fp8_kv, s)
-                    : launch_split_d<f16_t>(p, D, G, fp8_kv, s);
+                               bool rope, hipStream_t s) {
+  if (dtype == 0)
+    return (fp8_kv || rope) ? hipErrorInvalidValue : launch_split_d<float>(p, D, G, false, false, s);
+  return dtype == 1 ? launch_split_d<bf16_t>(p, D, G, fp8_kv, rope, s)
+                    : launch_split_d<f16_t>(p, D, G, fp8_kv, rope, s);
 }
 
 hipError_t launch_decode_combine(const DecodeParams& p, int dtype, int D, int G, hipStream_t s) {

@@ -37,6 +37,10 @@ struct DecodeParams {
   // Sliding window: the query (the last token) sees keys kv_len-1-window_left
   // .. kv_len-1; -1 = every key.
   int window_left;
+  // Rotary position embedding applied in the kernel to q (position kv_len-1)
+  // and to each key (its token index): pairs (d, d + D/2) turned by the angle
+  // position * rope_inv_scale * 2^(-2 d / D * log2(theta)).
+  float rope_log2_theta, rope_inv_scale;
 };
 
 struct PrefillParams {
@@ -74,9 +78,10 @@ struct PrefillParams {
 
 // dtype: 0 = f32, 1 = bf16, 2 = f16 (values of attn_dtype).
 bool decode_supported(int dtype, int D, int G, int page_size);
-// fp8_kv: K/V pages are E4M3 bytes (16-bit dtype only).
+// fp8_kv: K/V pages are E4M3 bytes (16-bit dtype only); rope: rotary
+// embedding of q and k in the kernel (16-bit dtype, D 64 or 128, not fp8_kv).
 hipError_t launch_decode_split(const DecodeParams& p, int dtype, int D, int G, bool fp8_kv,
-                               hipStream_t s);
+                               bool rope, hipStream_t s);
 hipError_t launch_decode_combine(const DecodeParams& p, int dtype, int D, int G, hipStream_t s);
 // Workgroups (of up to 8 waves, one per KV head) per CU in the balanced bf16 grid.
 #ifndef ATTN_DECODE_GROUPS_PER_CU

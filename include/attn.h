@@ -283,6 +283,28 @@ attn_status attn_decode_paged_window(attn_dtype dtype, int kv_layout, int window
                                      size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Batched decode with the rotary position embedding applied in the kernel
+ * (the dynamic RoPE of FlashInfer's single-request decode, "FlashInfer内核库
+ * 深度解析", decode kernels), for caches that hold keys before rotation.
+ * The query is at position kv_len - 1, key t at position t.  Each pair
+ * (x_d, x_{d+D/2}), d < D/2, of q and of every key is turned by the angle
+ *   position / rope_scale * rope_theta^(-2 d / D)
+ * (x_d cos - x_{d+D/2} sin, x_{d+D/2} cos + x_d sin) -- the rotate-half
+ * convention -- and rounded to the input type before the products.
+ * rope_theta, rope_scale: finite and positive (else ATTN_E_VALUE).
+ * Supported: BF16 / F16, D 64 or 128 (else ATTN_E_UNSUPPORTED); kv_layout,
+ * window_left and everything else as attn_decode_paged_window.
+ */
+attn_status attn_decode_paged_rope(attn_dtype dtype, int kv_layout, int window_left,
+                                   float rope_theta, float rope_scale, const void* q,
+                                   const void* k_pages, const void* v_pages,
+                                   const int32_t* page_table, const int32_t* kv_lens, int B, int Hq,
+                                   int Hkv, int D, int page_size, int num_pages,
+                                   int max_pages_per_req, int max_kv_len, int split_pages,
+                                   float scale, void* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Ragged and paged prefill with a sliding window (the window_size argument
  * of varlen_fwd in "FlashAttention-3 ..." section 二, left side): query i of
  * a sequence with Lq queries and Lk keys sees key j only if

@@ -185,6 +185,26 @@ def test_decode_window_rejects(lib):
     assert call(0, 5, B=0, q=None) == OK
 
 
+def test_rope_rejects(lib):
+    def call(theta=10000.0, scale=1.0, **kw):
+        a = dict(dtype=1, layout=0, w=-1, q=16, k=16, v=16, t=16, lens=16, B=2, Hq=8, Hkv=2, D=128,
+                 P=16, num_pages=10, max_pages=4, mkv=64, split=0, scale=0.1, out=16, lse=16,
+                 ws=256, ws_bytes=1 << 20)
+        a.update(kw)
+        return lib.attn_decode_paged_rope(a["dtype"], a["layout"], a["w"], theta, scale, a["q"],
+                                          a["k"], a["v"], a["t"], a["lens"], a["B"], a["Hq"],
+                                          a["Hkv"], a["D"], a["P"], a["num_pages"], a["max_pages"],
+                                          a["mkv"], a["split"], a["scale"], a["out"], a["lse"],
+                                          a["ws"], a["ws_bytes"], None)
+    assert call(theta=0.0) == E_VALUE
+    assert call(theta=float("nan")) == E_VALUE
+    assert call(scale=-1.0) == E_VALUE
+    assert call(D=256) == E_UNSUP
+    assert call(dtype=0) == E_UNSUP
+    assert call(layout=3) == E_VALUE
+    assert call(B=0, q=None) == OK
+
+
 def test_prefill_empty_is_noop(lib):
     assert _prefill(lib, B=0, q=None) == OK
     assert _prefill(lib, mq=0, q=None) == OK
