@@ -19,7 +19,8 @@ in HBM but not in the MALL or the L2s.  Call times come from one event
 pair per segment of the timed steps (mean, median and minimum); per-kernel
 durations (the roofline figures) from a second pass in which the library
 records HIP events around each of its launches on the launch stream.  Also
-reported: the decode workload over an E4M3 (fp8) copy of its cache, the
+reported: the decode workload over an E4M3 (fp8) copy of its cache and
+with the rotary position embedding, the
 chunked workload through the shared-prefix cascade, the launch-bound fp32
 single-sequence decode and the 1K-32K single-sequence
 causal prefill sweep.  The CPU oracle is timed on the host
@@ -27,7 +28,8 @@ cores over the whole decode workload (repeated to at least ~10 s), as a
 reported baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-flush]
-                       [--no-cpu-baseline] [--no-cascade] [--no-fp8] [--calibrate-copy MIB]
+                       [--no-cpu-baseline] [--no-cascade] [--no-fp8] [--no-rope]
+                       [--calibrate-copy MIB]
 Prints one JSON line.
 """
 import argparse
@@ -62,6 +64,7 @@ def main():
                     help="skip the shared-prefix cascade timing (its kernels share a name with "
                          "the direct paged prefill, so profiles of the latter skip it)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the E4M3-cache decode timing")
+    ap.add_argument("--no-rope", action="store_true", help="skip the rotary-embedding decode timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="finish with three plain device-to-device copies of MIB MiB, the "
@@ -265,6 +268,41 @@ def main():
         log("bench: fp8 decode", res["decode_fp8"])
         del f_kp, f_vp
 
+    # The decode workload with the rotary position embedding (theta 10000)
+    # applied to the query and to every cached key inside the kernel: the
+    # same bytes as the plain decode, more arithmetic per page.
+    if not args.no_rope:
+        def decode_rope():
+            A.decode_paged(d_q, d_kp, d_vp, d_table, d_lens, scale=dec.scale,
+                           max_kv_len=dec.max_kv_len, out=d_out, lse=d_lse, workspace=d_ws,
+                           rope_theta=10000.0)
+        for _ in range(3):
+            decode_rope()
+        torch.cuda.synchronize()
+        for i in range(K):
+            flush()
+            ev[i][0].record(stream)
+            decode_rope()
+            ev_end[i][0].record(stream)
+        torch.cuda.synchronize()
+        r_ms = sorted(ev[i][0].elapsed_time(ev_end[i][0]) for i in range(K))
+        A.timing_begin(2 * K + 4)
+        for i in range(K):
+            flush()
+            decode_rope()
+        kr = A.timing_end()
+        r_mean = sum(r_ms) / K
+        r_split = kr["decode_split"][0] / kr["decode_split"][1]
+        res["decode_rope"] = {
+            "metric": "decode KV GB/s with the rotary embedding", "unit": "GB/s",
+            "value": round(kv_bytes / (r_mean * 1e-3) / 1e9, 1), "rope_theta": 10000.0,
+            "call_ms": round(r_mean, 5), "call_ms_stats": stats(r_ms),
+            "split_kernel_ms": round(r_split, 5),
+            "combine_kernel_ms": round(kr["decode_combine"][0] / kr["decode_combine"][1], 5),
+            "slowdown_vs_plain_call": round(r_mean / ms_decode, 4),
+            "roofline": roofline_hbm(kv_bytes, r_split, "decode_rope")}
+        log("bench: rope decode", res["decode_rope"])
+
     # The chunked workload again through the shared-prefix cascade: one pass
     # of every query row over the 4096 shared tokens, then each request over
     # its own keys with the merge fused into the store.  Same flops as the
@@ -409,12 +447,14 @@ def main():
 TRAFFIC_FILES = {
     "decode_split": "profiles/traffic__decode_split__paged_decode_b64_hq32_hkv8_d128.md",
     "decode_fp8": "profiles/traffic__decode_split_fp8__paged_decode_e4m3_b64_hq32_hkv8_d128.md",
+    "decode_rope": "profiles/traffic__decode_split_rope__paged_decode_rope_b64_hq32_hkv8_d128.md",
     "prefill": "profiles/traffic__prefill__ragged_causal_b8_hq64_hkv8_d128.md",
     "prefill_paged": "profiles/traffic__prefill_paged__chunked_b16_q512_kv8704_h16_d256.md",
 }
 KERNEL_SOURCES = {
     "decode_split": ["decode.hip"],
     "decode_fp8": ["decode.hip"],
+    "decode_rope": ["decode.hip"],
     "prefill": ["prefill.hip"],
     "prefill_paged": ["prefill16.hip"],     # the chunked workload has head_dim 256
 }
