@@ -359,11 +359,14 @@ __device__ __forceinline__ int window_page0(const DecodeParams& p, int len) {
   return lo > 0 ? lo / kPage : 0;
 }
 
-// Pages of request b that hold keys the query sees (the schedule's units).
+// Pages of a request of `len` tokens that hold keys the query sees (the
+// schedule's units), and the same for request b.
+__device__ __forceinline__ int pages_from_len(const DecodeParams& p, int len) {
+  return (len + kPage - 1) / kPage - window_page0(p, len);
+}
 __device__ __forceinline__ int pages_of(const DecodeParams& p, int b) {
   bool bad;
-  const int len = request_len(p, b, bad);
-  return (len + kPage - 1) / kPage - window_page0(p, len);
+  return pages_from_len(p, request_len(p, b, bad));
 }
 
 __device__ __forceinline__ int wave_incl_scan(int x) {
@@ -424,11 +427,16 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
   using H = Half16<E>;
   using elem = typename H::elem;
   const int l16 = lane & 15, gq = lane >> 4;
-  // Request holding unit u0 (scan of units per request, 64 requests at a time).
-  int b = 0, start_b = 0;
+  // Request holding unit u0 (scan of units per request, 64 requests at a
+  // time).  The lengths of the 64 requests from c_base on stay one per lane
+  // (lenv, -1 for an inconsistent one), so later pieces read them without a
+  // memory round trip.
+  int b = 0, start_b = 0, c_base = 0, lenv = 0;
   for (int c = 0, cum = 0; c < p.B; c += 64) {
     const int bb = c + lane;
-    const int u = bb < p.B ? pages_of(p, bb) * p.nhg : 0;
+    bool bd = false;
+    const int ln = bb < p.B ? request_len(p, bb, bd) : 0;
+    const int u = bb < p.B ? pages_from_len(p, ln) * p.nhg : 0;
     const int incl = wave_incl_scan(u);
     const int tot = __builtin_amdgcn_readlane(incl, 63);
     if (cum + tot > u0) {
@@ -436,11 +444,22 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
       const int j = __builtin_ctzll(hit);
       b = c + j;
       start_b = cum + __builtin_amdgcn_readlane(incl, j) - __builtin_amdgcn_readlane(u, j);
+      c_base = c;
+      lenv = bd ? -1 : ln;
       break;
     }
     cum += tot;
   }
-  int np = pages_of(p, b);
+  auto len_of = [&](int bq) {
+    const int i = bq - c_base;
+    if (i >= 0 && i < 64) {
+      const int v = __builtin_amdgcn_readlane(lenv, i);
+      return v < 0 ? 0 : v;
+    }
+    bool bd;
+    return request_len(p, bq, bd);
+  };
+  int np = pages_from_len(p, len_of(b));
 
   char* myv = decode_vbuf<D>(wave);
   const char* kbase = reinterpret_cast<const char*>(p.k_pages);
@@ -458,12 +477,27 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
     bool ok;
   };
 
+  // Q^T fragments: lane (head l16, k-group gq) holds q[head][32 ks + 8 gq .. +8]
+  // (F8: q[head][64 (ks/2) + 16 gq + 8 (ks%2) .. +8], the order of its K chunks).
+  auto load_q = [&](int bq, int kvq, typename H::v8 (&dst)[C::KS]) {
+    const elem* qh = reinterpret_cast<const elem*>(p.q) +
+                     ((size_t)bq * p.Hq + (size_t)kvq * G + (l16 < G ? l16 : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int d0 = F8 ? 64 * (ks / 2) + 16 * gq + 8 * (ks % 2) : 32 * ks + 8 * gq;
+      const typename H::v8 v = *reinterpret_cast<const typename H::v8*>(qh + d0);
+      dst[ks] = l16 < G ? v : typename H::v8{};
+    }
+  };
+  typename H::v8 q_next[C::KS];
+  int ids_next = 0, b_next = -1, hg_next = -1;
+
   int u = u0;
   while (u < u1) {
     while (u >= start_b + p.nhg * np) {       // next request with units
       start_b += p.nhg * np;
       ++b;
-      np = pages_of(p, b);
+      np = pages_from_len(p, len_of(b));
     }
     const int r = u - start_b;
     const int hg = r / np, pg0 = r % np;
@@ -478,23 +512,41 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
     // Valid tokens (clamped) and the window: the piece's pages are counted
     // from page p0, the first one the window reaches; keys before win_lo
     // (relative to p0's first token) are masked.
-    bool bad_b;
-    const int len_b = request_len(p, b, bad_b);
+    const int len_b = len_of(b);
     const int p0 = window_page0(p, len_b);
-    const int len = min(p.kv_lens[b], (p0 + np) * kPage) - p0 * kPage;
+    const int len = len_b - p0 * kPage;
     const int win_lo = p.window_left >= 0 ? len_b - 1 - p.window_left - p0 * kPage : 0;
 
-    // Q^T fragments: lane (head l16, k-group gq) holds q[head][32 ks + 8 gq .. +8]
-    // (F8: q[head][64 (ks/2) + 16 gq + 8 (ks%2) .. +8], the order of its K chunks).
     typename H::v8 qf[C::KS];
-    {
-      const elem* qh = reinterpret_cast<const elem*>(p.q) +
-                         ((size_t)b * p.Hq + (size_t)kvh * G + (l16 < G ? l16 : 0)) * D;
+    const int32_t* table = p.page_table + (size_t)b * p.max_pages + p0 + pg0;
+    int ids0;
+    if (b == b_next && hg == hg_next) {        // prefetched during the previous piece
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const int d0 = F8 ? 64 * (ks / 2) + 16 * gq + 8 * (ks % 2) : 32 * ks + 8 * gq;
-        const typename H::v8 v = *reinterpret_cast<const typename H::v8*>(qh + d0);
-        qf[ks] = l16 < G ? v : typename H::v8{};
+      for (int ks = 0; ks < C::KS; ++ks) qf[ks] = q_next[ks];
+      ids0 = ids_next;
+    } else {
+      load_q(b, kvh, qf);
+      ids0 = lane < min(64, n) ? table[lane] : 0;
+    }
+    // The next piece of the run starts at page 0 of the next (request, head
+    // group) pair with units: fetch its query and first page ids now, so
+    // they are in registers when this piece ends (head_dim 256 has no
+    // registers to spare for it).
+    if (D <= 128 && u + n < u1) {
+      int bq = b, hq = hg + 1;
+      if (hq >= p.nhg) {
+        hq = 0;
+        for (++bq; bq < p.B && pages_from_len(p, len_of(bq)) == 0; ++bq) {}
+      }
+      const int kvq = hq * p.hw + wave;
+      if (bq < p.B && kvq < p.Hkv) {
+        const int lq = len_of(bq);
+        const int npq = pages_from_len(p, lq);
+        load_q(bq, kvq, q_next);
+        const int32_t* tq = p.page_table + (size_t)bq * p.max_pages + window_page0(p, lq);
+        ids_next = lane < min(64, npq) ? tq[lane] : 0;
+        b_next = bq;
+        hg_next = hq;
       }
     }
     // Rotary embedding: lane pair j = (k-step j / 8 < KS/2, element j % 8)
@@ -523,11 +575,10 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
     bool bad = false;
     const char* kh = kbase + (size_t)kvh * head_b;
     const char* vh = vbase + (size_t)kvh * head_b;
-    const int32_t* table = p.page_table + (size_t)b * p.max_pages + p0 + pg0;
 
     for (int c0 = 0; c0 < n; c0 += 64) {
       const int nc = min(64, n - c0);
-      const int ids = lane < nc ? table[c0 + lane] : 0;
+      const int ids = c0 == 0 ? ids0 : lane < nc ? table[c0 + lane] : 0;
       if constexpr (RP) {
         // Angle of this lane's key (token l16 of the page) at the first page of
         // the chunk, exact; later pages advance it by a 16-token rotation.
