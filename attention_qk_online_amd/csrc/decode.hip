@@ -806,6 +806,17 @@ __global__ __launch_bounds__(G * 64) void decode_merge_kernel(DecodeParams p) {
   for (int j0 = 0; j0 < nseg; j0 += 64) {
     const int nj = min(64, nseg - j0);
     const float ls = lane < nj ? pl[(size_t)(j0 + lane) * G] : kNegInf;
+    // Partial outputs of segments j0 + j .. j0 + j + 7; the first eight are
+    // requested together with the lse values (one memory round trip less).
+    float v[8][DL];
+    auto load_o = [&](int j) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < DL; ++i)
+          v[t][i] = (j + t < nj && lane + 64 * i < D) ? po[(size_t)(j0 + j + t) * G * D + lane + 64 * i] : 0.f;
+    };
+    load_o(0);
     nan_seen |= __builtin_amdgcn_ballot_w64(ls != ls) != 0;
     float cm = ls;
 #pragma unroll
@@ -822,12 +833,7 @@ __global__ __launch_bounds__(G * 64) void decode_merge_kernel(DecodeParams p) {
     for (int i = 0; i < DL; ++i) acc[i] *= resc;
     mx = mnew;
     for (int j = 0; j < nj; j += 8) {
-      float v[8][DL];
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int i = 0; i < DL; ++i)
-          v[t][i] = (j + t < nj && lane + 64 * i < D) ? po[(size_t)(j0 + j + t) * G * D + lane + 64 * i] : 0.f;
+      if (j > 0) load_o(j);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const float wt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), min(j + t, 63)));
