@@ -28,6 +28,9 @@ Readings where the pages are silent:
 * Causal masking is bottom-right aligned: query i of a sequence with Lq
   queries and Lk keys sees keys j <= i + (Lk - Lq).
 * A row with no visible key returns out = 0 and lse = -inf.
+* varlen_fwd's ``window_size`` is a (left, right) pair: query i sees keys
+  i + (Lk - Lq) - left .. i + (Lk - Lq) + right, -1 leaving that side open;
+  causal is the window (-1, 0), so with causal set a right window adds nothing.
 * Pages are NHD: ``pages[page, slot, kv_head, d]``; logical token t of a
   request lives at ``pages[table[t // P], t % P]``.
 
@@ -219,24 +222,37 @@ def ref_decode_paged_fp8(q, k_pages, v_pages, k_scale: float, v_scale: float, pa
     return out, lse
 
 
-def _prefill_one(qs, ks, vs, Hq, Hkv, scale, causal, rows: Optional[torch.Tensor],
-                 block: int = 1024, window_left: int = -1):
-    """One sequence: qs [Lq, Hq, D], ks/vs [Lk, Hkv, D]; causal is bottom-right;
-    window_left >= 0 adds the sliding-window bound (-1: none).
+def upper_bound_shift(causal: bool, window_right: int) -> int:
+    """How far right of its own diagonal position a query row may look: the
+    right half of varlen_fwd's window_size ("FlashAttention-3 内核在最新大模型
+    推理中的集成实践" section 二).  Row r sees keys j <= r + offset + shift;
+    causal is the window (-1, 0), so it caps the shift at 0; -1 means no bound."""
+    if causal:
+        return 0
+    return window_right if window_right >= 0 else -1
 
-    Rows go in blocks of at most ``block`` queries; under the causal mask a
+
+def _prefill_one(qs, ks, vs, Hq, Hkv, scale, causal, rows: Optional[torch.Tensor],
+                 block: int = 1024, window_left: int = -1, window_right: int = -1):
+    """One sequence: qs [Lq, Hq, D], ks/vs [Lk, Hkv, D]; causal is bottom-right;
+    window_left >= 0 adds the sliding-window bound on the left, window_right
+    >= 0 one on the right (-1: none; the causal bound is a right window of 0).
+
+    Rows go in blocks of at most ``block`` queries; under a right bound a
     block only multiplies against the keys its last row can see, since every
     later key is masked for the whole block anyway.
     """
     Lq, Lk = qs.shape[0], ks.shape[0]
     off = Lk - Lq
+    shift = upper_bound_shift(causal, window_right)
     idx = torch.arange(Lq) if rows is None else rows.long()
     out = torch.empty((idx.numel(), Hq, vs.shape[2]), dtype=F64)
     lse = torch.empty((idx.numel(), Hq), dtype=F64)
     for s0 in range(0, idx.numel(), block):
         r = idx[s0:s0 + block]
-        kmax = Lk if not causal else max(0, min(Lk, int(r.max()) + off + 1))
-        vis = causal_visible(r, kmax, off) if causal else None
+        bounded = shift >= 0
+        kmax = Lk if not bounded else max(0, min(Lk, int(r.max()) + off + shift + 1))
+        vis = causal_visible(r, kmax, off + shift) if bounded else None
         if window_left >= 0:
             w = window_visible(r, kmax, off, window_left)
             vis = w if vis is None else vis & w
@@ -249,7 +265,8 @@ def _prefill_one(qs, ks, vs, Hq, Hkv, scale, causal, rows: Optional[torch.Tensor
 
 
 def ref_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale,
-                       rows: Optional[torch.Tensor] = None, window_left: int = -1):
+                       rows: Optional[torch.Tensor] = None, window_left: int = -1,
+                       window_right: int = -1):
     """Ragged prefill addressed by cu_seqlens (length B+1).
 
     q [Tq, Hq, D]; k, v [Tk, Hkv, D].  Returns out [Tq, Hq, D], lse [Tq, Hq]
@@ -274,7 +291,7 @@ def ref_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale,
                 continue
             local = sel - q0
         o, l = _prefill_one(q[q0:q1], k[k0:k1], v[k0:k1], Hq, Hkv, scale, causal, local,
-                            window_left=window_left)
+                            window_left=window_left, window_right=window_right)
         tgt = torch.arange(q0, q1) if local is None else local + q0
         out[tgt] = o
         lse[tgt] = l
@@ -282,7 +299,8 @@ def ref_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, causal, scale,
 
 
 def ref_prefill_paged(q, cu_seqlens_q, k_pages, v_pages, page_table, kv_lens, causal, scale,
-                      rows: Optional[torch.Tensor] = None, window_left: int = -1):
+                      rows: Optional[torch.Tensor] = None, window_left: int = -1,
+                      window_right: int = -1):
     """Chunked prefill over a paged cache: request b's queries are the last
     Lq_b of its kv_lens[b] tokens (bottom-right causal)."""
     B = len(cu_seqlens_q) - 1
@@ -296,7 +314,7 @@ def ref_prefill_paged(q, cu_seqlens_q, k_pages, v_pages, page_table, kv_lens, ca
     k = torch.cat(ks) if ks else k_pages.new_zeros((0,) + tail)
     v = torch.cat(vs) if vs else v_pages.new_zeros((0,) + tail)
     return ref_prefill_varlen(q, k, v, cu_seqlens_q, torch.tensor(ck), causal, scale, rows=rows,
-                              window_left=window_left)
+                              window_left=window_left, window_right=window_right)
 
 
 def merge_states(states: Sequence[Tuple[torch.Tensor, torch.Tensor]]):

@@ -389,6 +389,52 @@ def pin_window_brute_force(R):
     _close(o[3, 0], c.v[6, 0], 0.0)       # last row of sequence 0 sits on key 6
 
 
+def pin_right_window_brute_force(R):
+    """Right-side window (window_size's second half) against explicit loops
+    over (i, j, d), alone and with a left window, with Lq < Lk and Lq > Lk
+    (bottom-right alignment, empty rows); its limits: a right window of 0 is
+    the causal mask, one as long as the keys is no bound, and the band
+    (0, 0) leaves each row its own diagonal key."""
+    c = workloads.make_prefill(B=3, Hq=2, Hkv=1, D=3, lens_q=[4, 3, 5], lens_k=[7, 3, 2], dtype=F64,
+                               seed=41, causal=False)
+    cq, ck = c.cu_seqlens_q.tolist(), c.cu_seqlens_k.tolist()
+    for left, right in ((-1, 0), (-1, 1), (-1, 3), (1, 1), (2, 0), (0, 2)):
+        o, l = R.ref_prefill_varlen(c.q, c.k, c.v, c.cu_seqlens_q, c.cu_seqlens_k, False,
+                                    c.scale, window_left=left, window_right=right)
+        for b in range(3):
+            Lq, Lk = cq[b + 1] - cq[b], ck[b + 1] - ck[b]
+            for i in range(Lq):
+                for h in range(2):
+                    js = [j for j in range(Lk) if j <= i + Lk - Lq + right and
+                          (left < 0 or j >= i + Lk - Lq - left)]
+                    if not js:
+                        assert float(l[cq[b] + i, h]) == -math.inf
+                        assert all(float(o[cq[b] + i, h, d]) == 0.0 for d in range(3))
+                        continue
+                    sc = [c.scale * sum(float(c.q[cq[b] + i, h, d]) * float(c.k[ck[b] + j, 0, d])
+                                        for d in range(3)) for j in js]
+                    mx = max(sc)
+                    w = [math.exp(x - mx) for x in sc]
+                    z = sum(w)
+                    for d in range(3):
+                        want = sum(wj * float(c.v[ck[b] + j, 0, d]) for wj, j in zip(w, js)) / z
+                        assert abs(float(o[cq[b] + i, h, d]) - want) < 1e-12
+                    assert abs(float(l[cq[b] + i, h]) - (mx + math.log(z))) < 1e-12
+    args = (c.q, c.k, c.v, c.cu_seqlens_q, c.cu_seqlens_k)
+    causal = R.ref_prefill_varlen(*args, True, c.scale)
+    right0 = R.ref_prefill_varlen(*args, False, c.scale, window_right=0)
+    _close(causal[0], right0[0], 0.0)
+    _close(causal[1], right0[1], 0.0)
+    plain = R.ref_prefill_varlen(*args, False, c.scale)
+    wide = R.ref_prefill_varlen(*args, False, c.scale, window_right=7)
+    _close(plain[0], wide[0], 0.0)
+    # causal set: a right window adds nothing
+    both = R.ref_prefill_varlen(*args, True, c.scale, window_right=2)
+    _close(causal[0], both[0], 0.0)
+    o, l = R.ref_prefill_varlen(*args, False, c.scale, window_left=0, window_right=0)
+    _close(o[1, 0], c.v[4, 0], 0.0)        # row 1 of sequence 0 sits on key 4
+
+
 def pin_decode_window(R):
     """Decode with a window is the last row of a causal windowed prefill over the
     same keys (one slices the keys, the other masks them), and a window of 0
@@ -456,7 +502,7 @@ PINS = [pin_golden, pin_brute_force, pin_sdpa_library, pin_single_key, pin_const
         pin_scale_zero_mean, pin_shift_invariance, pin_paging, pin_gqa_equals_repeated_mha,
         pin_causal_rows, pin_chunked_equals_full, pin_merge_partition, pin_empty_rows,
         pin_rows_subset, pin_fp8_decoder_library, pin_fp8_decode_equals_dequantised,
-        pin_window_brute_force, pin_decode_window, pin_rope]
+        pin_window_brute_force, pin_right_window_brute_force, pin_decode_window, pin_rope]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -484,6 +530,9 @@ MUTANTS = {
                        "return torch.cat([a * c + b * s, b * c - a * s], dim=-1)"),
     "rope_freq_exponent": ("-2.0 * torch.arange(h, dtype=F64) / D", "-1.0 * torch.arange(h, dtype=F64) / D"),
     "rope_query_position": ("torch.tensor([L - 1]), *rope)", "torch.tensor([L]), *rope)"),
+    "right_window_ignored": ("    return window_right if window_right >= 0 else -1", "    return -1"),
+    "right_window_overrides_causal": ("    if causal:\n        return 0", "    if causal and window_right < 0:\n        return 0"),
+    "right_window_off_by_one": ("int(r.max()) + off + shift + 1))", "int(r.max()) + off + shift))"),
     "window_ignored": ("            vis = w if vis is None else vis & w", "            vis = vis"),
     "fp8_exponent_bias": ("(e - 7).to(F64)", "(e - 8).to(F64)"),
     "fp8_subnormal_as_normal": ("mag = torch.where(e == 0, sub, norm)", "mag = norm"),
