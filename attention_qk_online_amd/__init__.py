@@ -106,10 +106,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_decode_paged_rope.argtypes = [c_int, c_int, c_int, c_float, c_float, vp, vp, vp, vp,
                                            vp] + [c_int] * 9 + [c_float, vp, vp, vp, c_size, vp]
     lib.attn_prefill_varlen_window.restype = c_int
-    lib.attn_prefill_varlen_window.argtypes = [c_int, vp, vp, vp, vp, vp] + [c_int] * 10 + [
+    lib.attn_prefill_varlen_window.argtypes = [c_int, vp, vp, vp, vp, vp] + [c_int] * 11 + [
         c_float, vp, vp, vp]
     lib.attn_prefill_paged_window.restype = c_int
-    lib.attn_prefill_paged_window.argtypes = [c_int, c_int, vp, vp, vp, vp, vp, vp] + [c_int] * 12 + [
+    lib.attn_prefill_paged_window.argtypes = [c_int, c_int, vp, vp, vp, vp, vp, vp] + [c_int] * 13 + [
         c_float, vp, vp, vp]
     # HND twins: same argument lists
     for name in ("attn_decode_paged", "attn_decode_paged_fp8", "attn_prefill_paged",
@@ -297,9 +297,11 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens
                    cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
                    causal: bool = True, scale: Optional[float] = None,
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                   window_left: int = -1) -> Tuple[torch.Tensor, torch.Tensor]:
+                   window_left: int = -1, window_right: int = -1) -> Tuple[torch.Tensor, torch.Tensor]:
     """Ragged prefill: q [Tq, Hq, D], k/v [Tk, Hkv, D] packed by cu_seqlens [B+1].
-    ``window_left`` >= 0 restricts query i to keys >= i + (Lk - Lq) - window_left.
+    ``window_left`` >= 0 restricts query i to keys >= i + (Lk - Lq) - window_left,
+    ``window_right`` >= 0 to keys <= i + (Lk - Lq) + window_right (``causal``
+    is the right window 0 and takes precedence).
 
     Returns (out [Tq, Hq, D], lse [Tq, Hq] float32).
     """
@@ -326,14 +328,15 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens
     _dev(lse, "lse", torch.float32, 2)
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (Tq, Hq):
         raise ValueError("out/lse have the wrong shape")
-    if window_left == -1:
+    if window_left == -1 and window_right == -1:
         _check(lib.attn_prefill_varlen(dt, pq, pk, pv, pcq, pck, B, Hq, Hkv, D, Tq, Tk,
                                        int(max_seqlen_q), int(max_seqlen_k), int(bool(causal)),
                                        s, out.data_ptr(), lse.data_ptr(), _stream(q.device)))
     else:
         _check(lib.attn_prefill_varlen_window(dt, pq, pk, pv, pcq, pck, B, Hq, Hkv, D, Tq, Tk,
                                               int(max_seqlen_q), int(max_seqlen_k),
-                                              int(bool(causal)), int(window_left), s,
+                                              int(bool(causal)), int(window_left),
+                                              int(window_right), s,
                                               out.data_ptr(), lse.data_ptr(), _stream(q.device)))
     return out, lse
 
@@ -343,11 +346,11 @@ def prefill_paged(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_pages: torch.Te
                   max_seqlen_q: int, max_kv_len: int, causal: bool = True,
                   scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                   lse: Optional[torch.Tensor] = None, kv_layout: str = "NHD",
-                  window_left: int = -1) -> Tuple[torch.Tensor, torch.Tensor]:
+                  window_left: int = -1, window_right: int = -1) -> Tuple[torch.Tensor, torch.Tensor]:
     """Chunked prefill over a paged KV cache: request b's queries are the last
     Lq_b of its kv_lens[b] cached tokens.  Pools are NHD or, with
-    ``kv_layout="HND"``, [num_pages, Hkv, page_size, D].  ``window_left`` as in
-    :func:`prefill_varlen`.  Returns (out, lse)."""
+    ``kv_layout="HND"``, [num_pages, Hkv, page_size, D].  ``window_left`` and
+    ``window_right`` as in :func:`prefill_varlen`.  Returns (out, lse)."""
     lib = load_library()
     suffix = _layout(kv_layout)
     dt = _dtype_code(q)
@@ -373,11 +376,12 @@ def prefill_paged(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_pages: torch.Te
     _dev(lse, "lse", torch.float32, 2)
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (Tq, Hq):
         raise ValueError("out/lse have the wrong shape")
-    if window_left != -1:
+    if window_left != -1 or window_right != -1:
         _check(lib.attn_prefill_paged_window(
             dt, 1 if suffix else 0, pq, pcq, pk, pv, pt, pl, B, Hq, Hkv, D, Tq, page_size,
             num_pages, page_table.shape[1], int(max_seqlen_q), int(max_kv_len), int(bool(causal)),
-            int(window_left), s, out.data_ptr(), lse.data_ptr(), _stream(q.device)))
+            int(window_left), int(window_right), s, out.data_ptr(), lse.data_ptr(),
+            _stream(q.device)))
         return out, lse
     _check(getattr(lib, "attn_prefill_paged" + suffix)(
         dt, pq, pcq, pk, pv, pt, pl, B, Hq, Hkv, D, Tq, page_size,

@@ -370,12 +370,15 @@ static attn_status prefill_varlen_impl(attn_dtype dtype, const void* q, const vo
                                        const void* v, const int32_t* cu_seqlens_q,
                                        const int32_t* cu_seqlens_k, int B, int Hq, int Hkv, int D,
                                        int total_q, int total_k, int max_seqlen_q,
-                                       int max_seqlen_k, int causal, int window_left, float scale,
-                                       void* out, float* lse, void* stream) {
+                                       int max_seqlen_k, int causal, int window_left,
+                                       int window_right, float scale, void* out, float* lse,
+                                       void* stream) {
   g_last_error[0] = 0;
   attn_status st = check_prefill_common(dtype, B, Hq, Hkv, D, total_q, max_seqlen_q, causal, scale);
   if (st != ATTN_OK) return st;
   if (window_left < -1) return fail(ATTN_E_VALUE, "window_left=%d (-1 = no window)", window_left);
+  if (window_right < -1)
+    return fail(ATTN_E_VALUE, "window_right=%d (-1 = no bound)", window_right);
   if (total_k < 0 || max_seqlen_k < 0)
     return fail(ATTN_E_SHAPE, "negative total_k=%d or max_seqlen_k=%d", total_k, max_seqlen_k);
   if (B == 0 || max_seqlen_q == 0 || total_q == 0) return ATTN_OK;
@@ -390,7 +393,11 @@ static attn_status prefill_varlen_impl(attn_dtype dtype, const void* q, const vo
   p.max_seqlen_q = max_seqlen_q; p.max_seqlen_k = max_seqlen_k; p.causal = causal;
   p.q_tiles = (max_seqlen_q + attn::kPrefillBM - 1) / attn::kPrefillBM;
   p.scale_log2 = scale * kLog2e;
-  p.window_left = window_left;
+  // A window at least as wide as every query-key span bounds nothing; -1
+  // keeps the kernel's index arithmetic small.
+  const long span = (long)max_seqlen_q + max_seqlen_k;
+  p.window_left = window_left >= span ? -1 : window_left;
+  p.window_right = window_right >= span ? -1 : window_right;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = timed(ATTN_KERNEL_PREFILL, s, [&] { return attn::launch_prefill(p, (int)dtype, D, false, s); });
   if (e != hipSuccess) return fail(ATTN_E_HIP, "prefill launch: %s", hipGetErrorString(e));
@@ -403,7 +410,7 @@ attn_status attn_prefill_varlen(attn_dtype dtype, const void* q, const void* k, 
                                 int max_seqlen_q, int max_seqlen_k, int causal, float scale,
                                 void* out, float* lse, void* stream) {
   return prefill_varlen_impl(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, D, total_q,
-                             total_k, max_seqlen_q, max_seqlen_k, causal, -1, scale, out, lse,
+                             total_k, max_seqlen_q, max_seqlen_k, causal, -1, -1, scale, out, lse,
                              stream);
 }
 
@@ -411,11 +418,12 @@ attn_status attn_prefill_varlen_window(attn_dtype dtype, const void* q, const vo
                                        const void* v, const int32_t* cu_seqlens_q,
                                        const int32_t* cu_seqlens_k, int B, int Hq, int Hkv, int D,
                                        int total_q, int total_k, int max_seqlen_q,
-                                       int max_seqlen_k, int causal, int window_left, float scale,
-                                       void* out, float* lse, void* stream) {
+                                       int max_seqlen_k, int causal, int window_left,
+                                       int window_right, float scale, void* out, float* lse,
+                                       void* stream) {
   return prefill_varlen_impl(dtype, q, k, v, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, D, total_q,
-                             total_k, max_seqlen_q, max_seqlen_k, causal, window_left, scale, out,
-                             lse, stream);
+                             total_k, max_seqlen_q, max_seqlen_k, causal, window_left,
+                             window_right, scale, out, lse, stream);
 }
 
 // Checks shared by the paged prefill entry points; on ATTN_OK, `p` holds the
@@ -457,12 +465,14 @@ static attn_status paged_prefill_params(attn_dtype dtype, const void* q,
   p.table_stride = max_pages_per_req; p.kv_offset = 0; p.kv_len_fixed = -1;
   p.kv_hnd = kv_hnd;
   p.window_left = -1;
+  p.window_right = -1;
   p.q_tiles = (max_seqlen_q + attn::kPrefillBM - 1) / attn::kPrefillBM;
   p.scale_log2 = scale * kLog2e;
   return ATTN_OK;
 }
 
-static attn_status prefill_paged_impl(attn_dtype dtype, int kv_hnd, int window_left, const void* q,
+static attn_status prefill_paged_impl(attn_dtype dtype, int kv_hnd, int window_left,
+                                      int window_right, const void* q,
                                       const int32_t* cu_seqlens_q, const void* k_pages,
                                       const void* v_pages, const int32_t* page_table,
                                       const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
@@ -479,8 +489,12 @@ static attn_status prefill_paged_impl(attn_dtype dtype, int kv_hnd, int window_l
                                         out, lse, kv_hnd, p, empty);
   if (st != ATTN_OK) return st;
   if (window_left < -1) return fail(ATTN_E_VALUE, "window_left=%d (-1 = no window)", window_left);
+  if (window_right < -1)
+    return fail(ATTN_E_VALUE, "window_right=%d (-1 = no bound)", window_right);
   if (empty) return ATTN_OK;
-  p.window_left = window_left;
+  const long span = (long)max_seqlen_q + max_kv_len;   // as in the ragged call
+  p.window_left = window_left >= span ? -1 : window_left;
+  p.window_right = window_right >= span ? -1 : window_right;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e =
       timed(ATTN_KERNEL_PREFILL_PAGED, s, [&] { return attn::launch_prefill(p, (int)dtype, D, true, s); });
@@ -494,7 +508,7 @@ attn_status attn_prefill_paged(attn_dtype dtype, const void* q, const int32_t* c
                                int Hkv, int D, int total_q, int page_size, int num_pages,
                                int max_pages_per_req, int max_seqlen_q, int max_kv_len,
                                int causal, float scale, void* out, float* lse, void* stream) {
-  return prefill_paged_impl(dtype, 0, -1, q, cu_seqlens_q, k_pages, v_pages, page_table, kv_lens, B,
+  return prefill_paged_impl(dtype, 0, -1, -1, q, cu_seqlens_q, k_pages, v_pages, page_table, kv_lens, B,
                             Hq, Hkv, D, total_q, page_size, num_pages, max_pages_per_req,
                             max_seqlen_q, max_kv_len, causal, scale, out, lse, stream);
 }
@@ -506,7 +520,7 @@ attn_status attn_prefill_paged_hnd(attn_dtype dtype, const void* q, const int32_
                                    int num_pages, int max_pages_per_req, int max_seqlen_q,
                                    int max_kv_len, int causal, float scale, void* out,
                                    float* lse, void* stream) {
-  return prefill_paged_impl(dtype, 1, -1, q, cu_seqlens_q, k_pages, v_pages, page_table, kv_lens, B,
+  return prefill_paged_impl(dtype, 1, -1, -1, q, cu_seqlens_q, k_pages, v_pages, page_table, kv_lens, B,
                             Hq, Hkv, D, total_q, page_size, num_pages, max_pages_per_req,
                             max_seqlen_q, max_kv_len, causal, scale, out, lse, stream);
 }
@@ -517,12 +531,12 @@ attn_status attn_prefill_paged_window(attn_dtype dtype, int kv_layout, const voi
                                       const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
                                       int total_q, int page_size, int num_pages,
                                       int max_pages_per_req, int max_seqlen_q, int max_kv_len,
-                                      int causal, int window_left, float scale, void* out,
-                                      float* lse, void* stream) {
+                                      int causal, int window_left, int window_right,
+                                      float scale, void* out, float* lse, void* stream) {
   g_last_error[0] = 0;
   if (kv_layout != 0 && kv_layout != 1)
     return fail(ATTN_E_VALUE, "kv_layout=%d (0 = NHD, 1 = HND)", kv_layout);
-  return prefill_paged_impl(dtype, kv_layout, window_left, q, cu_seqlens_q, k_pages, v_pages,
+  return prefill_paged_impl(dtype, kv_layout, window_left, window_right, q, cu_seqlens_q, k_pages, v_pages,
                             page_table, kv_lens, B, Hq, Hkv, D, total_q, page_size, num_pages,
                             max_pages_per_req, max_seqlen_q, max_kv_len, causal, scale, out, lse,
                             stream);

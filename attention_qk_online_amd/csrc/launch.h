@@ -73,6 +73,10 @@ struct PrefillParams {
   // Sliding window: query i sees only keys >= i + (Lk - Lq) - window_left
   // (bottom-right aligned like the causal mask); -1 = no window.
   int window_left;
+  // Right side of the window: query i sees only keys <= i + (Lk - Lq) +
+  // window_right; -1 = no bound.  causal is the right window 0 and takes
+  // precedence.
+  int window_right;
   float scale_log2;
 };
 

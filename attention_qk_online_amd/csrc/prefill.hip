@@ -173,8 +173,11 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
     Lk = k_end - k_start;
   }
   int off = Lk - Lq;                             // bottom-right causal offset
+  // Right bound: query i sees keys j <= i + off + rb (causal: rb = 0).
+  const int rb = p.causal ? 0 : p.window_right;
+  const bool up = rb >= 0;
   const int r_last = min(r0 + BM, Lq) - 1;
-  int kend = p.causal ? min(Lk, r_last + off + 1) : Lk;
+  int kend = up ? min(Lk, r_last + off + rb + 1) : Lk;
   if (kend < 0) kend = 0;
   // Sliding window: query i sees keys from i + off - window_left on.  Whole
   // tiles before the first row's window are skipped by moving the key origin
@@ -320,10 +323,10 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
   if (wave_rows) {
     // tiles before w_lead hold keys left of some row's window
     if (win >= 0) w_lead = max(0, w_last + off - win + C::BN - 1) / C::BN;
-    const int wkend = p.causal ? max(0, min(Lk, w_last + off + 1)) : Lk;
+    const int wkend = up ? max(0, min(Lk, w_last + off + rb + 1)) : Lk;
     w_kt = min(n_kt, (wkend + C::BN - 1) / C::BN);
     int lim = t_full;
-    if (p.causal) lim = min(lim, max(0, w_first + off + 1) / C::BN);
+    if (up) lim = min(lim, max(0, w_first + off + rb + 1) / C::BN);
     w_fast = min(lim, w_kt);
   }
 
@@ -342,7 +345,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
   // its window -> -inf.
   auto mask = [&](int kt, f32x16 (&s)[C::KB]) {
     const int k0 = kt * C::BN;
-    const int lim = p.causal ? min(pos, Lk - 1) : Lk - 1;
+    const int lim = up ? min(pos + rb, Lk - 1) : Lk - 1;
     const int lo = win >= 0 ? pos - win : 0;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
@@ -481,9 +484,9 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
   // unmasked and needed tiles (its rows come first); waves past the last
   // row compute on zero queries and store nothing.
   int n_fast = t_full;
-  if (p.causal) n_fast = min(n_fast, max(0, r0 + off + 1) / C::BN);
+  if (up) n_fast = min(n_fast, max(0, r0 + off + rb + 1) / C::BN);
   {
-    const int wkend0 = p.causal ? max(0, min(Lk, min(r0 + 31, Lq - 1) + off + 1)) : Lk;
+    const int wkend0 = up ? max(0, min(Lk, min(r0 + 31, Lq - 1) + off + rb + 1)) : Lk;
     const int w_kt0 = min(n_kt, (wkend0 + C::BN - 1) / C::BN);
     n_fast = max(0, min(n_fast, w_kt0 - 1));
     n_fast -= n_fast % C::R;

@@ -306,28 +306,33 @@ attn_status attn_decode_paged_rope(attn_dtype dtype, int kv_layout, int window_l
 
 /* ------------------------------------------------------------------------ */
 /* Ragged and paged prefill with a sliding window (the window_size argument
- * of varlen_fwd in "FlashAttention-3 ..." section 二, left side): query i of
- * a sequence with Lq queries and Lk keys sees key j only if
- * j >= i + (Lk - Lq) - window_left, in addition to the causal bound when
- * causal = 1 (both aligned bottom-right).  window_left = -1 is no window
- * (the calls above); other negative values return ATTN_E_VALUE.  Whole key
- * tiles left of a query tile's windows are never loaded.  kv_layout: 0 NHD,
- * 1 HND pages.  Everything else as attn_prefill_varlen / attn_prefill_paged.
+ * of varlen_fwd in "FlashAttention-3 ..." section 二, a (left, right) pair):
+ * query i of a sequence with Lq queries and Lk keys sees key j only if
+ * j >= i + (Lk - Lq) - window_left and j <= i + (Lk - Lq) + window_right
+ * (both aligned bottom-right like the causal mask).  -1 leaves that side
+ * open (window_left = window_right = -1 are the calls above); other negative
+ * values return ATTN_E_VALUE.  causal = 1 is the right window 0 and takes
+ * precedence over window_right.  A window at least max_seqlen_q +
+ * max_seqlen_k (paged: max_kv_len) wide bounds nothing.  Rows left with no
+ * visible key get out = 0 and lse = -inf.  Whole key tiles outside a query
+ * tile's windows are never loaded.  kv_layout: 0 NHD, 1 HND pages.
+ * Everything else as attn_prefill_varlen / attn_prefill_paged.
  */
 attn_status attn_prefill_varlen_window(attn_dtype dtype, const void* q, const void* k,
                                        const void* v, const int32_t* cu_seqlens_q,
                                        const int32_t* cu_seqlens_k, int B, int Hq, int Hkv, int D,
                                        int total_q, int total_k, int max_seqlen_q,
-                                       int max_seqlen_k, int causal, int window_left, float scale,
-                                       void* out, float* lse, void* stream);
+                                       int max_seqlen_k, int causal, int window_left,
+                                       int window_right, float scale, void* out, float* lse,
+                                       void* stream);
 attn_status attn_prefill_paged_window(attn_dtype dtype, int kv_layout, const void* q,
                                       const int32_t* cu_seqlens_q, const void* k_pages,
                                       const void* v_pages, const int32_t* page_table,
                                       const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
                                       int total_q, int page_size, int num_pages,
                                       int max_pages_per_req, int max_seqlen_q, int max_kv_len,
-                                      int causal, int window_left, float scale, void* out,
-                                      float* lse, void* stream);
+                                      int causal, int window_left, int window_right,
+                                      float scale, void* out, float* lse, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* The paged entry points above read NHD pages: [num_pages, page_size, Hkv, D],

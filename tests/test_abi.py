@@ -153,19 +153,23 @@ def test_prefill_rejects(lib, kw, status):
 
 
 def test_window_rejects(lib):
-    def call(w, **kw):
+    def call(w, wr=-1, **kw):
         a = dict(dtype=1, q=16, k=16, v=16, cq=16, ck=16, B=2, Hq=8, Hkv=2, D=128, Tq=100, Tk=100,
                  mq=64, mk=64, causal=1, scale=0.1, out=16, lse=16)
         a.update(kw)
         return lib.attn_prefill_varlen_window(a["dtype"], a["q"], a["k"], a["v"], a["cq"], a["ck"],
                                               a["B"], a["Hq"], a["Hkv"], a["D"], a["Tq"], a["Tk"],
-                                              a["mq"], a["mk"], a["causal"], w, a["scale"],
+                                              a["mq"], a["mk"], a["causal"], w, wr, a["scale"],
                                               a["out"], a["lse"], None)
     assert call(-2) == E_VALUE
+    assert call(-1, -2) == E_VALUE               # right side: -1 is the only negative value
     assert call(5, D=64) == E_UNSUP
     assert call(5, B=0, q=None) == OK
+    assert call(-1, 3, B=0, q=None) == OK
     assert lib.attn_prefill_paged_window(1, 2, 16, 16, 16, 16, 16, 16, 2, 4, 4, 256, 10, 16, 10, 4,
-                                         5, 64, 1, 3, 0.1, 16, 16, None) == E_VALUE   # layout 2
+                                         5, 64, 1, 3, -1, 0.1, 16, 16, None) == E_VALUE   # layout 2
+    assert lib.attn_prefill_paged_window(1, 0, 16, 16, 16, 16, 16, 16, 2, 4, 4, 256, 10, 16, 10, 4,
+                                         5, 64, 0, -1, -3, 0.1, 16, 16, None) == E_VALUE
 
 
 def test_decode_window_rejects(lib):

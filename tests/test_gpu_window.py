@@ -1,5 +1,6 @@
 """GPU parity of the sliding-window prefill (attn_prefill_varlen_window,
-attn_prefill_paged_window) against the oracle's window_left."""
+attn_prefill_paged_window) against the oracle's window_left / window_right,
+and of the sliding-window decode."""
 import pytest
 import torch
 
@@ -10,21 +11,22 @@ from helpers import assert_parity
 pytestmark = pytest.mark.gpu
 
 
-def _varlen(case, gpu, window, causal=None):
+def _varlen(case, gpu, window, causal=None, right=-1):
     import attention_qk_online_amd as A
     causal = case.causal if causal is None else causal
     out, lse = A.prefill_varlen(case.q.to(gpu), case.k.to(gpu), case.v.to(gpu),
                                 case.cu_seqlens_q.to(gpu), case.cu_seqlens_k.to(gpu),
                                 case.max_seqlen_q, case.max_seqlen_k, causal=causal,
-                                scale=case.scale, window_left=window)
+                                scale=case.scale, window_left=window, window_right=right)
     torch.cuda.synchronize()
     return out, lse
 
 
-def _ref(case, window, causal=None, rows=None):
+def _ref(case, window, causal=None, rows=None, right=-1):
     causal = case.causal if causal is None else causal
     return oracle.ref_prefill_varlen(case.q, case.k, case.v, case.cu_seqlens_q, case.cu_seqlens_k,
-                                     causal, case.scale, rows=rows, window_left=window)
+                                     causal, case.scale, rows=rows, window_left=window,
+                                     window_right=right)
 
 
 @pytest.mark.parametrize("D", [128, 256])
@@ -109,6 +111,87 @@ def test_window_chunked_paged_config_sampled(gpu):
                                       case.page_table, case.kv_lens, True, case.scale, rows=rows,
                                       window_left=2048)
     assert_parity(out, lse, ro, rl, torch.bfloat16, "chunked paged window 2048 (sampled)", rows=rows)
+
+
+# --------------------------------------------------- right side of the window ---
+WINDOWS = [(-1, 0), (-1, 1), (-1, 63), (-1, 64), (-1, 200), (10, 5), (0, 0), (100, 30), (64, 64)]
+
+
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("left,right", WINDOWS)
+def test_right_window_small(gpu, D, left, right):
+    lens = [1, 17, 128, 129, 300, 64, 255]
+    case = workloads.make_prefill(B=len(lens), Hq=4, Hkv=2, D=D, lens_q=lens, dtype=torch.bfloat16,
+                                  seed=770 + D, causal=False)
+    out, lse = _varlen(case, gpu, left, right=right)
+    ro, rl = _ref(case, left, right=right)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, f"window ({left}, {right}) D{D}")
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_right_window_q_and_k_lengths_differ(gpu, D):
+    """Lq < Lk and Lq > Lk (bottom-right alignment; rows with no visible key
+    get out 0 and lse -inf)."""
+    case = workloads.make_prefill(B=4, Hq=4, Hkv=4, D=D, lens_q=[50, 200, 7, 300],
+                                  lens_k=[400, 333, 900, 120], dtype=torch.bfloat16, seed=780 + D,
+                                  causal=False)
+    for left, right in ((-1, 0), (-1, 40), (20, 3), (300, 100)):
+        out, lse = _varlen(case, gpu, left, right=right)
+        ro, rl = _ref(case, left, right=right)
+        assert_parity(out, lse, ro, rl, torch.bfloat16, f"Lq!=Lk window ({left}, {right}) D{D}")
+
+
+def test_right_window_zero_is_causal_and_wide_is_none(gpu):
+    """A right window of 0 gives the causal call's result bit for bit; one
+    covering every key gives the plain non-causal call's; causal set, a right
+    window changes nothing."""
+    case = workloads.make_prefill(B=2, Hq=8, Hkv=2, D=128, lens_q=[300, 129], lens_k=[300, 200],
+                                  dtype=torch.bfloat16, seed=790, causal=False)
+    oc, lc = _varlen(case, gpu, -1, causal=True)
+    o0, l0 = _varlen(case, gpu, -1, causal=False, right=0)
+    assert torch.equal(oc, o0) and torch.equal(lc, l0)
+    on, ln = _varlen(case, gpu, -1, causal=False)
+    ow, lw = _varlen(case, gpu, -1, causal=False, right=100000)
+    assert torch.equal(on, ow) and torch.equal(ln, lw)
+    ob, lb = _varlen(case, gpu, -1, causal=True, right=50)
+    assert torch.equal(oc, ob) and torch.equal(lc, lb)
+
+
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_right_window_paged(gpu, D, layout):
+    import attention_qk_online_amd as A
+    case = workloads.make_paged_prefill(B=3, Hq=4, Hkv=2, D=D, page_size=16, chunk=90, cached=250,
+                                        shared_prefix=64, dtype=torch.bfloat16, seed=800 + D)
+    kp, vp = case.pools(gpu, layout=layout)
+    for left, right in ((-1, 0), (-1, 45), (77, 20), (0, 0)):
+        out, lse = A.prefill_paged(case.q.to(gpu), case.cu_seqlens_q.to(gpu), kp, vp,
+                                   case.page_table.to(gpu), case.kv_lens.to(gpu), case.max_seqlen_q,
+                                   case.max_kv_len, causal=False, scale=case.scale,
+                                   kv_layout=layout, window_left=left, window_right=right)
+        torch.cuda.synchronize()
+        ro, rl = oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, case.pool_k, case.pool_v,
+                                          case.page_table, case.kv_lens, False, case.scale,
+                                          window_left=left, window_right=right)
+        assert_parity(out, lse, ro, rl, torch.bfloat16,
+                      f"paged {layout} D{D} window ({left}, {right})")
+
+
+def test_right_window_ragged_config_sampled(gpu):
+    """The ragged workload (B 8, L in [1024, 4096], Hq 64, Hkv 8, D 128), non-causal
+    with the band window (512, 256), sampled rows."""
+    case = workloads.make_config(3)
+    out, lse = _varlen(case, gpu, 512, causal=False, right=256)
+    cu = [int(x) for x in case.cu_seqlens_q]
+    g = torch.Generator().manual_seed(810)
+    rows = set(torch.randint(0, cu[-1], (64,), generator=g).tolist())
+    for a, b in zip(cu[:-1], cu[1:]):
+        rows.update(r for r in (a, a + 255, a + 256, a + 700, b - 257, b - 256, b - 1) if a <= r < b)
+    rows = torch.tensor(sorted(rows))
+    ro, rl = _ref(case, 512, causal=False, rows=rows, right=256)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, "ragged window (512, 256) (sampled rows)",
+                  rows=rows)
+    assert torch.isfinite(out.float()).all()
 
 
 # ---------------------------------------------------------------- decode ---
