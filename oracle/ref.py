@@ -133,6 +133,12 @@ def _check_heads(Hq: int, Hkv: int):
         raise ValueError(f"Hq={Hq} must be a positive multiple of Hkv={Hkv}")
 
 
+def decode_window_first(L: int, window_left: int) -> int:
+    """First key a decode query (the last of L tokens, position L - 1) sees
+    under a left window of window_left keys (-1: no window, key 0)."""
+    return max(0, L - 1 - window_left) if window_left >= 0 else 0
+
+
 def ref_decode_paged(q, k_pages, v_pages, page_table, kv_lens, scale,
                      requests: Optional[Iterable[int]] = None, window_left: int = -1,
                      rope: Optional[Tuple[float, float]] = None):
@@ -159,9 +165,8 @@ def ref_decode_paged(q, k_pages, v_pages, page_table, kv_lens, scale,
         if rope is not None:
             k = rope_rotate(k.transpose(0, 1), torch.arange(L), *rope).transpose(0, 1)
             qb = rope_rotate(q[b].unsqueeze(1), torch.tensor([L - 1]), *rope).squeeze(1)
-        if window_left >= 0:
-            first = max(0, L - 1 - window_left)
-            k, v = k[first:], v[first:]
+        first = decode_window_first(L, window_left)
+        k, v = k[first:], v[first:]
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
             o, l = softmax_attend(qb[h:h + 1], k[:, g], v[:, g], scale)
@@ -193,7 +198,7 @@ def fp8_e4m3_to_float(b: torch.Tensor) -> torch.Tensor:
 
 
 def ref_decode_paged_fp8(q, k_pages, v_pages, k_scale: float, v_scale: float, page_table, kv_lens,
-                         scale, requests: Optional[Iterable[int]] = None):
+                         scale, requests: Optional[Iterable[int]] = None, window_left: int = -1):
     """Decode over a KV cache stored as E4M3 bytes with one scale per tensor:
     each key is k_scale times the value of its bytes, each value vector
     v_scale times the value of its bytes; then plain decode attention.  (In
@@ -201,9 +206,9 @@ def ref_decode_paged_fp8(q, k_pages, v_pages, k_scale: float, v_scale: float, pa
     scale is folded into the softmax's exponent scaling; mathematically that
     is this product.)
 
-    k_pages / v_pages: uint8 [num_pages, P, Hkv, D]; other arguments and the
-    result as :func:`ref_decode_paged`.  Only the tokens a request uses are
-    decoded.
+    k_pages / v_pages: uint8 [num_pages, P, Hkv, D]; other arguments (the
+    sliding window included) and the result as :func:`ref_decode_paged`.
+    Only the tokens a request uses are decoded.
     """
     B, Hq, D = q.shape
     Hkv = k_pages.shape[2]
@@ -214,6 +219,8 @@ def ref_decode_paged_fp8(q, k_pages, v_pages, k_scale: float, v_scale: float, pa
         L = int(kv_lens[b])
         k = fp8_e4m3_to_float(gather_pages(k_pages, page_table[b], L)) * float(k_scale)
         v = fp8_e4m3_to_float(gather_pages(v_pages, page_table[b], L)) * float(v_scale)
+        first = decode_window_first(L, window_left)
+        k, v = k[first:], v[first:]
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
             o, l = softmax_attend(q[b, h:h + 1], k[:, g], v[:, g], scale)

@@ -352,6 +352,13 @@ def pin_fp8_decode_equals_dequantised(R):
                                     c.scale / 2)
     _close(o3, 3 * o, 1e-12)
     _close(l3, l, 1e-12)
+    # with a sliding window: the windowed decode of the dequantised cache
+    for left in (0, 3):
+        o4, l4 = R.ref_decode_paged_fp8(c.q, kb, vb, ks, vs, c.page_table, c.kv_lens, c.scale,
+                                        window_left=left)
+        o5, l5 = R.ref_decode_paged(c.q, kf, vf, c.page_table, c.kv_lens, c.scale, window_left=left)
+        _close(o4, o5, 1e-13)
+        _close(l4, l5, 1e-13)
 
 
 def pin_window_brute_force(R):
@@ -525,7 +532,7 @@ MUTANTS = {
     "mask_strict": ("<= (rows.long().unsqueeze(1) + offset)", "< (rows.long().unsqueeze(1) + offset)"),
     "window_sign": ("(rows.long().unsqueeze(1) + offset - left)", "(rows.long().unsqueeze(1) - offset - left)"),
     "window_strict": (">= (rows.long().unsqueeze(1) + offset - left)", "> (rows.long().unsqueeze(1) + offset - left)"),
-    "decode_window_off_by_one": ("first = max(0, L - 1 - window_left)", "first = max(0, L - window_left)"),
+    "decode_window_off_by_one": ("return max(0, L - 1 - window_left) if", "return max(0, L - window_left) if"),
     "rope_turn_sign": ("return torch.cat([a * c - b * s, b * c + a * s], dim=-1)",
                        "return torch.cat([a * c + b * s, b * c - a * s], dim=-1)"),
     "rope_freq_exponent": ("-2.0 * torch.arange(h, dtype=F64) / D", "-1.0 * torch.arange(h, dtype=F64) / D"),
@@ -537,6 +544,12 @@ MUTANTS = {
     "fp8_exponent_bias": ("(e - 7).to(F64)", "(e - 8).to(F64)"),
     "fp8_subnormal_as_normal": ("mag = torch.where(e == 0, sub, norm)", "mag = norm"),
     "fp8_nan_on_exponent_15": ("(e == 15) & ((x & 7) == 7)", "(e == 15)"),
+    "fp8_window_ignored": ("k = fp8_e4m3_to_float(gather_pages(k_pages, page_table[b], L)) * float(k_scale)\n"
+                           "        v = fp8_e4m3_to_float(gather_pages(v_pages, page_table[b], L)) * float(v_scale)\n"
+                           "        first = decode_window_first(L, window_left)",
+                           "k = fp8_e4m3_to_float(gather_pages(k_pages, page_table[b], L)) * float(k_scale)\n"
+                           "        v = fp8_e4m3_to_float(gather_pages(v_pages, page_table[b], L)) * float(v_scale)\n"
+                           "        first = 0"),
     "fp8_k_scale_on_values": ("* float(v_scale)", "* float(k_scale)"),
     "softmax_no_exp_shift": ("p = torch.exp(s - torch.where(empty, torch.zeros_like(lse), lse).unsqueeze(1))",
                              "p = torch.exp(s - torch.where(empty, torch.zeros_like(m), m).unsqueeze(1))"),
