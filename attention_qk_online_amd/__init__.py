@@ -105,6 +105,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_decode_paged_rope.restype = c_int
     lib.attn_decode_paged_rope.argtypes = [c_int, c_int, c_int, c_float, c_float, vp, vp, vp, vp,
                                            vp] + [c_int] * 9 + [c_float, vp, vp, vp, c_size, vp]
+    lib.attn_decode_paged_fp8_window.restype = c_int
+    lib.attn_decode_paged_fp8_window.argtypes = [c_int, c_int, c_int, vp, vp, vp, vp, vp] + [c_int] * 9 + [
+        c_float, c_float, c_float, vp, vp, vp, c_size, vp]
     lib.attn_prefill_varlen_window.restype = c_int
     lib.attn_prefill_varlen_window.argtypes = [c_int, vp, vp, vp, vp, vp] + [c_int] * 11 + [
         c_float, vp, vp, vp]
@@ -243,9 +246,11 @@ def _decode(q, k_pages, v_pages, page_table, kv_lens, scale, max_kv_len, split_p
             raise ValueError("the rotary embedding is not built for the E4M3 cache")
         _check(lib.attn_decode_paged_rope(dt, 1 if suffix else 0, int(window_left),
                                           float(rope[0]), float(rope[1]), *args, *tail))
+    elif window_left != -1 and fp8_scales is not None:
+        _check(lib.attn_decode_paged_fp8_window(dt, 1 if suffix else 0, int(window_left), *args,
+                                                float(fp8_scales[0]), float(fp8_scales[1]),
+                                                *tail))
     elif window_left != -1:
-        if fp8_scales is not None:
-            raise ValueError("a sliding window is not built for the E4M3 cache")
         _check(lib.attn_decode_paged_window(dt, 1 if suffix else 0, int(window_left), *args,
                                             *tail))
     elif fp8_scales is None:
@@ -284,13 +289,14 @@ def decode_paged_fp8(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tens
                      v_scale: float, scale: Optional[float] = None,
                      max_kv_len: Optional[int] = None, split_pages: int = 0,
                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None,
-                     kv_layout: str = "NHD") -> Tuple[torch.Tensor, torch.Tensor]:
+                     workspace: Optional[torch.Tensor] = None, kv_layout: str = "NHD",
+                     window_left: int = -1) -> Tuple[torch.Tensor, torch.Tensor]:
     """:func:`decode_paged` over a cache of E4M3 bytes (uint8 pools): token t's
     key is ``k_scale * E4M3(k_pages[...])`` and its value ``v_scale * E4M3(...)``.
-    q and out are bf16 or fp16."""
+    q and out are bf16 or fp16; ``window_left`` as in :func:`decode_paged`."""
     return _decode(q, k_pages, v_pages, page_table, kv_lens, scale, max_kv_len, split_pages, out,
-                   lse, workspace, fp8_scales=(k_scale, v_scale), kv_layout=kv_layout)
+                   lse, workspace, fp8_scales=(k_scale, v_scale), kv_layout=kv_layout,
+                   window_left=window_left)
 
 
 def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,

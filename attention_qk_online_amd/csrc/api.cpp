@@ -299,6 +299,23 @@ attn_status attn_decode_paged_fp8(attn_dtype dtype, const void* q, const void* k
                      k_scale, v_scale, out, lse, workspace, workspace_bytes, stream);
 }
 
+attn_status attn_decode_paged_fp8_window(attn_dtype dtype, int kv_layout, int window_left,
+                                         const void* q, const void* k_pages, const void* v_pages,
+                                         const int32_t* page_table, const int32_t* kv_lens, int B,
+                                         int Hq, int Hkv, int D, int page_size, int num_pages,
+                                         int max_pages_per_req, int max_kv_len, int split_pages,
+                                         float scale, float k_scale, float v_scale, void* out,
+                                         float* lse, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  g_last_error[0] = 0;
+  if (kv_layout != 0 && kv_layout != 1)
+    return fail(ATTN_E_VALUE, "kv_layout=%d (0 = NHD, 1 = HND)", kv_layout);
+  return decode_impl(dtype, true, kv_layout, window_left, false, 0.f, 0.f, q, k_pages, v_pages,
+                     page_table, kv_lens, B, Hq, Hkv, D, page_size, num_pages, max_pages_per_req,
+                     max_kv_len, split_pages, scale, k_scale, v_scale, out, lse, workspace,
+                     workspace_bytes, stream);
+}
+
 attn_status attn_decode_paged_window(attn_dtype dtype, int kv_layout, int window_left,
                                      const void* q, const void* k_pages, const void* v_pages,
                                      const int32_t* page_table, const int32_t* kv_lens, int B,

@@ -304,6 +304,21 @@ attn_status attn_decode_paged_rope(attn_dtype dtype, int kv_layout, int window_l
                                    float scale, void* out, float* lse, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* Decode over an E4M3 (fp8) cache with a sliding window: the window of
+ * attn_decode_paged_window (the query sees keys kv_len-1-window_left ..
+ * kv_len-1; window_left = -1: all, other negative values ATTN_E_VALUE; pages
+ * before the window are never read) on the cache, scales and dtypes of
+ * attn_decode_paged_fp8.  kv_layout: 0 NHD, 1 HND pages.
+ */
+attn_status attn_decode_paged_fp8_window(attn_dtype dtype, int kv_layout, int window_left,
+                                         const void* q, const void* k_pages, const void* v_pages,
+                                         const int32_t* page_table, const int32_t* kv_lens, int B,
+                                         int Hq, int Hkv, int D, int page_size, int num_pages,
+                                         int max_pages_per_req, int max_kv_len, int split_pages,
+                                         float scale, float k_scale, float v_scale, void* out,
+                                         float* lse, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Ragged and paged prefill with a sliding window (the window_size argument
  * of varlen_fwd in "FlashAttention-3 ..." section 二, a (left, right) pair):

@@ -14,23 +14,67 @@ from helpers import assert_parity
 pytestmark = pytest.mark.gpu
 
 
-def _run(case, gpu, fp8, split_pages=0, table=None, lens=None, max_kv_len=None, q=None):
+def _run(case, gpu, fp8, split_pages=0, table=None, lens=None, max_kv_len=None, q=None, window=-1,
+         layout="NHD"):
     import attention_qk_online_amd as A
     kb, vb, ks, vs = fp8
+    if layout == "HND":
+        kb, vb = kb.transpose(1, 2).contiguous(), vb.transpose(1, 2).contiguous()
     t = (case.page_table if table is None else table).to(gpu)
     kl = (case.kv_lens if lens is None else lens).to(gpu)
     out, lse = A.decode_paged_fp8((case.q if q is None else q).to(gpu), kb.to(gpu), vb.to(gpu), t,
                                   kl, ks, vs, scale=case.scale,
                                   max_kv_len=case.max_kv_len if max_kv_len is None else max_kv_len,
-                                  split_pages=split_pages)
+                                  split_pages=split_pages, kv_layout=layout, window_left=window)
     torch.cuda.synchronize()
     return out, lse
 
 
-def _oracle(case, fp8, q=None, requests=None):
+def _oracle(case, fp8, q=None, requests=None, window=-1):
     kb, vb, ks, vs = fp8
     return oracle.ref_decode_paged_fp8(case.q if q is None else q, kb, vb, ks, vs, case.page_table,
-                                       case.kv_lens, case.scale, requests=requests)
+                                       case.kv_lens, case.scale, requests=requests,
+                                       window_left=window)
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 8, 8), (256, 16, 2)])
+@pytest.mark.parametrize("split_pages", [0, 2])
+def test_fp8_window(gpu, D, Hq, Hkv, split_pages):
+    """Sliding window on the E4M3 cache: windows inside a page, on page edges
+    and wider than the keys, against the oracle's windowed fp8 decode."""
+    lens = [1, 15, 16, 17, 300, 64, 1000, 0, 33]
+    case = workloads.make_decode(B=len(lens), Hq=Hq, Hkv=Hkv, D=D, page_size=16, kv_lens=lens,
+                                 dtype=torch.bfloat16, seed=520 + D + Hq, extra_pages=4)
+    fp8 = case.fp8_pools()
+    for window in (0, 5, 15, 16, 17, 100, 1000):
+        out, lse = _run(case, gpu, fp8, split_pages, window=window)
+        ro, rl = _oracle(case, fp8, window=window)
+        assert_parity(out, lse, ro, rl, torch.bfloat16, f"fp8 D{D} window {window} split{split_pages}")
+
+
+def test_fp8_window_hnd_and_wide(gpu):
+    """HND equals NHD bit for bit with a window; a window covering every key
+    equals the plain E4M3 call bit for bit."""
+    case = workloads.make_decode(B=5, Hq=16, Hkv=4, D=128, page_size=16, kv_lens=[33, 400, 16, 1, 250],
+                                 dtype=torch.bfloat16, seed=530, extra_pages=3)
+    fp8 = case.fp8_pools()
+    o1, l1 = _run(case, gpu, fp8, 2, window=37)
+    o2, l2 = _run(case, gpu, fp8, 2, window=37, layout="HND")
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o3, l3 = _run(case, gpu, fp8, 2)
+    o4, l4 = _run(case, gpu, fp8, 2, window=400)
+    assert torch.equal(o3, o4) and torch.equal(l3, l4)
+
+
+def test_fp8_window_paged_config(gpu):
+    """The batched paged GQA decode workload (B 64, Hq 32, Hkv 8, D 128) over an
+    E4M3 cache with a 1024-key window, every request against the oracle."""
+    case = workloads.make_decode(B=64, Hq=32, Hkv=8, D=128, page_size=16, len_range=(512, 4096),
+                                 dtype=torch.bfloat16, seed=2, num_pages=20000)
+    fp8 = case.fp8_pools()
+    out, lse = _run(case, gpu, fp8, window=1024)
+    ro, rl = _oracle(case, fp8, window=1024)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, "fp8 paged decode window 1024")
 
 
 @pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (128, 8, 2), (64, 8, 8), (256, 16, 2),
