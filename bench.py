@@ -29,6 +29,7 @@ reported baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-flush]
                        [--no-cpu-baseline] [--no-cascade] [--no-fp8] [--no-rope]
+                       [--no-window]
                        [--calibrate-copy MIB]
 Prints one JSON line.
 """
@@ -65,6 +66,8 @@ def main():
                          "the direct paged prefill, so profiles of the latter skip it)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the E4M3-cache decode timing")
     ap.add_argument("--no-rope", action="store_true", help="skip the rotary-embedding decode timing")
+    ap.add_argument("--no-window", action="store_true",
+                    help="skip the sliding-window decode and prefill timings")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="finish with three plain device-to-device copies of MIB MiB, the "
@@ -303,6 +306,67 @@ def main():
             "roofline": roofline_hbm(kv_bytes, r_split, "decode_rope")}
         log("bench: rope decode", res["decode_rope"])
 
+    # Sliding windows on the same workloads: the decode workload with a
+    # 1024-key window (pages before each window never read), the ragged causal
+    # prefill with a 1024-key window, and the ragged workload non-causal with
+    # the band window (512, 256).  Rates count only what the window leaves
+    # visible: K+V bytes of the keys in each window, flops of the visible pairs.
+    if not args.no_window:
+        def timed(fn, kinds):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            for i in range(K):
+                flush()
+                ev[i][0].record(stream)
+                fn()
+                ev_end[i][0].record(stream)
+            torch.cuda.synchronize()
+            ms = sorted(ev[i][0].elapsed_time(ev_end[i][0]) for i in range(K))
+            A.timing_begin(2 * K + 4)
+            for i in range(K):
+                flush()
+                fn()
+            kw = A.timing_end()
+            return ms, {k: kw[k][0] / kw[k][1] for k in kinds if kw[k][1]}
+
+        wdec = 1024
+        w_bytes = 2 * dec.Hkv * dec.D * dec.dtype.itemsize * sum(
+            min(int(x), wdec + 1) for x in dec.kv_lens.tolist())
+        ms, kk = timed(lambda: A.decode_paged(d_q, d_kp, d_vp, d_table, d_lens, scale=dec.scale,
+                                              max_kv_len=dec.max_kv_len, out=d_out, lse=d_lse,
+                                              workspace=d_ws, window_left=wdec),
+                       ("decode_split", "decode_combine"))
+        mean = sum(ms) / K
+        a = w_bytes / (kk["decode_split"] * 1e-3) / 1e9
+        windows = {"decode": {
+            "workload": workloads.CONFIG_NAMES[2], "window_left": wdec, "kv_bytes_visible": w_bytes,
+            "value": round(w_bytes / (mean * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "call_ms": round(mean, 5), "call_ms_stats": stats(ms),
+            "split_kernel_ms": round(kk["decode_split"], 5),
+            "roofline": {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None}}}
+        for name, causal, left, right in (("prefill_causal_window_1024", True, 1024, -1),
+                                          ("prefill_band_512_256", False, 512, 256)):
+            fl = 4 * pre.D * pre.Hq * visible_pairs(pre.lens_q, pre.lens_k, causal, left, right)
+            ms, kk = timed(lambda: A.prefill_varlen(p_q, p_k, p_v, p_cq, p_ck, pre.max_seqlen_q,
+                                                    pre.max_seqlen_k, causal=causal, scale=pre.scale,
+                                                    out=p_out, lse=p_lse, window_left=left,
+                                                    window_right=right), ("prefill",))
+            mean = sum(ms) / K
+            a = fl / (kk["prefill"] * 1e-3) / 1e12
+            windows[name] = {
+                "workload": workloads.CONFIG_NAMES[3], "causal": causal, "window_left": left,
+                "window_right": right, "flops_visible": fl,
+                "value": round(fl / (mean * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                "call_ms": round(mean, 4), "call_ms_stats": stats(ms),
+                "kernel_ms": round(kk["prefill"], 4),
+                "roofline": {"bound": "mfma", "achieved": round(a, 1), "peak": BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(a / BF16_PEAK_TFLOPS, 4),
+                             "traffic": None}}
+        res["windows"] = windows
+        log("bench: windows", windows)
+
     # The chunked workload again through the shared-prefix cascade: one pass
     # of every query row over the 4096 shared tokens, then each request over
     # its own keys with the merge fused into the store.  Same flops as the
@@ -496,6 +560,25 @@ def measured_traffic(kind):
     if rec.get("source_sha256") != source_digest(kind):
         return None
     return int(rec["hbm_bytes_per_launch"])
+
+
+def visible_pairs(lens_q, lens_k, causal, left=-1, right=-1):
+    """(query, key) pairs a windowed attention computes: query i of a sequence
+    sees keys i + (Lk - Lq) - left .. i + (Lk - Lq) + right within 0 .. Lk - 1
+    (-1: that side open; causal is the right bound 0)."""
+    import torch
+    shift = 0 if causal else right
+    tot = 0
+    for lq, lk in zip(lens_q, lens_k):
+        i = torch.arange(lq, dtype=torch.int64)
+        hi = torch.full_like(i, lk - 1)
+        if shift >= 0:
+            hi = torch.minimum(hi, i + (lk - lq) + shift)
+        lo = torch.zeros_like(i)
+        if left >= 0:
+            lo = torch.maximum(lo, i + (lk - lq) - left)
+        tot += int((hi - lo + 1).clamp(min=0).sum())
+    return tot
 
 
 def cpu_baseline(dec, seconds):
