@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -115,16 +116,20 @@ DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int D, int page_size, 
   return pl;
 }
 
-// Compute units of the current device (cached per device id).
+// Compute units of the current device (cached per device id; threads that
+// race on a first query store the same value).
 int device_cus() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     n = 256;
-  if (dev < 64) cache[dev] = n;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
