@@ -61,3 +61,68 @@ def test_decode_and_prefill_replay_in_a_graph(gpu):
         torch.cuda.synchronize()
         for got, ref in zip((d_out, d_lse, o_out, o_lse, p_out, p_lse), refs):
             assert torch.equal(got, ref), f"replay {rep}"
+
+
+def test_more_entry_points_replay_in_a_graph(gpu):
+    """E4M3 decode with a sliding window, paged prefill (HND) with a window on
+    both sides, the shared-prefix cascade (two launches through a workspace)
+    and the state merge, captured together: every replay equals the eager run."""
+    import attention_qk_online_amd as A
+    dec = workloads.make_decode(B=5, Hq=16, Hkv=4, D=128, page_size=16, kv_lens=[33, 400, 16, 1, 250],
+                                dtype=torch.bfloat16, seed=510, extra_pages=3)
+    kb, vb, ks, vs = dec.fp8_pools()
+    f_in = (dec.q.to(gpu), kb.to(gpu), vb.to(gpu), dec.page_table.to(gpu), dec.kv_lens.to(gpu))
+    f_out, f_lse = torch.empty_like(f_in[0]), torch.empty(dec.B, dec.Hq, device=gpu)
+    ws_f = torch.empty(A.decode_paged_workspace_size(torch.bfloat16, dec.B, dec.Hq, dec.Hkv, dec.D, 16,
+                                                     dec.max_kv_len, 0), dtype=torch.uint8, device=gpu)
+    pg = workloads.make_paged_prefill(B=3, Hq=4, Hkv=2, D=128, page_size=16, chunk=90, cached=250,
+                                      shared_prefix=64, dtype=torch.bfloat16, seed=511)
+    h_kp, h_vp = pg.pools(gpu, layout="HND")
+    n_kp, n_vp = pg.pools(gpu)
+    g_in = (pg.q.to(gpu), pg.cu_seqlens_q.to(gpu))
+    g_tab = (pg.page_table.to(gpu), pg.kv_lens.to(gpu))
+    w_out, w_lse = torch.empty_like(g_in[0]), torch.empty(g_in[0].shape[:2], device=gpu)
+    c_out, c_lse = torch.empty_like(g_in[0]), torch.empty(g_in[0].shape[:2], device=gpu)
+    ws_c = torch.empty(A.prefill_paged_cascade_workspace_size(torch.bfloat16, g_in[0].shape[0], pg.Hq,
+                                                              pg.D), dtype=torch.uint8, device=gpu)
+    m_a = torch.randn(300, 4, 128, generator=torch.Generator().manual_seed(512)).to(torch.bfloat16).to(gpu)
+    m_b = torch.randn(300, 4, 128, generator=torch.Generator().manual_seed(513)).to(torch.bfloat16).to(gpu)
+    l_a = torch.randn(300, 4, generator=torch.Generator().manual_seed(514)).to(gpu)
+    l_b = torch.randn(300, 4, generator=torch.Generator().manual_seed(515)).to(gpu)
+    m_out, m_lse = torch.empty_like(m_a), torch.empty_like(l_a)
+    outs = (f_out, f_lse, w_out, w_lse, c_out, c_lse, m_out, m_lse)
+
+    def run():
+        A.decode_paged_fp8(*f_in, ks, vs, scale=dec.scale, max_kv_len=dec.max_kv_len, out=f_out,
+                           lse=f_lse, workspace=ws_f, window_left=37)
+        A.prefill_paged(*g_in, h_kp, h_vp, *g_tab, pg.max_seqlen_q, pg.max_kv_len, causal=False,
+                        scale=pg.scale, out=w_out, lse=w_lse, kv_layout="HND", window_left=70,
+                        window_right=20)
+        A.prefill_paged_cascade(*g_in, n_kp, n_vp, *g_tab, pg.max_seqlen_q, pg.max_kv_len, 64,
+                                causal=True, scale=pg.scale, out=c_out, lse=c_lse, workspace=ws_c)
+        A.merge_states(m_a, l_a, m_b, l_b, out=m_out, lse_out=m_lse)
+
+    run()
+    torch.cuda.synchronize()
+    refs = [t.clone() for t in outs]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+
+    for rep in range(4):
+        for t in outs:
+            t.fill_(float("nan"))
+        # eager work of the program between replays, on other buffers
+        A.prefill_paged(*g_in, n_kp, n_vp, *g_tab, pg.max_seqlen_q, pg.max_kv_len, causal=True,
+                        scale=pg.scale)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip(outs, refs):
+            assert torch.equal(got, ref), f"replay {rep}"
