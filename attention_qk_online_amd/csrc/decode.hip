@@ -763,15 +763,19 @@ __global__ __launch_bounds__(kMaxGroupWaves * 64, D == 256 ? 1 : 2) void decode_
   }
 }
 
-// Merge of the balanced runs: one workgroup per (KV head, request) and one
-// wave per query head of the group; lanes own d.  Pairs held by a single run
-// were written by that run; empty requests get out 0 and lse -inf and
-// inconsistent ones NaN.
-template <typename E, int D, int G>
-__global__ __launch_bounds__(G * 64) void decode_merge_kernel(DecodeParams p) {
+// Merge of the balanced runs: one workgroup per (KV head, request) with S
+// waves per query head of the group, each folding a slice of the pair's
+// segments; with S > 1 (a batch of a few long requests, each split over
+// hundreds of runs) the S partial states of a head are combined through LDS.
+// Lanes own d.  Pairs held by a single run were written by that run; empty
+// requests get out 0 and lse -inf and inconsistent ones NaN.
+template <typename E, int D, int G, int S>
+__global__ __launch_bounds__(G * S * 64) void decode_merge_kernel(DecodeParams p) {
+  constexpr int DL = D / 64 > 0 ? D / 64 : 1;
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = wv / S, sl = wv % S;
   int U = 0, pre = 0;
   for (int c = 0; c < p.B; c += 64) {
     const int bb = c + lane;
@@ -785,33 +789,39 @@ __global__ __launch_bounds__(G * 64) void decode_merge_kernel(DecodeParams p) {
   const int np = pages_of(p, b);
   const int start_pair = pre + (kvh / p.hw) * np;
   const int nseg = np > 0 ? (start_pair + np - 1) / W - start_pair / W + 1 : 0;
-  if (nseg == 1) return;
+  if (nseg == 1) return;                 // the same for every wave of the workgroup
   const int h = kvh * G + g;
   E* og = reinterpret_cast<E*>(p.out) + ((size_t)b * p.Hq + h) * D;
   if (bad || nseg == 0) {
-    const float val = bad ? __builtin_nanf("") : 0.f;
-    for (int d = lane; d < D; d += 64) store_out(og + d, val);
-    if (lane == 0) p.lse[(size_t)b * p.Hq + h] = bad ? val : kNegInf;
+    if (sl == 0) {
+      const float val = bad ? __builtin_nanf("") : 0.f;
+      for (int d = lane; d < D; d += 64) store_out(og + d, val);
+      if (lane == 0) p.lse[(size_t)b * p.Hq + h] = bad ? val : kNegInf;
+    }
     return;
   }
   const size_t slot0 = ((size_t)b * p.Hkv + kvh) * p.max_segs;
   const float* pl = p.part_lse + slot0 * G + g;           // stride G between segments
   const float* po = p.part_o + (slot0 * G + g) * D;       // stride G*D between segments
-  constexpr int DL = D / 64 > 0 ? D / 64 : 1;
+  // This wave's slice of the segments.
+  const int per = (nseg + S - 1) / S;
+  const int s0 = min(nseg, sl * per), s1 = min(nseg, s0 + per);
   float acc[DL] = {};
   float mx = kNegInf, ws = 0.f;
   bool nan_seen = false;
   // Segments in chunks of 64: lane j holds segment j's lse and weight, then
-  // the partial outputs are read eight segments at a time.
-  for (int j0 = 0; j0 < nseg; j0 += 64) {
-    const int nj = min(64, nseg - j0);
+  // the partial outputs are read MB segments at a time (one memory round
+  // trip per batch).
+  constexpr int MB = D > 128 ? 16 : 32;
+  for (int j0 = s0; j0 < s1; j0 += 64) {
+    const int nj = min(64, s1 - j0);
     const float ls = lane < nj ? pl[(size_t)(j0 + lane) * G] : kNegInf;
-    // Partial outputs of segments j0 + j .. j0 + j + 7; the first eight are
-    // requested together with the lse values (one memory round trip less).
-    float v[8][DL];
+    // Partial outputs of segments j0 + j .. j0 + j + MB - 1; the first batch
+    // is requested together with the lse values (one memory round trip less).
+    float v[MB][DL];
     auto load_o = [&](int j) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
+      for (int t = 0; t < MB; ++t)
 #pragma unroll
         for (int i = 0; i < DL; ++i)
           v[t][i] = (j + t < nj && lane + 64 * i < D) ? po[(size_t)(j0 + j + t) * G * D + lane + 64 * i] : 0.f;
@@ -832,23 +842,65 @@ __global__ __launch_bounds__(G * 64) void decode_merge_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < DL; ++i) acc[i] *= resc;
     mx = mnew;
-    for (int j = 0; j < nj; j += 8) {
+    for (int j = 0; j < nj; j += MB) {
       if (j > 0) load_o(j);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < MB; ++t) {
         const float wt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), min(j + t, 63)));
 #pragma unroll
         for (int i = 0; i < DL; ++i) acc[i] += (j + t < nj ? wt : 0.f) * v[t][i];
       }
     }
   }
-  const float mu = mx == kNegInf ? 0.f : mx;
-  const float inv = ws > 0.f ? 1.f / ws : 0.f;
-  float lse_nat = ws > 0.f ? mu + log2_fast(ws) * kLn2 : kNegInf;
-  if (nan_seen) lse_nat = __builtin_nanf("");
+  if constexpr (S == 1) {
+    const float mu = mx == kNegInf ? 0.f : mx;
+    const float inv = ws > 0.f ? 1.f / ws : 0.f;
+    float lse_nat = ws > 0.f ? mu + log2_fast(ws) * kLn2 : kNegInf;
+    if (nan_seen) lse_nat = __builtin_nanf("");
+#pragma unroll
+    for (int i = 0; i < DL; ++i)
+      if (lane + 64 * i < D) store_out(og + lane + 64 * i, nan_seen ? lse_nat : acc[i] * inv);
+    if (lane == 0) p.lse[(size_t)b * p.Hq + h] = lse_nat;
+    return;
+  }
+  // Combine the S slices of each head: weights e^(mx_s - M) over the slices'
+  // maxima M; an empty slice (mx -inf, ws 0, acc 0) adds nothing.
+  __shared__ float sh_acc[16][D];
+  __shared__ float sh_mx[16], sh_ws[16];
+  __shared__ int sh_nan[16];
 #pragma unroll
   for (int i = 0; i < DL; ++i)
-    if (lane + 64 * i < D) store_out(og + lane + 64 * i, nan_seen ? lse_nat : acc[i] * inv);
+    if (lane + 64 * i < D) sh_acc[wv][lane + 64 * i] = acc[i];
+  if (lane == 0) {
+    sh_mx[wv] = mx;
+    sh_ws[wv] = ws;
+    sh_nan[wv] = nan_seen ? 1 : 0;
+  }
+  __syncthreads();
+  if (sl != 0) return;
+  float M = kNegInf;
+  bool any_nan = false;
+#pragma unroll
+  for (int k = 0; k < S; ++k) {
+    M = fmaxf(M, sh_mx[g * S + k]);
+    any_nan |= sh_nan[g * S + k] != 0;
+  }
+  const float mu = M == kNegInf ? 0.f : M;
+  float wtot = 0.f, tot[DL] = {};
+#pragma unroll
+  for (int k = 0; k < S; ++k) {
+    const float f = exp2_fast((sh_mx[g * S + k] - mu) * kLog2e);
+    wtot += f * sh_ws[g * S + k];
+#pragma unroll
+    for (int i = 0; i < DL; ++i)
+      if (lane + 64 * i < D) tot[i] += f * sh_acc[g * S + k][lane + 64 * i];
+  }
+  const float inv = wtot > 0.f ? 1.f / wtot : 0.f;
+  float lse_nat = wtot > 0.f ? mu + log2_fast(wtot) * kLn2 : kNegInf;
+  if (any_nan) lse_nat = __builtin_nanf("");
+#pragma unroll
+  for (int i = 0; i < DL; ++i)
+    if (lane + 64 * i < D) store_out(og + lane + 64 * i, any_nan ? lse_nat : tot[i] * inv);
   if (lane == 0) p.lse[(size_t)b * p.Hq + h] = lse_nat;
 }
 
@@ -938,14 +990,24 @@ hipError_t launch_combine_t(const DecodeParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename E, int D, int G>
+void launch_merge_gs(const DecodeParams& p, hipStream_t s) {
+  // Segment-parallel merge (16 waves) when a pair is expected to span more
+  // than 64 runs, i.e. fewer than one (request, head group) per 64 workgroups.
+  dim3 grid(p.Hkv, p.B);
+  if ((long)p.B * p.nhg * 64 < p.n_groups)
+    hipLaunchKernelGGL((decode_merge_kernel<E, D, G, 16 / G>), grid, dim3(1024), 0, s, p);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<E, D, G, 1>), grid, dim3(G * 64), 0, s, p);
+}
+
 template <typename E, int D>
 hipError_t launch_merge_g(const DecodeParams& p, int G, hipStream_t s) {
-  dim3 grid(p.Hkv, p.B);
   switch (G) {
-    case 1: hipLaunchKernelGGL((decode_merge_kernel<E, D, 1>), grid, dim3(64), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((decode_merge_kernel<E, D, 2>), grid, dim3(128), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((decode_merge_kernel<E, D, 4>), grid, dim3(256), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((decode_merge_kernel<E, D, 8>), grid, dim3(512), 0, s, p); break;
+    case 1: launch_merge_gs<E, D, 1>(p, s); break;
+    case 2: launch_merge_gs<E, D, 2>(p, s); break;
+    case 4: launch_merge_gs<E, D, 4>(p, s); break;
+    case 8: launch_merge_gs<E, D, 8>(p, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

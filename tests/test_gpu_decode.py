@@ -201,3 +201,36 @@ def test_paged_config_fp16(gpu):
     out, lse = _run(case, gpu)
     ro, rl = _oracle(case)
     assert_parity(out, lse, ro, rl, torch.float16, "fp16 paged decode B64")
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv", [(torch.bfloat16, 128, 32, 8), (torch.bfloat16, 64, 8, 8),
+                                            (torch.bfloat16, 256, 16, 2), (torch.float16, 128, 8, 4),
+                                            (torch.bfloat16, 128, 4, 4)])
+def test_few_long_requests(gpu, dtype, D, Hq, Hkv):
+    """One to three long requests: each (request, head group) spans more than
+    64 runs, so the merge folds its segments on several waves per head and
+    combines them through LDS (G = 1, 2, 4, 8); an empty request among them
+    gets out 0 and lse -inf."""
+    for lens in ([20000], [9000, 0, 5000], [12001, 7777]):
+        case = workloads.make_decode(B=len(lens), Hq=Hq, Hkv=Hkv, D=D, page_size=16, kv_lens=lens,
+                                     dtype=dtype, seed=900 + D + Hq + len(lens), extra_pages=3)
+        out, lse = _run(case, gpu)
+        ro, rl = _oracle(case)
+        assert_parity(out, lse, ro, rl, dtype, f"{dtype} D{D} Hq{Hq} Hkv{Hkv} lens {lens}")
+
+
+def test_few_long_requests_bad_page(gpu):
+    """A bad page id in one of two long requests poisons only that request."""
+    import attention_qk_online_amd as A
+    case = workloads.make_decode(B=2, Hq=32, Hkv=8, D=128, page_size=16, kv_lens=[16000, 16000],
+                                 dtype=torch.bfloat16, seed=950, extra_pages=2)
+    ro, rl = _oracle(case)
+    kp, vp = case.pools(gpu)
+    table = case.page_table.clone()
+    table[1, 700] = case.num_pages + 3
+    out, lse = A.decode_paged(case.q.to(gpu), kp, vp, table.to(gpu), case.kv_lens.to(gpu),
+                              scale=case.scale, max_kv_len=case.max_kv_len)
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu()
+    assert_parity(out[0:1], lse[0:1], ro[0:1], rl[0:1], torch.bfloat16, "clean request")
+    assert torch.isnan(out[1].float()).all() and torch.isnan(lse[1]).all()
