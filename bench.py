@@ -75,7 +75,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the kernels shard by request/head with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(the kernels shard by request or head with no exchange; this benchmark measures one GPU)", file=sys.stderr)
         sys.exit(2)
 
     import torch
