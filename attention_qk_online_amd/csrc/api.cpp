@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -94,11 +95,13 @@ DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int D, int page_size, 
   DecodePlan pl{};
   const int max_pages = page_size > 0 ? (max_kv_len + page_size - 1) / page_size : 0;
   if (dtype == ATTN_BF16 || dtype == ATTN_F16) {
-    // A (request, KV head) pair of at most max_pages units spans at most
-    // ceil(max_pages / run) + 1 runs, and every run has >= min_run units.
+    // The balanced schedule counts 16-token blocks, whatever the page size.
+    const int max_blocks = (max_kv_len + 15) / 16;
+    // A (request, KV head) pair of at most max_blocks units spans at most
+    // ceil(max_blocks / run) + 1 runs, and every run has >= min_run units.
     pl.split_pages = split_pages;
     pl.min_run = split_pages > 0 ? split_pages : kMinRun;
-    pl.max_segs = (max_pages + pl.min_run - 1) / pl.min_run + 1;
+    pl.max_segs = (max_blocks + pl.min_run - 1) / pl.min_run + 1;
     const size_t slots = (size_t)B * Hkv * pl.max_segs * (Hq / (Hkv > 0 ? Hkv : 1));
     pl.part_o_elems = slots * D;
     pl.part_lse_elems = slots;
@@ -214,7 +217,12 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int wi
   const int G = Hq / Hkv;
   if (!attn::decode_supported((int)dtype, D, G, page_size))
     return fail(ATTN_E_UNSUPPORTED, "decode: dtype=%d D=%d G=%d page_size=%d not built "
-                "(bf16/f16: D in {64,128,256}; f32: D in {64,128}; G in {1,2,4,8}; page_size 16)", dtype, D, G, page_size);
+                "(bf16/f16: D in {64,128,256}, page_size 16, 32, ..., 256; f32: D in {64,128}, page_size 16; G in {1,2,4,8})", dtype, D, G, page_size);
+  if (dtype != ATTN_F32 &&
+      (long)num_pages * (kv_hnd ? Hkv : 1) * (page_size / 16) > (long)INT_MAX)
+    return fail(ATTN_E_UNSUPPORTED, "decode: num_pages=%d too large for 16-token block ids "
+                "(num_pages * %s page_size/16 must stay below 2^31)", num_pages,
+                kv_hnd ? "Hkv *" : "");
   if (B == 0) return ATTN_OK;
   if (!q || !k_pages || !v_pages || !page_table || !kv_lens || !out || !lse)
     return fail(ATTN_E_NULL, "a required pointer is NULL");
@@ -239,6 +247,9 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int wi
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.num_pages = num_pages; p.max_pages = max_pages_per_req;
   p.max_kv_len = max_kv_len; p.split_pages = pl.split_pages; p.n_splits = pl.n_splits;
   p.min_run = pl.min_run; p.max_segs = pl.max_segs;
+  p.page_shift = 0;
+  while ((16 << p.page_shift) < page_size) ++p.page_shift;   // page_size = 16 << shift (checked)
+  p.max_tokens = (int)std::min<long>((long)max_pages_per_req * page_size, (long)INT_MAX);
   // Balanced bf16 grid: one wave per KV head of a group of up to 8 heads,
   // kDecodeGroupsPerCU workgroups per compute unit.
   p.hw = Hkv < 8 ? Hkv : 8;

@@ -18,6 +18,8 @@
 // 2^(m_old - m_new) ("FlashAttention-3 ..." section 一: online softmax,
 // section 四: keep the rescaling).  Scores are kept in log2 units (scale is
 // premultiplied by log2 e) so the exponentials are single v_exp_f32.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -106,7 +108,7 @@ __device__ __forceinline__ void store_out<f16_t>(f16_t* dst, float x) {
 // (negative, above max_kv_len or above the page table's capacity -> bad).
 __device__ __forceinline__ int request_len(const DecodeParams& p, int b, bool& bad) {
   int kv = p.kv_lens[b];
-  bad = kv < 0 || kv > p.max_kv_len || kv > p.max_pages * kPage;
+  bad = kv < 0 || kv > p.max_kv_len || kv > p.max_tokens;
   return bad ? 0 : kv;
 }
 
@@ -415,7 +417,7 @@ __device__ __forceinline__ typename H::v8 fp8x8(uint32_t w0, uint32_t w1) {
 // group of hw KV heads; wave w of the workgroup folds KV head hg * hw + w of
 // every unit, so a workgroup reads whole pages (all heads of a token are
 // adjacent in the NHD layout).
-template <typename E, int D, int G, int NB, bool F8, bool RP>
+template <typename E, int D, int G, int NB, bool F8, bool RP, bool LP>
 __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1, int W, int lane,
                                            int wave) {
   static_assert(!(RP && F8), "rotary embedding on the 16-bit cache only");
@@ -467,8 +469,24 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
   // Bytes between consecutive tokens of one head, and per page (NHD
   // interleaves the heads of a token, HND keeps each head's 16 rows together).
   const size_t tok_b = p.kv_hnd ? (size_t)GROWB : (size_t)p.Hkv * GROWB;
-  const size_t page_b = (size_t)kPage * p.Hkv * GROWB;
-  const size_t head_b = p.kv_hnd ? (size_t)kPage * GROWB : (size_t)GROWB;
+  // 16-token blocks: block k of a request is block k mod m of page
+  // table[k / m] (m = 1 << page_shift).  Lanes hold block ids: the index of
+  // that block in the pool counted in strides of blk_b (NHD: page * m + sub;
+  // HND: page * Hkv * m + sub, the head adding head_b), or -1 for an
+  // out-of-range page id, so a page step costs what it does with 16-token pages.
+  // With 16-token pages (!LP) a block id is the page id for both layouts.
+  const size_t blk_b = (LP && p.kv_hnd) ? (size_t)kPage * GROWB : (size_t)kPage * p.Hkv * GROWB;
+  const int shift = LP ? p.page_shift : 0;               // LP: pages of more than 16 tokens
+  const size_t head_b = p.kv_hnd ? ((size_t)kPage << shift) * GROWB : (size_t)GROWB;
+  const int blk_mask = (1 << shift) - 1;
+  const int blk_per_page = LP ? (p.kv_hnd ? p.Hkv << shift : 1 << shift) : 1;
+  // Lane value for block k of a table row: with 16-token pages the raw page
+  // id (checked when the page is fetched), else the block id or -1.
+  auto block_id = [&](const int32_t* row, int k) {
+    if constexpr (!LP) return row[k];
+    const int pid = row[k >> shift];
+    return (unsigned)pid < (unsigned)p.num_pages ? pid * blk_per_page + (k & blk_mask) : -1;
+  };
   const float c = p.scale_log2;
   const float qnan = __builtin_nanf("");
 
@@ -518,7 +536,11 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
     const int win_lo = p.window_left >= 0 ? len_b - 1 - p.window_left - p0 * kPage : 0;
 
     typename H::v8 qf[C::KS];
-    const int32_t* table = p.page_table + (size_t)b * p.max_pages + p0 + pg0;
+    // Page-table row of request b; this piece starts at block blk0.
+    // (16-token pages: the row pointer starts at the piece's first page.)
+    const int blk0 = p0 + pg0;
+    const int32_t* table = p.page_table + (size_t)b * p.max_pages + (LP ? 0 : blk0);
+    const int kb = LP ? blk0 : 0;
     int ids0;
     if (b == b_next && hg == hg_next) {        // prefetched during the previous piece
 #pragma unroll
@@ -526,7 +548,7 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
       ids0 = ids_next;
     } else {
       load_q(b, kvh, qf);
-      ids0 = lane < min(64, n) ? table[lane] : 0;
+      ids0 = lane < min(64, n) ? block_id(table, kb + lane) : 0;
     }
     // The next piece of the run starts at page 0 of the next (request, head
     // group) pair with units: fetch its query and first page ids now, so
@@ -543,8 +565,9 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
         const int lq = len_of(bq);
         const int npq = pages_from_len(p, lq);
         load_q(bq, kvq, q_next);
-        const int32_t* tq = p.page_table + (size_t)bq * p.max_pages + window_page0(p, lq);
-        ids_next = lane < min(64, npq) ? tq[lane] : 0;
+        const int w0 = window_page0(p, lq);
+        const int32_t* tq = p.page_table + (size_t)bq * p.max_pages + (LP ? 0 : w0);
+        ids_next = lane < min(64, npq) ? block_id(tq, (LP ? w0 : 0) + lane) : 0;
         b_next = bq;
         hg_next = hq;
       }
@@ -578,7 +601,7 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
 
     for (int c0 = 0; c0 < n; c0 += 64) {
       const int nc = min(64, n - c0);
-      const int ids = c0 == 0 ? ids0 : lane < nc ? table[c0 + lane] : 0;
+      const int ids = c0 == 0 ? ids0 : lane < nc ? block_id(table, kb + c0 + lane) : 0;
       if constexpr (RP) {
         // Angle of this lane's key (token l16 of the page) at the first page of
         // the chunk, exact; later pages advance it by a 16-token rotation.
@@ -587,11 +610,11 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
         for (int j = 0; j < NR; ++j) sincosf(pos * rf[j], &rs[j], &rc[j]);
       }
       auto fetch = [&](int i, Page& pg) {
-        int pid = __builtin_amdgcn_readlane(ids, i);
-        pg.ok = (unsigned)pid < (unsigned)p.num_pages;
-        pid = pg.ok ? pid : 0;
-        const char* kp = kh + (size_t)pid * page_b;
-        const char* vp = vh + (size_t)pid * page_b;
+        int bid = __builtin_amdgcn_readlane(ids, i);
+        pg.ok = LP ? bid >= 0 : (unsigned)bid < (unsigned)p.num_pages;
+        bid = pg.ok ? bid : 0;
+        const char* kp = kh + (size_t)bid * blk_b;
+        const char* vp = vh + (size_t)bid * blk_b;
 #pragma unroll
         for (int j = 0; j < NK; ++j) {
           const int off = F8 ? 64 * j + 16 * gq : (32 * j + 8 * gq) * 2;
@@ -750,7 +773,7 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
   }
 }
 
-template <typename E, int D, int G, int NB, bool F8, bool RP>
+template <typename E, int D, int G, int NB, bool F8, bool RP, bool LP>
 __global__ __launch_bounds__(kMaxGroupWaves * 64, D == 256 ? 1 : 2) void decode_mfma_kernel(DecodeParams p) {
   static_assert(G >= 1 && G <= 16, "one 16-column MFMA tile holds the query heads");
   const int lane = threadIdx.x & 63;
@@ -759,7 +782,7 @@ __global__ __launch_bounds__(kMaxGroupWaves * 64, D == 256 ? 1 : 2) void decode_
   const int U = total_units(p);
   const int W = run_length(p, U);
   for (int run = blockIdx.x; (long)run * W < U; run += gridDim.x) {
-    decode_run<E, D, G, NB, F8, RP>(p, run * W, min(run * W + W, U), W, lane, wave);
+    decode_run<E, D, G, NB, F8, RP, LP>(p, run * W, min(run * W + W, U), W, lane, wave);
   }
 }
 
@@ -939,18 +962,25 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
 template <typename T, int D, int G>
 hipError_t launch_split_t(const DecodeParams& p, bool fp8, bool rope, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    if (fp8)
-      hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, (D == 256 ? 1 : kFp8Batch), true, false>),
-                         dim3(p.n_groups), dim3(p.hw * 64), 0, s, p);
-    else if (rope) {
-      if constexpr (D <= 128)
-        hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, kMfmaBatch, false, true>),
+    // Pages of 16 tokens take instances without the block arithmetic.
+    auto go = [&](auto lp) {
+      constexpr bool LP = decltype(lp)::value;
+      if (fp8)
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, (D == 256 ? 1 : kFp8Batch), true, false, LP>),
                            dim3(p.n_groups), dim3(p.hw * 64), 0, s, p);
-      else
-        return hipErrorInvalidValue;
-    } else
-      hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, (D == 256 ? 1 : kMfmaBatch), false, false>),
-                         dim3(p.n_groups), dim3(p.hw * 64), 0, s, p);
+      else if (rope) {
+        if constexpr (D <= 128)
+          hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, kMfmaBatch, false, true, LP>),
+                             dim3(p.n_groups), dim3(p.hw * 64), 0, s, p);
+        else
+          return hipErrorInvalidValue;
+      } else
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, (D == 256 ? 1 : kMfmaBatch), false, false, LP>),
+                           dim3(p.n_groups), dim3(p.hw * 64), 0, s, p);
+      return hipSuccess;
+    };
+    const hipError_t e = p.page_shift > 0 ? go(std::true_type{}) : go(std::false_type{});
+    if (e != hipSuccess) return e;
   } else {
     if (fp8 || rope) return hipErrorInvalidValue;
     hipLaunchKernelGGL((decode_split_kernel<T, D, G, kBatch>), dim3(p.n_splits, p.Hkv, p.B),
@@ -1018,7 +1048,11 @@ hipError_t launch_merge_g(const DecodeParams& p, int G, hipStream_t s) {
 bool decode_supported(int dtype, int D, int G, int page_size) {
   const bool d_ok = (dtype == 1 || dtype == 2) ? (D == 64 || D == 128 || D == 256)
                                                 : (dtype == 0 && (D == 64 || D == 128));
-  return d_ok && (G == 1 || G == 2 || G == 4 || G == 8) && page_size == kPage;
+  // 16-bit paths: pages of 16, 32, ..., 256 tokens; fp32: 16.
+  const bool p_ok = page_size == kPage ||
+                    (dtype != 0 && page_size <= 16 * kPage && page_size % kPage == 0 &&
+                     ((page_size / kPage) & (page_size / kPage - 1)) == 0);
+  return d_ok && (G == 1 || G == 2 || G == 4 || G == 8) && p_ok;
 }
 
 hipError_t launch_decode_split(const DecodeParams& p, int dtype, int D, int G, bool fp8_kv,

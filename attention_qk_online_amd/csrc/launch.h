@@ -19,6 +19,11 @@ struct DecodeParams {
   float* part_o;           // workspace: partial outputs (layout per kernel below)
   float* part_lse;         // workspace: partial log-sum-exp
   int B, Hq, Hkv, num_pages, max_pages, max_kv_len, split_pages;
+  // Pages hold 16 << page_shift tokens (16-bit path; the fp32 path takes 16
+  // only).  The kernels work in 16-token blocks: block k of a request is
+  // block k & ((1 << page_shift) - 1) of page table[k >> page_shift].
+  int page_shift;
+  int max_tokens;          // max_pages * page size, capped at INT_MAX (table capacity)
   // fp32 split grid: n_splits splits of split_pages pages per request,
   //   part_o [B, n_splits, Hq, D], part_lse [B, n_splits, Hq].
   int n_splits;

@@ -101,7 +101,8 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_F16 = 2 } attn_dtype;
  *  page_table  [B, max_pages_per_req]       int32
  *  kv_lens     [B]                          int32, 0 <= kv_len <= max_kv_len
  *  max_kv_len  host int: an upper bound of every kv_len (sizes the plan)
- *  split_pages host int: run / split length in pages; 0 picks a default
+ *  split_pages host int: run / split length in pages (BF16/F16: in 16-token
+ *              blocks); 0 picks a default
  *  scale       finite float (the caller's softmax scale, usually 1/sqrt(D))
  *  out         [B, Hq, D]                   dtype
  *  lse         [B, Hq]                      float
@@ -110,7 +111,9 @@ typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_F16 = 2 } attn_dtype;
  *              do not matter and are clobbered.
  *
  * Supported: dtype BF16 or F16 with D in {64, 128, 256}, or F32 with D in {64, 128};
- * Hq/Hkv in {1, 2, 4, 8}; page_size 16.  Anything else returns
+ * Hq/Hkv in {1, 2, 4, 8}; page_size 16, 32, 64, 128 or 256 (BF16/F16; the
+ * kernel walks 16-token blocks, so a cache gives the same result bit for bit
+ * whatever its page size) or 16 (F32).  Anything else returns
  * ATTN_E_UNSUPPORTED.  The workspace size depends on dtype, the sizes and
  * split_pages only (not on the device or on kv_lens).
  */

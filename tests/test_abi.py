@@ -63,7 +63,10 @@ def _decode(lib, **kw):
     (dict(scale=float("inf")), E_VALUE),
     (dict(scale=float("nan")), E_VALUE),
     (dict(D=96), E_UNSUP),
-    (dict(P=32, max_pages=4), E_UNSUP),
+    (dict(P=24, max_pages=6), E_UNSUP),       # not 16 << k
+    (dict(P=48, max_pages=3), E_UNSUP),
+    (dict(P=512, max_pages=1), E_UNSUP),      # above 256
+    (dict(dtype=0, P=32, max_pages=4), E_UNSUP),   # fp32: 16 only
     (dict(Hq=32, Hkv=2), E_UNSUP),            # group of 16
     (dict(dtype=0, D=256), E_UNSUP),
     (dict(q=None), E_NULL),
@@ -77,6 +80,12 @@ def _decode(lib, **kw):
 def test_decode_rejects(lib, kw, status):
     assert _decode(lib, **kw) == status
     assert lib.attn_last_error()
+
+
+@pytest.mark.parametrize("P", [32, 64, 128, 256])
+def test_decode_larger_pages_pass_the_checks(lib, P):
+    # B = 0: every argument check runs, nothing is launched
+    assert _decode(lib, P=P, max_pages=max(1, 128 // P), B=0) == OK
 
 
 def test_decode_empty_batch_is_noop(lib):

@@ -234,3 +234,70 @@ def test_few_long_requests_bad_page(gpu):
     out, lse = out.cpu(), lse.cpu()
     assert_parity(out[0:1], lse[0:1], ro[0:1], rl[0:1], torch.bfloat16, "clean request")
     assert torch.isnan(out[1].float()).all() and torch.isnan(lse[1]).all()
+
+
+def _repage16(case, kp, vp):
+    """The same NHD cache seen as 16-token pages (zero copy) and its page table."""
+    m = case.page_size // 16
+    kp16 = kp.reshape(kp.shape[0] * m, 16, *kp.shape[2:])
+    vp16 = vp.reshape(vp.shape[0] * m, 16, *vp.shape[2:])
+    t = case.page_table.long()
+    j = torch.arange(t.shape[1] * m)
+    return kp16, vp16, (t[:, j // m] * m + j % m).to(torch.int32)
+
+
+@pytest.mark.parametrize("P", [32, 64, 256])
+@pytest.mark.parametrize("dtype,D,Hq,Hkv", [(torch.bfloat16, 128, 32, 8), (torch.float16, 64, 8, 8),
+                                            (torch.bfloat16, 256, 16, 2)])
+def test_larger_pages(gpu, P, dtype, D, Hq, Hkv):
+    """Pages of 32 to 256 tokens: parity with the oracle, and the same cache seen
+    as 16-token pages gives the same result bit for bit (the kernel walks
+    16-token blocks either way)."""
+    import attention_qk_online_amd as A
+    lens = [1, 15, 16, 17, 300, 64, 1000, 0, 33, 257]
+    case = workloads.make_decode(B=len(lens), Hq=Hq, Hkv=Hkv, D=D, page_size=P, kv_lens=lens,
+                                 dtype=dtype, seed=960 + P + D, extra_pages=3)
+    ro, rl = _oracle(case)
+    kp, vp = case.pools(gpu)
+    kp16, vp16, t16 = _repage16(case, kp, vp)
+    q, lens_d = case.q.to(gpu), case.kv_lens.to(gpu)
+    for split in (0, 2):
+        out, lse = A.decode_paged(q, kp, vp, case.page_table.to(gpu), lens_d, scale=case.scale,
+                                  max_kv_len=case.max_kv_len, split_pages=split)
+        o16, l16 = A.decode_paged(q, kp16, vp16, t16.to(gpu), lens_d, scale=case.scale,
+                                  max_kv_len=case.max_kv_len, split_pages=split)
+        torch.cuda.synchronize()
+        assert_parity(out, lse, ro, rl, dtype, f"page {P} {dtype} D{D} split {split}")
+        assert torch.equal(out, o16) and torch.equal(lse, l16)
+
+
+def test_larger_pages_variants(gpu):
+    """64-token pages with a sliding window (NHD and HND), the rotary
+    embedding and an E4M3 cache, each against the oracle."""
+    import attention_qk_online_amd as A
+    case = workloads.make_decode(B=5, Hq=16, Hkv=4, D=128, page_size=64, kv_lens=[33, 400, 16, 1, 250],
+                                 dtype=torch.bfloat16, seed=970, extra_pages=3)
+    kc, vc = case.pools("cpu")
+    q, t, lens_d = case.q.to(gpu), case.page_table.to(gpu), case.kv_lens.to(gpu)
+    for layout in ("NHD", "HND"):
+        kp, vp = case.pools(gpu, layout=layout)
+        out, lse = A.decode_paged(q, kp, vp, t, lens_d, scale=case.scale, max_kv_len=case.max_kv_len,
+                                  kv_layout=layout, window_left=37)
+        torch.cuda.synchronize()
+        ro, rl = oracle.ref_decode_paged(case.q, kc, vc, case.page_table, case.kv_lens, case.scale,
+                                         window_left=37)
+        assert_parity(out, lse, ro, rl, torch.bfloat16, f"page 64 {layout} window 37")
+    kp, vp = case.pools(gpu)
+    out, lse = A.decode_paged(q, kp, vp, t, lens_d, scale=case.scale, max_kv_len=case.max_kv_len,
+                              rope_theta=10000.0)
+    torch.cuda.synchronize()
+    ro, rl = oracle.ref_decode_paged(case.q, kc, vc, case.page_table, case.kv_lens, case.scale,
+                                     rope=(10000.0, 1.0))
+    assert_parity(out, lse, ro, rl, torch.bfloat16, "page 64 rope")
+    kb, vb, ks, vs = case.fp8_pools()
+    out, lse = A.decode_paged_fp8(q, kb.to(gpu), vb.to(gpu), t, lens_d, ks, vs, scale=case.scale,
+                                  max_kv_len=case.max_kv_len)
+    torch.cuda.synchronize()
+    ro, rl = oracle.ref_decode_paged_fp8(case.q, kb, vb, ks, vs, case.page_table, case.kv_lens,
+                                         case.scale)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, "page 64 E4M3")
