@@ -29,7 +29,7 @@ reported baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-flush]
                        [--no-cpu-baseline] [--no-cascade] [--no-fp8] [--no-rope]
-                       [--no-window]
+                       [--no-window] [--no-shapes]
                        [--calibrate-copy MIB]
 Prints one JSON line.
 """
@@ -66,6 +66,8 @@ def main():
                          "the direct paged prefill, so profiles of the latter skip it)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the E4M3-cache decode timing")
     ap.add_argument("--no-rope", action="store_true", help="skip the rotary-embedding decode timing")
+    ap.add_argument("--no-shapes", action="store_true",
+                    help="skip the single 32K-request decode and the 64-token-page decode")
     ap.add_argument("--no-window", action="store_true",
                     help="skip the sliding-window decode and prefill timings")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -311,25 +313,27 @@ def main():
     # prefill with a 1024-key window, and the ragged workload non-causal with
     # the band window (512, 256).  Rates count only what the window leaves
     # visible: K+V bytes of the keys in each window, flops of the visible pairs.
-    if not args.no_window:
-        def timed(fn, kinds):
-            for _ in range(2):
-                fn()
-            torch.cuda.synchronize()
-            for i in range(K):
-                flush()
-                ev[i][0].record(stream)
-                fn()
-                ev_end[i][0].record(stream)
-            torch.cuda.synchronize()
-            ms = sorted(ev[i][0].elapsed_time(ev_end[i][0]) for i in range(K))
-            A.timing_begin(2 * K + 4)
-            for i in range(K):
-                flush()
-                fn()
-            kw = A.timing_end()
-            return ms, {k: kw[k][0] / kw[k][1] for k in kinds if kw[k][1]}
+    def timed(fn, kinds):
+        """K calls after a flush each: sorted call times (event pairs) and the
+        mean duration of each kernel kind (the library's launch events)."""
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        for i in range(K):
+            flush()
+            ev[i][0].record(stream)
+            fn()
+            ev_end[i][0].record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(ev[i][0].elapsed_time(ev_end[i][0]) for i in range(K))
+        A.timing_begin(2 * K + 4)
+        for i in range(K):
+            flush()
+            fn()
+        kw = A.timing_end()
+        return ms, {k: kw[k][0] / kw[k][1] for k in kinds if kw[k][1]}
 
+    if not args.no_window:
         wdec = 1024
         w_bytes = 2 * dec.Hkv * dec.D * dec.dtype.itemsize * sum(
             min(int(x), wdec + 1) for x in dec.kv_lens.tolist())
@@ -366,6 +370,39 @@ def main():
                              "traffic": None}}
         res["windows"] = windows
         log("bench: windows", windows)
+
+    # Two more decode shapes of the same model (Hq 32, Hkv 8, D 128, bf16): one
+    # 32768-token request (every head group split over all runs, merged by
+    # the segment-parallel merge), and the decode workload's lengths over a
+    # cache of 64-token pages.
+    if not args.no_shapes:
+        shapes = {}
+        for name, kw in (("b1_kv32768_p16", dict(B=1, page_size=16, kv_lens=[32768], seed=21)),
+                         ("b64_kv512-4096_p64", dict(B=dec.B, page_size=64, kv_lens=dec.kv_lens,
+                                                     seed=22))):
+            c = workloads.make_decode(Hq=dec.Hq, Hkv=dec.Hkv, D=dec.D, dtype=dec.dtype, **kw)
+            s_kp, s_vp = c.pools(dev)
+            s_q, s_t, s_l = c.q.to(dev), c.page_table.to(dev), c.kv_lens.to(dev)
+            s_out, s_lse = torch.empty_like(s_q), torch.empty(c.B, c.Hq, device=dev)
+            s_ws = torch.empty(max(1, A.decode_paged_workspace_size(c.dtype, c.B, c.Hq, c.Hkv, c.D,
+                                                                    c.page_size, c.max_kv_len, 0)),
+                               dtype=torch.uint8, device=dev)
+            ms, kk = timed(lambda: A.decode_paged(s_q, s_kp, s_vp, s_t, s_l, scale=c.scale,
+                                                  max_kv_len=c.max_kv_len, out=s_out, lse=s_lse,
+                                                  workspace=s_ws), ("decode_split", "decode_combine"))
+            nb = c.kv_bytes()
+            mean = sum(ms) / K
+            a = nb / (kk["decode_split"] * 1e-3) / 1e9
+            shapes[name] = {
+                "kv_bytes": nb, "value": round(nb / (mean * 1e-3) / 1e9, 1), "unit": "GB/s",
+                "call_ms": round(mean, 5), "call_ms_stats": stats(ms),
+                "split_kernel_ms": round(kk["decode_split"], 5),
+                "combine_kernel_ms": round(kk.get("decode_combine", 0.0), 5),
+                "roofline": {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None}}
+            del s_kp, s_vp
+        res["decode_shapes"] = shapes
+        log("bench: decode shapes", shapes)
 
     # The chunked workload again through the shared-prefix cascade: one pass
     # of every query row over the 4096 shared tokens, then each request over
