@@ -475,8 +475,12 @@ static attn_status paged_prefill_params(attn_dtype dtype, const void* q,
     return fail(ATTN_E_SHAPE, "negative or zero size (page_size=%d num_pages=%d "
                 "max_pages_per_req=%d max_kv_len=%d)", page_size, num_pages, max_pages_per_req,
                 max_kv_len);
-  if (page_size != 16)
-    return fail(ATTN_E_UNSUPPORTED, "prefill_paged: page_size=%d not built (16)", page_size);
+  if (page_size < 16 || page_size > 256 || (page_size & (page_size - 1)) != 0)
+    return fail(ATTN_E_UNSUPPORTED, "prefill_paged: page_size=%d not built (16, 32, ..., 256)",
+                page_size);
+  if ((long)num_pages * (kv_hnd ? Hkv : 1) * (page_size / 16) > (long)INT_MAX)
+    return fail(ATTN_E_UNSUPPORTED, "prefill_paged: num_pages=%d too large for 16-token block ids",
+                num_pages);
   if ((long)max_kv_len > (long)max_pages_per_req * page_size)
     return fail(ATTN_E_SHAPE, "max_kv_len=%d exceeds max_pages_per_req*page_size=%ld", max_kv_len,
                 (long)max_pages_per_req * page_size);
@@ -499,6 +503,9 @@ static attn_status paged_prefill_params(attn_dtype dtype, const void* q,
   p.kv_hnd = kv_hnd;
   p.window_left = -1;
   p.window_right = -1;
+  p.page_shift = 0;
+  while ((16 << p.page_shift) < page_size) ++p.page_shift;
+  p.max_tokens = (int)std::min<long>((long)max_pages_per_req * page_size, (long)INT_MAX);
   p.q_tiles = (max_seqlen_q + attn::kPrefillBM - 1) / attn::kPrefillBM;
   p.scale_log2 = scale * kLog2e;
   return ATTN_OK;

@@ -82,6 +82,9 @@ struct PrefillParams {
   // window_right; -1 = no bound.  causal is the right window 0 and takes
   // precedence.
   int window_right;
+  // Paged only: pages hold 16 << page_shift tokens; max_tokens = max_pages *
+  // page size (capped at INT_MAX), the capacity of a page-table row.
+  int page_shift, max_tokens;
   float scale_log2;
 };
 

@@ -96,7 +96,7 @@ __device__ __forceinline__ float sum_groups(float x) {
   return sum_halves(x);
 }
 
-template <typename E, bool PAGED>
+template <typename E, bool PAGED, bool LP>
 __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
                                                          const int32_t* __restrict__ page_table) {
   using H = Half16<E>;
@@ -151,15 +151,20 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
   bool bad = Lq > p.max_seqlen_q;
   int k_start = 0, Lk;
   const int32_t* table = nullptr;
+  // LP (pages of 32..256 tokens): table stays at the row start and blk_off
+  // counts the 16-token blocks skipped (key offset, window); a block's page is
+  // table[block >> page_shift].
+  int blk_off = 0;
   if constexpr (PAGED) {
     if (fixed) {
       Lk = p.kv_len_fixed;
       table = page_table;
     } else {
       Lk = p.kv_lens[b] - p.kv_offset;
-      if (Lk < 0 || Lk > p.max_pages * kPage - p.kv_offset) { bad = true; Lk = 0; }
+      if (Lk < 0 || Lk > p.max_tokens - p.kv_offset) { bad = true; Lk = 0; }
       if (p.kv_offset > 0 && p.causal && Lk < Lq) bad = true;
-      table = page_table + (size_t)b * p.table_stride + p.kv_offset / kPage;
+      table = page_table + (size_t)b * p.table_stride + (LP ? 0 : p.kv_offset / kPage);
+      if constexpr (LP) blk_off = p.kv_offset / kPage;
     }
   } else {
     k_start = min(max(p.cu_k[b], 0), p.total_k);
@@ -180,7 +185,10 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
   if (win >= 0) {
     const int kt0 = min(max(0, r0 + off - win), kend) / BN;
     const int sh = kt0 * BN;
-    if constexpr (PAGED) table += sh / kPage;
+    if constexpr (PAGED) {
+      if constexpr (LP) blk_off += sh / kPage;
+      else table += sh / kPage;
+    }
     else k_start += sh;
     Lk -= sh;
     off -= sh;
@@ -216,8 +224,12 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
   // Bytes between consecutive keys of one head: NHD interleaves the heads of
   // a token, HND (paged only) keeps each head's 16 rows of a page together.
   const int kv_rowb = (PAGED && p.kv_hnd) ? ROWB : p.Hkv * ROWB;
-  const size_t page_b = (size_t)kPage * p.Hkv * ROWB;
-  const size_t head_b = (PAGED && p.kv_hnd) ? (size_t)kPage * ROWB : (size_t)ROWB;
+  // A 16-token block is addressed as base + id * page_b + kv head * head_b:
+  // with 16-token pages the id is the page id; with larger pages (LP) it is
+  // page * m + block (NHD, m = 1 << page_shift) or page * Hkv * m + block (HND).
+  const size_t page_b = (LP && p.kv_hnd) ? (size_t)kPage * ROWB : (size_t)kPage * p.Hkv * ROWB;
+  const size_t head_b = (PAGED && p.kv_hnd) ? ((size_t)kPage << (LP ? p.page_shift : 0)) * ROWB
+                                            : (size_t)ROWB;
   const int wrow0 = wave * WROWS;
   const int lane_row = lane / CH, lane_q = lane % CH;
   const int lane_rowb = lane_row * kv_rowb;
@@ -232,8 +244,16 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
   auto load_pid = [&](int t) -> int {
     int pid = 0;
     if constexpr (PAGED) {
-      pid = table[min(t * BN + wrow0, Lk - 1) >> 4];
-      if ((unsigned)pid >= (unsigned)p.num_pages) { bad = true; pid = 0; }
+      if constexpr (LP) {
+        const int k16 = (min(t * BN + wrow0, Lk - 1) >> 4) + blk_off;
+        pid = table[k16 >> p.page_shift];
+        if ((unsigned)pid >= (unsigned)p.num_pages) { bad = true; pid = 0; }
+        pid = pid * (p.kv_hnd ? p.Hkv << p.page_shift : 1 << p.page_shift) +
+              (k16 & ((1 << p.page_shift) - 1));
+      } else {
+        pid = table[min(t * BN + wrow0, Lk - 1) >> 4];
+        if ((unsigned)pid >= (unsigned)p.num_pages) { bad = true; pid = 0; }
+      }
     }
     return pid;
   };
@@ -522,7 +542,10 @@ template <typename E, bool PAGED>
 hipError_t launch16_t(const PrefillParams& p, hipStream_t s) {
   const int total = p.Hq * p.B * p.q_tiles;
   dim3 grid(8 * ((total + 7) / 8));
-  hipLaunchKernelGGL((prefill16_kernel<E, PAGED>), grid, dim3(NT), 0, s, p, p.page_table);
+  if (PAGED && p.page_shift > 0)
+    hipLaunchKernelGGL((prefill16_kernel<E, PAGED, PAGED>), grid, dim3(NT), 0, s, p, p.page_table);
+  else
+    hipLaunchKernelGGL((prefill16_kernel<E, PAGED, false>), grid, dim3(NT), 0, s, p, p.page_table);
   return hipGetLastError();
 }
 

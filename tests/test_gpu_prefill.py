@@ -267,3 +267,49 @@ def test_ragged_config_fp16_sampled(gpu):
     rows = _sample_rows(case.cu_seqlens_q, 64, 33)
     ro, rl = _ref(case, rows=rows)
     assert_parity(out, lse, ro, rl, torch.float16, "fp16 ragged (sampled rows)", rows=rows)
+
+
+def _repage16(case, kp, vp):
+    """The same NHD pools seen as 16-token pages (zero copy) and the page table."""
+    m = case.page_size // 16
+    j = torch.arange(case.page_table.shape[1] * m)
+    t = case.page_table.long()
+    return (kp.reshape(kp.shape[0] * m, 16, *kp.shape[2:]), vp.reshape(vp.shape[0] * m, 16, *vp.shape[2:]),
+            (t[:, j // m] * m + j % m).to(torch.int32))
+
+
+@pytest.mark.parametrize("P", [32, 64, 256])
+@pytest.mark.parametrize("D", [128, 256])
+def test_paged_larger_pages(gpu, P, D):
+    """Pages of 32 to 256 tokens: parity with the oracle (causal, and with a
+    sliding window that skips whole key tiles), bit-for-bit equality with the
+    same cache seen as 16-token pages and with the HND layout, and the
+    shared-prefix cascade."""
+    import attention_qk_online_amd as A
+    case = workloads.make_paged_prefill(B=3, Hq=4, Hkv=2, D=D, page_size=P, chunk=90, cached=422,
+                                        shared_prefix=256, dtype=torch.bfloat16, seed=980 + P + D)
+    kp, vp = case.pools(gpu)
+    kh, vh = case.pools(gpu, layout="HND")
+    kp16, vp16, t16 = _repage16(case, kp, vp)
+    q, cq, lens = case.q.to(gpu), case.cu_seqlens_q.to(gpu), case.kv_lens.to(gpu)
+    t = case.page_table.to(gpu)
+    for window in (-1, 77):
+        out, lse = A.prefill_paged(q, cq, kp, vp, t, lens, case.max_seqlen_q, case.max_kv_len,
+                                   causal=True, scale=case.scale, window_left=window)
+        o16, l16 = A.prefill_paged(q, cq, kp16, vp16, t16.to(gpu), lens, case.max_seqlen_q,
+                                   case.max_kv_len, causal=True, scale=case.scale, window_left=window)
+        oh, lh = A.prefill_paged(q, cq, kh, vh, t, lens, case.max_seqlen_q, case.max_kv_len,
+                                 causal=True, scale=case.scale, kv_layout="HND", window_left=window)
+        torch.cuda.synchronize()
+        ro, rl = oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, case.pool_k, case.pool_v,
+                                          case.page_table, case.kv_lens, True, case.scale,
+                                          window_left=window)
+        assert_parity(out, lse, ro, rl, torch.bfloat16, f"page {P} D{D} window {window}")
+        assert torch.equal(out, o16) and torch.equal(lse, l16)
+        assert torch.equal(out, oh) and torch.equal(lse, lh)
+    out, lse = A.prefill_paged_cascade(q, cq, kp, vp, t, lens, case.max_seqlen_q, case.max_kv_len, 256,
+                                       causal=True, scale=case.scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, case.pool_k, case.pool_v,
+                                      case.page_table, case.kv_lens, True, case.scale)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, f"page {P} D{D} cascade")
