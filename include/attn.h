@@ -197,8 +197,9 @@ attn_status attn_prefill_varlen(attn_dtype dtype, const void* q, const void* k, 
  *  max_seqlen_q, max_kv_len  host bounds
  *  out [total_q, Hq, D] same type;  lse [total_q, Hq] float
  *
- * Supported: dtype BF16 or F16; D in {128, 256}; page_size 16; the same work-item
- * bound as attn_prefill_varlen.
+ * Supported: dtype BF16 or F16; D in {128, 256}; page_size 16, 32, 64, 128 or
+ * 256 (the same cache gives the same result bit for bit whatever its page
+ * size); the same work-item bound as attn_prefill_varlen.
  */
 attn_status attn_prefill_paged(attn_dtype dtype, const void* q, const int32_t* cu_seqlens_q,
                                const void* k_pages, const void* v_pages,
