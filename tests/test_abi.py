@@ -233,6 +233,10 @@ def test_prefill_paged_rejects(lib):
                                       a["num_pages"], a["max_pages"], a["mq"], a["mkv"], a["causal"],
                                       a["scale"], a["out"], a["lse"], None)
     assert call(P=8) == E_UNSUP
+    assert call(P=48, max_pages=2) == E_UNSUP       # not 16 << k
+    assert call(P=512, max_pages=1) == E_UNSUP      # above 256
+    for P in (32, 64, 128, 256):                    # B = 0: every check runs, no launch
+        assert call(P=P, max_pages=max(1, 64 // P), B=0, q=None) == OK
     assert call(mkv=65) == E_SHAPE
     assert call(t=None) == E_NULL
     assert call(D=100) == E_UNSUP
