@@ -23,14 +23,15 @@ reported: the decode workload over an E4M3 (fp8) copy of its cache and
 with the rotary position embedding, the
 chunked workload through the shared-prefix cascade, the launch-bound fp32
 single-sequence decode and the 1K-32K single-sequence
-causal prefill sweep.  The CPU oracle is timed on the host
-cores over the whole decode workload (repeated to at least ~10 s), as a
-reported baseline.
+causal prefill sweep.  The CPU oracle is timed on the host cores beside
+each workload (the whole decode workloads; every n-th query row of the
+prefill workloads, with the exact flops of those rows), as a reported
+baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-flush]
                        [--no-cpu-baseline] [--no-cascade] [--no-fp8] [--no-rope]
-                       [--no-window] [--no-shapes]
-                       [--calibrate-copy MIB]
+                       [--no-window] [--no-shapes] [--sweep-lengths L,...]
+                       [--calibrate-copy MIB] [--only sweep|single]
 Prints one JSON line.
 """
 import argparse
@@ -70,7 +71,13 @@ def main():
                     help="skip the single 32K-request decode and the 64-token-page decode")
     ap.add_argument("--no-window", action="store_true",
                     help="skip the sliding-window decode and prefill timings")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="seconds of CPU-oracle work on the decode workload")
+    ap.add_argument("--only", choices=("sweep", "single"), default=None,
+                    help="profiling aid: run only the 1K-32K prefill sweep or only the fp32 "
+                         "single-sequence decode (their kernels share names with other parts)")
+    ap.add_argument("--sweep-lengths", default=None,
+                    help="comma-separated subset of 1024,4096,16384,32768 for the sweep")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="finish with three plain device-to-device copies of MIB MiB, the "
                          "reference for HBM byte counters read under a profiler")
@@ -86,6 +93,20 @@ def main():
 
     dev = torch.device("cuda:0")
     A.load_library()
+    lengths = SWEEP_LENGTHS if args.sweep_lengths is None else tuple(
+        int(x) for x in args.sweep_lengths.split(","))
+    if any(L not in SWEEP_LENGTHS for L in lengths):
+        print(f"--sweep-lengths takes values from {SWEEP_LENGTHS}", file=sys.stderr)
+        sys.exit(2)
+    if args.only is not None:
+        # Profiling aid: one part on its own, one JSON line with its figures.
+        if args.only == "single":
+            part = bench_single(A, dev, args.steps)
+        else:
+            part = bench_sweep(A, dev, workloads.make_config(4), lengths, args.steps,
+                               lambda: None)
+        print(json.dumps({"only": args.only, "steps": args.steps, args.only: part}), flush=True)
+        return
 
     # ---------------------------------------------------------------- inputs
     log("bench: generating inputs")
@@ -202,6 +223,9 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round((t1 - t0) * 1e3 / K, 4),
+        # ms_per_step is wall time per step and includes the three cache
+        # flushes; this is the hot path alone (mean call times, flushes out).
+        "hot_path_ms_per_step": round(ms_decode + ms_prefill + ms_paged, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -444,14 +468,65 @@ def main():
         log("bench: cascade", res["prefill_paged"]["cascade"])
         del c_ws
 
+    res["decode_fp32_single"] = bench_single(A, dev, K)
+
+    if not args.no_sweep:
+        del p_q, p_k, p_v, p_out, p_lse
+        long = workloads.make_config(4)
+        res["prefill_sweep"] = bench_sweep(A, dev, long, lengths, K, flush)
+
+    if not args.no_cpu_baseline:
+        # The oracle as it stands, on the host cores, after the GPU timing:
+        # one leg per workload (and per sweep length), each placed beside
+        # that workload's GPU figures.
+        threads, tinfo = cpu_threads()
+        torch.set_num_threads(threads)
+        res["cpu_baseline"] = cpu_baseline(dec, args.cpu_seconds, threads)
+        log("bench: cpu baseline (oracle), single fp32 decode")
+        res["decode_fp32_single"]["cpu_baseline"] = cpu_single(workloads.make_config(1), threads)
+        log("bench: cpu baseline (oracle), ragged prefill")
+        res["prefill"]["cpu_baseline"] = cpu_prefill(pre, CPU_STRIDE["prefill"], threads)
+        log("bench: cpu baseline (oracle), chunked paged prefill")
+        res["prefill_paged"]["cpu_baseline"] = cpu_prefill(pg, CPU_STRIDE["prefill_paged"], threads,
+                                                           paged=True)
+        if not args.no_sweep:
+            for L in lengths:
+                log("bench: cpu baseline (oracle), sweep", L)
+                res["prefill_sweep"]["by_length"][str(L)]["cpu_baseline"] = cpu_prefill(
+                    long.prefix(L), CPU_STRIDE["sweep"][L], threads)
+        res["cpu_host"] = dict(tinfo, threads=threads, cpu_model=cpu_model())
+
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["calibrate_copy_bytes"] = n
+
+    print(json.dumps(res), flush=True)
+
+
+def bench_single(A, dev, K):
+    """The launch-bound fp32 single-sequence decode: eager call times and the
+    per-call share of a HIP graph of 20 calls."""
+    import torch
+    import workloads
+    stream = torch.cuda.current_stream(dev)
     # Single-sequence fp32 decode (1 query token, 4 heads, head_dim 64, 256
     # contiguous keys as an identity-paged NHD view): launch-latency bound.
     one = workloads.make_config(1)
     o_kp, o_vp = one.pools(dev)
     o_q, o_t, o_l = one.q.to(dev), one.page_table.to(dev), one.kv_lens.to(dev)
 
+    o_ws = torch.empty(max(1, A.decode_paged_workspace_size(one.dtype, one.B, one.Hq, one.Hkv, one.D,
+                                                            one.page_size, one.max_kv_len, 0)),
+                       dtype=torch.uint8, device=dev)
+
     def single():
-        A.decode_paged(o_q, o_kp, o_vp, o_t, o_l, scale=one.scale, max_kv_len=one.max_kv_len)
+        A.decode_paged(o_q, o_kp, o_vp, o_t, o_l, scale=one.scale, max_kv_len=one.max_kv_len,
+                       workspace=o_ws)
     for _ in range(5):
         single()
     torch.cuda.synchronize()
@@ -463,6 +538,14 @@ def main():
         e1[i].record(stream)
     torch.cuda.synchronize()
     one_ms = sorted(e0[i].elapsed_time(e1[i]) for i in range(K))
+    # Kernel durations (the library's launch events): the split kernel and
+    # the combine of its two partial states.
+    A.timing_begin(2 * K + 4)
+    for i in range(K):
+        single()
+    kk = A.timing_end()
+    split_ms = kk["decode_split"][0] / kk["decode_split"][1]
+    comb_ms = kk["decode_combine"][0] / kk["decode_combine"][1] if kk["decode_combine"][1] else None
     # The same call captured 20 times back to back in one HIP graph (static
     # buffers) and replayed: the per-call share of a replay, as when the
     # decode of many layers is captured together.
@@ -489,56 +572,56 @@ def main():
         e1[i].record(stream)
     torch.cuda.synchronize()
     rep_ms = sorted(e0[i].elapsed_time(e1[i]) / NG for i in range(K))
-    res["decode_fp32_single"] = {
+    return {
         "workload": workloads.CONFIG_NAMES[1], "kv_bytes": one.kv_bytes(),
         "call_us_median": round(one_ms[K // 2] * 1e3, 2), "call_us_min": round(one_ms[0] * 1e3, 2),
         "GBs_at_median": round(one.kv_bytes() / (one_ms[K // 2] * 1e-3) / 1e9, 2),
         "graph_us_per_call_median": round(rep_ms[K // 2] * 1e3, 2),
         "graph_us_per_call_min": round(rep_ms[0] * 1e3, 2),
+        "split_kernel_us": round(split_ms * 1e3, 3),
+        "combine_kernel_us": None if comb_ms is None else round(comb_ms * 1e3, 3),
+        "roofline": {"bound": "hbm", "achieved": round(one.kv_bytes() / (split_ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(one.kv_bytes() / (split_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 5),
+                     "traffic": None},
         "note": "launch-latency bound (512 KiB of KV). Eager: one event pair around one call "
                 "(host overhead included). Graph: 20 calls captured in one graph, replay time / 20"}
 
-    if not args.no_sweep:
-        del p_q, p_k, p_v, p_out, p_lse
-        long = workloads.make_config(4)
-        q, k, v = long.q.to(dev), long.k.to(dev), long.v.to(dev)
-        out = torch.empty_like(q)
-        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
-        sweep = {}
-        for L in (1024, 4096, 16384, 32768):
-            cu = torch.tensor([0, L], dtype=torch.int32, device=dev)
-            fl = workloads.prefill_flops([L], [L], long.Hq, long.D, True)
-            reps = max(3, min(50, int(2e12 / fl * 20)))
 
-            def call():
-                A.prefill_varlen(q[:L], k[:L], v[:L], cu, cu, L, L, causal=True, scale=long.scale,
-                                 out=out[:L], lse=lse[:L])
-            for _ in range(2):
-                call()
-            torch.cuda.synchronize()
-            A.timing_begin(reps + 4)
-            for _ in range(reps):
-                call()
-            kk = A.timing_end()
-            ms = kk["prefill"][0] / kk["prefill"][1]
-            sweep[str(L)] = {"kernel_ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
-                             "frac": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
-            log("bench: sweep", L, sweep[str(L)])
-        res["prefill_sweep"] = {"workload": workloads.CONFIG_NAMES[4], "by_length": sweep}
+SWEEP_LENGTHS = (1024, 4096, 16384, 32768)
 
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(dec, args.cpu_seconds)
 
-    if args.calibrate_copy > 0:
-        n = args.calibrate_copy << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
+def bench_sweep(A, dev, long, lengths, K, flush):
+    """Single-sequence causal prefill over the first L tokens of the 32K
+    workload: mean kernel duration (the library's launch events) per length."""
+    import torch
+    import workloads
+    q, k, v = long.q.to(dev), long.k.to(dev), long.v.to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    sweep = {}
+    for L in lengths:
+        cu = torch.tensor([0, L], dtype=torch.int32, device=dev)
+        fl = workloads.prefill_flops([L], [L], long.Hq, long.D, True)
+        reps = max(3, min(K, int(2e12 / fl * 20)))
+
+        def call():
+            A.prefill_varlen(q[:L], k[:L], v[:L], cu, cu, L, L, causal=True, scale=long.scale,
+                             out=out[:L], lse=lse[:L])
+        for _ in range(2):
+            call()
         torch.cuda.synchronize()
-        res["calibrate_copy_bytes"] = n
-
-    print(json.dumps(res), flush=True)
+        A.timing_begin(reps + 4)
+        for _ in range(reps):
+            flush()
+            call()
+        kk = A.timing_end()
+        ms = kk["prefill"][0] / kk["prefill"][1]
+        sweep[str(L)] = {"flops": fl, "launches": reps, "kernel_ms": round(ms, 4),
+                         "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                         "frac": round(fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        log("bench: sweep", L, sweep[str(L)])
+    return {"workload": workloads.CONFIG_NAMES[4], "by_length": sweep}
 
 
 # Measured HBM traffic per launch (FETCH_SIZE + WRITE_SIZE under rocprofv3,
@@ -618,14 +701,44 @@ def visible_pairs(lens_q, lens_k, causal, left=-1, right=-1):
     return tot
 
 
-def cpu_baseline(dec, seconds):
+def cpu_threads():
+    """Threads for the CPU oracle: the CPUs this process may run on (its
+    affinity mask), bounded by the cgroup CPU quota and by OMP_NUM_THREADS
+    when either is set -- a GPU machine gives one GPU's job a share of the host
+    (os.cpu_count() reports the whole machine).  Returns (threads, details)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    info = {"os_cpu_count": os.cpu_count(), "affinity_cpus": n}
+    try:
+        quota, period = open("/sys/fs/cgroup/cpu.max").read().split()
+        if quota != "max":
+            q = max(1, int(quota) // int(period))
+            info["cgroup_quota_cpus"] = q
+            n = min(n, q)
+    except (OSError, ValueError):
+        pass
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        info["OMP_NUM_THREADS"] = int(omp)
+        n = min(n, int(omp))
+    return max(1, n), info
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
+def cpu_baseline(dec, seconds, threads):
     """The float64 oracle over the whole decode workload on the host cores,
     repeated until at least ``seconds`` have passed; GB/s of algorithmic KV bytes."""
     import torch
     import oracle
-    # The host's CPU share: OMP_NUM_THREADS when set, else at most 16 threads.
-    torch.set_num_threads(int(os.environ.get("OMP_NUM_THREADS") or min(16, os.cpu_count() or 1)))
-    log("bench: cpu baseline (oracle)")
+    log("bench: cpu baseline (oracle), decode")
     # The oracle only reads referenced pages, so the pool is left unfilled elsewhere.
     shape = (dec.num_pages, dec.page_size, dec.Hkv, dec.D)
     kp = torch.empty(shape, dtype=dec.dtype)
@@ -639,19 +752,76 @@ def cpu_baseline(dec, seconds):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
-    cpu_model = ""
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu_model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
     return {"value": round(dec.kv_bytes() * reps / dt / 1e9, 3), "unit": "GB/s",
-            "cores": torch.get_num_threads(), "kind": "oracle",
-            "sample": f"whole decode workload ({dec.B} requests) x {reps} repetitions, "
-                      f"{dt:.1f} s, float64 torch on CPU; os.cpu_count()={os.cpu_count()}",
-            "cpu_model": cpu_model}
+            "cores": threads, "kind": "oracle",
+            "sample": f"whole workload ({dec.B} requests) x {reps} repetitions, {dt:.1f} s, "
+                      f"float64 torch on CPU",
+            "ms_per_call": round(dt * 1e3 / reps, 2)}
+
+
+def sampled_pairs(lens_q, lens_k, rows, causal):
+    """Visible (query, key) pairs per head of the given global query rows
+    (causal: bottom-right aligned), summed."""
+    import bisect
+    cu = [0]
+    for L in lens_q:
+        cu.append(cu[-1] + int(L))
+    tot = 0
+    for r in rows:
+        b = bisect.bisect_right(cu, r) - 1
+        i, lq, lk = r - cu[b], int(lens_q[b]), int(lens_k[b])
+        tot += min(max(i + lk - lq + 1, 0), lk) if causal else lk
+    return tot
+
+
+def cpu_prefill(case, stride, threads, paged=False):
+    """The float64 oracle on every ``stride``-th query row (all heads) of a
+    prefill workload: effective TFLOP/s over the algorithmic flops of those rows."""
+    import torch
+    import oracle
+    Tq = case.q.shape[0]
+    rows = torch.arange(0, Tq, stride)
+    lens_k = case.kv_lens.tolist() if paged else case.lens_k
+    pairs = sampled_pairs(case.lens_q, lens_k, rows.tolist(), case.causal)
+    flops = 4 * case.D * case.Hq * pairs
+    t0 = time.perf_counter()
+    if paged:
+        oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, case.pool_k, case.pool_v,
+                                 case.page_table, case.kv_lens, case.causal, case.scale, rows=rows)
+    else:
+        oracle.ref_prefill_varlen(case.q, case.k, case.v, case.cu_seqlens_q, case.cu_seqlens_k,
+                                  case.causal, case.scale, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{rows.numel()} of {Tq} query rows (every {stride}th row, all {case.Hq} "
+                      f"heads): {pairs} visible pairs per head, {flops} algorithmic flops, "
+                      f"{dt:.2f} s, float64 torch on CPU",
+            "ms": round(dt * 1e3, 1), "flops": flops}
+
+
+def cpu_single(one, threads, seconds=1.0):
+    """The float64 oracle over the single-sequence fp32 decode, repeated for
+    at least ``seconds``."""
+    import oracle
+    kp, vp = one.pools()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.ref_decode_paged(one.q, kp, vp, one.page_table, one.kv_lens, one.scale)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(one.kv_bytes() * reps / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"whole workload x {reps} repetitions, {dt:.2f} s, float64 torch on CPU",
+            "us_per_call": round(dt * 1e6 / reps, 1)}
+
+
+# Row strides of the CPU samples: each leg is a few seconds of float64 work
+# on 16 host threads.
+CPU_STRIDE = {"prefill": 16, "prefill_paged": 16,
+              "sweep": {1024: 1, 4096: 16, 16384: 64, 32768: 128}}
 
 
 if __name__ == "__main__":
