@@ -38,7 +38,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["decode_paged", "decode_paged_fp8", "decode_paged_workspace_size", "prefill_varlen", "prefill_paged",
+__all__ = ["decode_paged", "decode_paged_noalloc", "DECODE_NOALLOC_SCRATCH_BYTES", "decode_paged_fp8",
+           "decode_paged_workspace_size", "prefill_varlen", "prefill_paged",
            "prefill_paged_cascade", "prefill_paged_cascade_workspace_size", "merge_states",
            "timing_begin", "timing_end", "library_path", "load_library", "AttnError",
            "KERNEL_KINDS"]
@@ -82,6 +83,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_decode_paged.restype = c_int
     lib.attn_decode_paged.argtypes = [c_int, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int,
                                       c_int, c_int, c_int, c_int, c_float, vp, vp, vp, c_size, vp]
+    lib.attn_decode_paged_noalloc.restype = c_int
+    lib.attn_decode_paged_noalloc.argtypes = [c_int, vp, vp, vp, vp, vp] + [c_int] * 9 + [
+        c_float, vp, vp, vp]
     lib.attn_decode_paged_fp8.restype = c_int
     lib.attn_decode_paged_fp8.argtypes = [c_int, vp, vp, vp, vp, vp] + [c_int] * 9 + [
         c_float, c_float, c_float, vp, vp, vp, c_size, vp]
@@ -282,6 +286,44 @@ def decode_paged(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
     return _decode(q, k_pages, v_pages, page_table, kv_lens, scale, max_kv_len, split_pages, out,
                    lse, workspace, kv_layout=kv_layout, window_left=window_left,
                    rope=None if rope_theta is None else (rope_theta, rope_scale))
+
+
+DECODE_NOALLOC_SCRATCH_BYTES = 64 << 20   # ATTN_DECODE_NOALLOC_SCRATCH_BYTES in attn.h
+
+
+def decode_paged_noalloc(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                         page_table: torch.Tensor, kv_lens: torch.Tensor, out: torch.Tensor,
+                         lse: torch.Tensor, max_kv_len: int, scale: Optional[float] = None,
+                         split_pages: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """:func:`decode_paged` (NHD pages) that allocates nothing: the caller
+    passes ``out`` [B, Hq, D] and ``lse`` [B, Hq] and the host bound
+    ``max_kv_len``; the partial states live in the library's static per-GPU
+    scratch array (``DECODE_NOALLOC_SCRATCH_BYTES``), so calls that overlap
+    on one GPU race.  For code under graph capture or loops that must not
+    allocate."""
+    lib = load_library()
+    dt = _dtype_code(q)
+    pq = _dev(q, "q", dim=3)
+    pk = _dev(k_pages, "k_pages", q.dtype, 4)
+    pv = _dev(v_pages, "v_pages", q.dtype, 4)
+    pt = _dev(page_table, "page_table", torch.int32, 2)
+    pl = _dev(kv_lens, "kv_lens", torch.int32, 1)
+    B, Hq, D = q.shape
+    num_pages, page_size, Hkv, Dk = k_pages.shape
+    if tuple(v_pages.shape) != tuple(k_pages.shape) or Dk != D:
+        raise ValueError(f"k_pages {tuple(k_pages.shape)} / v_pages {tuple(v_pages.shape)} do not "
+                         f"match q {tuple(q.shape)}")
+    if page_table.shape[0] != B or kv_lens.shape[0] != B:
+        raise ValueError("page_table and kv_lens need one row per request")
+    _dev(out, "out", q.dtype, 3)
+    _dev(lse, "lse", torch.float32, 2)
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq):
+        raise ValueError("out/lse have the wrong shape")
+    _check(lib.attn_decode_paged_noalloc(dt, pq, pk, pv, pt, pl, B, Hq, Hkv, D, page_size,
+                                         num_pages, page_table.shape[1], int(max_kv_len),
+                                         int(split_pages), _scale(scale, D), out.data_ptr(),
+                                         lse.data_ptr(), _stream(q.device)))
+    return out, lse
 
 
 def decode_paged_fp8(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,

@@ -189,7 +189,7 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int wi
                                int page_size, int num_pages, int max_pages_per_req,
                                int max_kv_len, int split_pages, float scale, float k_scale,
                                float v_scale, void* out, float* lse, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               size_t workspace_bytes, void* stream, bool noalloc = false) {
   g_last_error[0] = 0;
   if (!dtype_ok(dtype)) return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32/ATTN_BF16/ATTN_F16", dtype);
   if (fp8_kv && dtype == ATTN_F32)
@@ -229,6 +229,17 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int wi
   if (num_pages == 0 && max_kv_len > 0)
     return fail(ATTN_E_SHAPE, "num_pages is 0 but max_kv_len=%d", max_kv_len);
   const DecodePlan pl = plan_decode((int)dtype, B, Hq, Hkv, D, page_size, max_kv_len, split_pages);
+  if (noalloc && pl.bytes > 0) {
+    // Partial states in the static per-device array instead of a workspace.
+    if (pl.bytes > (size_t)ATTN_DECODE_NOALLOC_SCRATCH_BYTES)
+      return fail(ATTN_E_WORKSPACE,
+                  "decode_paged_noalloc: this call needs %zu bytes of partial state, more than the "
+                  "%zu-byte static scratch array (use attn_decode_paged with a workspace)",
+                  pl.bytes, (size_t)ATTN_DECODE_NOALLOC_SCRATCH_BYTES);
+    const hipError_t e = attn::decode_scratch(&workspace, &workspace_bytes);
+    if (e != hipSuccess)
+      return fail(ATTN_E_HIP, "decode_paged_noalloc: scratch address: %s", hipGetErrorString(e));
+  }
   if (pl.bytes > 0 && (!workspace || workspace_bytes < pl.bytes))
     return fail(ATTN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.bytes,
                 workspace ? workspace_bytes : (size_t)0);
@@ -287,6 +298,18 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pag
                      kv_lens, B, Hq, Hkv, D,
                      page_size, num_pages, max_pages_per_req, max_kv_len, split_pages, scale, 1.f,
                      1.f, out, lse, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_decode_paged_noalloc(attn_dtype dtype, const void* q, const void* k_pages,
+                                      const void* v_pages, const int32_t* page_table,
+                                      const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                                      int page_size, int num_pages, int max_pages_per_req,
+                                      int max_kv_len, int split_pages, float scale, void* out,
+                                      float* lse, void* stream) {
+  return decode_impl(dtype, false, 0, -1, false, 0.f, 0.f, q, k_pages, v_pages, page_table,
+                     kv_lens, B, Hq, Hkv, D, page_size, num_pages, max_pages_per_req, max_kv_len,
+                     split_pages, scale, 1.f, 1.f, out, lse, nullptr, 0, stream,
+                     /*noalloc=*/true);
 }
 
 attn_status attn_decode_paged_hnd(attn_dtype dtype, const void* q, const void* k_pages,

@@ -18,7 +18,10 @@
 // 2^(m_old - m_new) ("FlashAttention-3 ..." section 一: online softmax,
 // section 四: keep the rescaling).  Scores are kept in log2 units (scale is
 // premultiplied by log2 e) so the exponentials are single v_exp_f32.
+#include <atomic>
 #include <type_traits>
+
+#include "attn.h"
 
 #include "common.h"
 #include "launch.h"
@@ -1061,6 +1064,37 @@ hipError_t launch_decode_split(const DecodeParams& p, int dtype, int D, int G, b
     return (fp8_kv || rope) ? hipErrorInvalidValue : launch_split_d<float>(p, D, G, false, false, s);
   return dtype == 1 ? launch_split_d<bf16_t>(p, D, G, fp8_kv, rope, s)
                     : launch_split_d<f16_t>(p, D, G, fp8_kv, rope, s);
+}
+
+// Partial decode states of attn_decode_paged_noalloc, for callers that
+// cannot allocate device memory.  Each GPU the library runs on holds its own
+// copy until the process ends; every call on a GPU shares it, so calls that
+// overlap on one GPU race.  The decode kernels need no particular contents on
+// entry (every slot they read was written earlier in the same call).
+static __device__ __align__(256) char scratch[ATTN_DECODE_NOALLOC_SCRATCH_BYTES];
+
+hipError_t decode_scratch(void** ptr, size_t* bytes) {
+  // In host code `scratch` names a host-side stand-in: kernels get the device
+  // address hipGetSymbolAddress returns, kept per device (racing first calls
+  // store the same value).
+  static std::atomic<void*> cache[64] = {};
+  *bytes = sizeof(scratch);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    void* c = cache[dev].load(std::memory_order_acquire);
+    if (c != nullptr) {
+      *ptr = c;
+      return hipSuccess;
+    }
+  }
+  void* a = nullptr;
+  e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) cache[dev].store(a, std::memory_order_release);
+  *ptr = a;
+  return hipSuccess;
 }
 
 hipError_t launch_decode_combine(const DecodeParams& p, int dtype, int D, int G, hipStream_t s) {

@@ -95,6 +95,10 @@ bool decode_supported(int dtype, int D, int G, int page_size);
 hipError_t launch_decode_split(const DecodeParams& p, int dtype, int D, int G, bool fp8_kv,
                                bool rope, hipStream_t s);
 hipError_t launch_decode_combine(const DecodeParams& p, int dtype, int D, int G, hipStream_t s);
+// Device address of the file-scope decode scratch array (partial states of
+// the allocation-free decode entry point) on the current device, taken once
+// per device with hipGetSymbolAddress; *bytes receives its size.
+hipError_t decode_scratch(void** ptr, size_t* bytes);
 // Workgroups (of up to 8 waves, one per KV head) per CU in the balanced bf16 grid.
 #ifndef ATTN_DECODE_GROUPS_PER_CU
 #define ATTN_DECODE_GROUPS_PER_CU 1

@@ -129,6 +129,35 @@ attn_status attn_decode_paged(attn_dtype dtype, const void* q, const void* k_pag
                               void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* attn_decode_paged for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Arguments, results, supported shapes and NaN rules are those of
+ * attn_decode_paged (NHD pages) without the workspace: the partial states go
+ * to a static device array of ATTN_DECODE_NOALLOC_SCRATCH_BYTES owned by the
+ * library, one per GPU, held until the process ends.  The call allocates
+ * nothing (no hipMalloc / hipFree, no allocating library routine).
+ *
+ *  - A call whose attn_decode_paged_workspace_size(dtype, ...) exceeds
+ *    ATTN_DECODE_NOALLOC_SCRATCH_BYTES returns ATTN_E_WORKSPACE and launches
+ *    nothing (use attn_decode_paged with a workspace then).  The bf16 decode
+ *    of 64 requests of up to 4096 tokens, Hq 32, Hkv 8, D 128 needs ~35 MB.
+ *  - Every call on one GPU uses that GPU's array: calls that overlap on one
+ *    GPU (other streams, other threads, concurrent graph replays) race and
+ *    give undefined results.  Calls ordered on one stream do not.
+ *  - The array's contents on entry do not matter; they keep the last call's
+ *    partial states.
+ *  - The first call on a device looks up the array's device address
+ *    (hipGetSymbolAddress); a failure there returns ATTN_E_HIP.
+ */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES (64u << 20)
+attn_status attn_decode_paged_noalloc(attn_dtype dtype, const void* q, const void* k_pages,
+                                      const void* v_pages, const int32_t* page_table,
+                                      const int32_t* kv_lens, int B, int Hq, int Hkv, int D,
+                                      int page_size, int num_pages, int max_pages_per_req,
+                                      int max_kv_len, int split_pages, float scale, void* out,
+                                      float* lse, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Batched decode over a paged KV cache stored as 8-bit floats E4M3 (FP8 of
  * "FlashInfer内核库深度解析", precision support), one scale per tensor:
  * token t's key is k_scale * E4M3(k byte), its value v_scale * E4M3(v byte).

@@ -82,6 +82,42 @@ def test_decode_rejects(lib, kw, status):
     assert lib.attn_last_error()
 
 
+def _noalloc(lib, **kw):
+    a = dict(dtype=1, q=16, k=16, v=16, table=16, lens=16, B=2, Hq=8, Hkv=2, D=128, P=16,
+             num_pages=100, max_pages=8, max_kv_len=128, split=0, scale=0.1, out=16, lse=16,
+             stream=None)
+    a.update(kw)
+    return lib.attn_decode_paged_noalloc(a["dtype"], a["q"], a["k"], a["v"], a["table"], a["lens"],
+                                         a["B"], a["Hq"], a["Hkv"], a["D"], a["P"], a["num_pages"],
+                                         a["max_pages"], a["max_kv_len"], a["split"], a["scale"],
+                                         a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), E_DTYPE),
+    (dict(Hq=6, Hkv=4), E_SHAPE),
+    (dict(D=96), E_UNSUP),
+    (dict(scale=float("nan")), E_VALUE),
+    (dict(q=None), E_NULL),
+    # partial states above the static array: refused before any HIP call
+    (dict(B=4096, Hq=32, Hkv=8, max_pages=256, max_kv_len=4096, num_pages=300000), E_WS),
+])
+def test_decode_noalloc_rejects(lib, kw, status):
+    assert _noalloc(lib, **kw) == status
+    assert lib.attn_last_error()
+
+
+def test_decode_noalloc_limit_is_the_header_constant(lib):
+    import attention_qk_online_amd as A
+    text = open(HEADER).read()
+    m = re.search(r"#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == A.DECODE_NOALLOC_SCRATCH_BYTES
+    # the largest decode of 64 requests of 4096 tokens (Hq 32, Hkv 8, D 128) fits
+    assert lib.attn_decode_paged_workspace_size(1, 64, 32, 8, 128, 16, 4096, 0) <= \
+        A.DECODE_NOALLOC_SCRATCH_BYTES
+    assert _noalloc(lib, B=0, q=None, k=None) == OK
+
+
 @pytest.mark.parametrize("P", [32, 64, 128, 256])
 def test_decode_larger_pages_pass_the_checks(lib, P):
     # B = 0: every argument check runs, nothing is launched
