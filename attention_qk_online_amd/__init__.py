@@ -41,7 +41,7 @@ import torch
 __all__ = ["decode_paged", "decode_paged_noalloc", "DECODE_NOALLOC_SCRATCH_BYTES", "decode_paged_fp8",
            "decode_paged_workspace_size", "prefill_varlen", "prefill_paged",
            "prefill_paged_cascade", "prefill_paged_cascade_workspace_size", "merge_states",
-           "timing_begin", "timing_end", "library_path", "load_library", "AttnError",
+           "timing_begin", "timing_end", "library_path", "load_library", "AttnError", "AttnValueError",
            "KERNEL_KINDS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +61,10 @@ class AttnError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"libattn: {_STATUS.get(status, status)} error: {detail}")
         self.status = status
+
+
+class AttnValueError(AttnError, ValueError):
+    """A call into libattn.so rejected its arguments (nothing was launched)."""
 
 
 def library_path() -> str:
@@ -127,6 +131,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.attn_status_string.argtypes = [c_int]
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
+    lib.attn_last_hip_error.restype = ctypes.c_char_p
+    lib.attn_last_hip_error.argtypes = []
     lib.attn_timing_begin.restype = c_int
     lib.attn_timing_begin.argtypes = [c_int]
     lib.attn_timing_end.restype = c_int
@@ -139,10 +145,15 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
 
 
 def _check(status: int):
+    """Raise for a non-zero status: ValueError for argument errors (null,
+    shape, dtype, unsupported, value, workspace), AttnError (a RuntimeError)
+    for a failure of the HIP runtime."""
     if status != 0:
         lib = load_library()
-        raise AttnError(status, lib.attn_last_error().decode() or
-                        lib.attn_status_string(status).decode())
+        detail = lib.attn_last_error().decode() or lib.attn_status_string(status).decode()
+        if status == 7:
+            raise AttnError(status, detail + f" [{lib.attn_last_hip_error().decode()}]")
+        raise AttnValueError(status, detail)
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -238,8 +249,11 @@ def _decode(q, k_pages, v_pages, page_table, kv_lens, scale, max_kv_len, split_p
         raise ValueError("out/lse have the wrong shape")
     ws_bytes = int(lib.attn_decode_paged_workspace_size(dt, B, Hq, Hkv, D, page_size, max_kv_len,
                                                         split_pages))
-    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
+    if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < ws_bytes:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                         f"this call needs {ws_bytes} (decode_paged_workspace_size)")
     pw = _dev(workspace, "workspace")
     args = (pq, pk, pv, pt, pl, B, Hq, Hkv, D, page_size, num_pages, page_table.shape[1],
             max_kv_len, split_pages, s)
@@ -487,6 +501,9 @@ def prefill_paged_cascade(q: torch.Tensor, cu_seqlens_q: torch.Tensor, k_pages: 
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     pw = _dev(workspace, "workspace", torch.uint8, 1)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, this call needs {need} "
+                         "(prefill_paged_cascade_workspace_size)")
     _check(getattr(lib, "attn_prefill_paged_cascade" + suffix)(
         dt, pq, pcq, pk, pv, pt, pl, B, Hq, Hkv, D, Tq,
                                           page_size, num_pages, page_table.shape[1],

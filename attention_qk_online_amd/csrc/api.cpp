@@ -19,6 +19,9 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
+// The HIP runtime's text for the error behind the calling thread's last
+// ATTN_E_HIP (empty when its last call returned something else).
+thread_local char g_last_hip_error[256] = "";
 
 attn_status fail(attn_status s, const char* fmt, ...) {
   va_list ap;
@@ -26,6 +29,12 @@ attn_status fail(attn_status s, const char* fmt, ...) {
   vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
   va_end(ap);
   return s;
+}
+
+attn_status fail_hip(hipError_t e, const char* what) {
+  snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s (%s)", hipGetErrorString(e),
+           hipGetErrorName(e));
+  return fail(ATTN_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -158,6 +167,8 @@ const char* attn_status_string(attn_status s) {
 
 const char* attn_last_error(void) { return g_last_error; }
 
+const char* attn_last_hip_error(void) { return g_last_hip_error; }
+
 const char* attn_kernel_name(attn_kernel_kind kind) {
   switch (kind) {
     case ATTN_KERNEL_DECODE_SPLIT: return "decode_split";
@@ -191,6 +202,7 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int wi
                                float v_scale, void* out, float* lse, void* workspace,
                                size_t workspace_bytes, void* stream, bool noalloc = false) {
   g_last_error[0] = 0;
+  g_last_hip_error[0] = 0;
   if (!dtype_ok(dtype)) return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32/ATTN_BF16/ATTN_F16", dtype);
   if (fp8_kv && dtype == ATTN_F32)
     return fail(ATTN_E_UNSUPPORTED, "decode_paged_fp8: queries must be ATTN_BF16 or ATTN_F16");
@@ -238,7 +250,7 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int wi
                   pl.bytes, (size_t)ATTN_DECODE_NOALLOC_SCRATCH_BYTES);
     const hipError_t e = attn::decode_scratch(&workspace, &workspace_bytes);
     if (e != hipSuccess)
-      return fail(ATTN_E_HIP, "decode_paged_noalloc: scratch address: %s", hipGetErrorString(e));
+      return fail_hip(e, "decode_paged_noalloc: scratch address");
   }
   if (pl.bytes > 0 && (!workspace || workspace_bytes < pl.bytes))
     return fail(ATTN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", pl.bytes,
@@ -277,12 +289,12 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int wi
   hipError_t e = timed(ATTN_KERNEL_DECODE_SPLIT, s,
                        [&] { return attn::launch_decode_split(p, (int)dtype, D, G, fp8_kv, rope, s); });
   if (e != hipSuccess)
-    return fail(ATTN_E_HIP, "decode_split launch: %s", hipGetErrorString(e));
+    return fail_hip(e, "decode_split launch");
   if (dtype != ATTN_F32 || pl.n_splits > 1) {
     e = timed(ATTN_KERNEL_DECODE_COMBINE, s,
               [&] { return attn::launch_decode_combine(p, (int)dtype, D, G, s); });
     if (e != hipSuccess)
-      return fail(ATTN_E_HIP, "decode_combine launch: %s", hipGetErrorString(e));
+      return fail_hip(e, "decode_combine launch");
   }
   return ATTN_OK;
 }
@@ -347,6 +359,7 @@ attn_status attn_decode_paged_fp8_window(attn_dtype dtype, int kv_layout, int wi
                                          float* lse, void* workspace, size_t workspace_bytes,
                                          void* stream) {
   g_last_error[0] = 0;
+  g_last_hip_error[0] = 0;
   if (kv_layout != 0 && kv_layout != 1)
     return fail(ATTN_E_VALUE, "kv_layout=%d (0 = NHD, 1 = HND)", kv_layout);
   return decode_impl(dtype, true, kv_layout, window_left, false, 0.f, 0.f, q, k_pages, v_pages,
@@ -363,6 +376,7 @@ attn_status attn_decode_paged_window(attn_dtype dtype, int kv_layout, int window
                                      float scale, void* out, float* lse, void* workspace,
                                      size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
+  g_last_hip_error[0] = 0;
   if (kv_layout != 0 && kv_layout != 1)
     return fail(ATTN_E_VALUE, "kv_layout=%d (0 = NHD, 1 = HND)", kv_layout);
   return decode_impl(dtype, false, kv_layout, window_left, false, 0.f, 0.f, q, k_pages, v_pages,
@@ -380,6 +394,7 @@ attn_status attn_decode_paged_rope(attn_dtype dtype, int kv_layout, int window_l
                                    float scale, void* out, float* lse, void* workspace,
                                    size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
+  g_last_hip_error[0] = 0;
   if (kv_layout != 0 && kv_layout != 1)
     return fail(ATTN_E_VALUE, "kv_layout=%d (0 = NHD, 1 = HND)", kv_layout);
   return decode_impl(dtype, false, kv_layout, window_left, true, rope_theta, rope_scale, q,
@@ -430,6 +445,7 @@ static attn_status prefill_varlen_impl(attn_dtype dtype, const void* q, const vo
                                        int window_right, float scale, void* out, float* lse,
                                        void* stream) {
   g_last_error[0] = 0;
+  g_last_hip_error[0] = 0;
   attn_status st = check_prefill_common(dtype, B, Hq, Hkv, D, total_q, max_seqlen_q, causal, scale);
   if (st != ATTN_OK) return st;
   if (window_left < -1) return fail(ATTN_E_VALUE, "window_left=%d (-1 = no window)", window_left);
@@ -456,7 +472,7 @@ static attn_status prefill_varlen_impl(attn_dtype dtype, const void* q, const vo
   p.window_right = window_right >= span ? -1 : window_right;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = timed(ATTN_KERNEL_PREFILL, s, [&] { return attn::launch_prefill(p, (int)dtype, D, false, s); });
-  if (e != hipSuccess) return fail(ATTN_E_HIP, "prefill launch: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail_hip(e, "prefill launch");
   return ATTN_OK;
 }
 
@@ -544,6 +560,7 @@ static attn_status prefill_paged_impl(attn_dtype dtype, int kv_hnd, int window_l
                                       int causal, float scale, void* out, float* lse,
                                       void* stream) {
   g_last_error[0] = 0;
+  g_last_hip_error[0] = 0;
   attn::PrefillParams p;
   bool empty = false;
   attn_status st = paged_prefill_params(dtype, q, cu_seqlens_q, k_pages, v_pages, page_table,
@@ -561,7 +578,7 @@ static attn_status prefill_paged_impl(attn_dtype dtype, int kv_hnd, int window_l
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e =
       timed(ATTN_KERNEL_PREFILL_PAGED, s, [&] { return attn::launch_prefill(p, (int)dtype, D, true, s); });
-  if (e != hipSuccess) return fail(ATTN_E_HIP, "prefill_paged launch: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail_hip(e, "prefill_paged launch");
   return ATTN_OK;
 }
 
@@ -597,6 +614,7 @@ attn_status attn_prefill_paged_window(attn_dtype dtype, int kv_layout, const voi
                                       int causal, int window_left, int window_right,
                                       float scale, void* out, float* lse, void* stream) {
   g_last_error[0] = 0;
+  g_last_hip_error[0] = 0;
   if (kv_layout != 0 && kv_layout != 1)
     return fail(ATTN_E_VALUE, "kv_layout=%d (0 = NHD, 1 = HND)", kv_layout);
   return prefill_paged_impl(dtype, kv_layout, window_left, window_right, q, cu_seqlens_q, k_pages, v_pages,
@@ -624,6 +642,7 @@ static attn_status cascade_impl(attn_dtype dtype, int kv_hnd, const void* q,
                                        float* lse, void* workspace, size_t workspace_bytes,
                                        void* stream) {
   g_last_error[0] = 0;
+  g_last_hip_error[0] = 0;
   attn::PrefillParams p;
   bool empty = false;
   attn_status st = paged_prefill_params(dtype, q, cu_seqlens_q, k_pages, v_pages, page_table,
@@ -642,7 +661,7 @@ static attn_status cascade_impl(attn_dtype dtype, int kv_hnd, const void* q,
   if (shared_prefix_len == 0) {
     hipError_t e = timed(ATTN_KERNEL_PREFILL_PAGED, s,
                          [&] { return attn::launch_prefill(p, (int)dtype, D, true, s); });
-    if (e != hipSuccess) return fail(ATTN_E_HIP, "prefill_paged launch: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail_hip(e, "prefill_paged launch");
     return ATTN_OK;
   }
   // The shared-prefix pass runs every query row as one sequence.
@@ -672,7 +691,7 @@ static attn_status cascade_impl(attn_dtype dtype, int kv_hnd, const void* q,
   pre.lse = pre_lse;
   hipError_t e = timed(ATTN_KERNEL_CASCADE_PREFIX, s,
                        [&] { return attn::launch_prefill(pre, (int)dtype, D, true, s); });
-  if (e != hipSuccess) return fail(ATTN_E_HIP, "cascade prefix launch: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail_hip(e, "cascade prefix launch");
 
   attn::PrefillParams suf = p;
   suf.kv_offset = shared_prefix_len;
@@ -680,7 +699,7 @@ static attn_status cascade_impl(attn_dtype dtype, int kv_hnd, const void* q,
   suf.merge_lse = pre_lse;
   e = timed(ATTN_KERNEL_CASCADE_SUFFIX, s,
             [&] { return attn::launch_prefill(suf, (int)dtype, D, true, s); });
-  if (e != hipSuccess) return fail(ATTN_E_HIP, "cascade suffix launch: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail_hip(e, "cascade suffix launch");
   return ATTN_OK;
 }
 
@@ -718,6 +737,7 @@ attn_status attn_merge_states(attn_dtype dtype, const void* o_a, const float* ls
                               const void* o_b, const float* lse_b, int rows, int D, void* out,
                               float* lse_out, void* stream) {
   g_last_error[0] = 0;
+  g_last_hip_error[0] = 0;
   if (!dtype_ok(dtype)) return fail(ATTN_E_DTYPE, "dtype %d is not ATTN_F32/ATTN_BF16/ATTN_F16", dtype);
   if (rows < 0 || D <= 0) return fail(ATTN_E_SHAPE, "rows=%d D=%d", rows, D);
   if (!attn::merge_supported((int)dtype, D))
@@ -731,17 +751,23 @@ attn_status attn_merge_states(attn_dtype dtype, const void* o_a, const float* ls
   hipError_t e = timed(ATTN_KERNEL_MERGE, s, [&] {
     return attn::launch_merge_states(o_a, lse_a, o_b, lse_b, out, lse_out, rows, (int)dtype, D, s);
   });
-  if (e != hipSuccess) return fail(ATTN_E_HIP, "merge_states launch: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail_hip(e, "merge_states launch");
   return ATTN_OK;
 }
 
 attn_status attn_timing_begin(int capacity) {
   g_last_error[0] = 0;
+  g_last_hip_error[0] = 0;
   if (capacity <= 0) return fail(ATTN_E_SHAPE, "capacity must be positive");
   while ((int)g_timing.recs.size() < capacity) {
     TimingRecord r{};
-    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess)
-      return fail(ATTN_E_HIP, "hipEventCreate failed");
+    hipError_t e = hipEventCreate(&r.start);
+    if (e != hipSuccess) return fail_hip(e, "hipEventCreate");
+    e = hipEventCreate(&r.stop);
+    if (e != hipSuccess) {
+      (void)hipEventDestroy(r.start);
+      return fail_hip(e, "hipEventCreate");
+    }
     g_timing.recs.push_back(r);
   }
   g_timing.capacity = capacity;
@@ -752,6 +778,7 @@ attn_status attn_timing_begin(int capacity) {
 
 attn_status attn_timing_end(double* ms_per_kind, int* launches_per_kind) {
   g_last_error[0] = 0;
+  g_last_hip_error[0] = 0;
   g_timing.on = false;
   for (int k = 0; k < ATTN_KERNEL_KINDS; ++k) {
     if (ms_per_kind) ms_per_kind[k] = 0.0;
@@ -759,11 +786,11 @@ attn_status attn_timing_end(double* ms_per_kind, int* launches_per_kind) {
   }
   for (int i = 0; i < g_timing.used; ++i) {
     TimingRecord& r = g_timing.recs[i];
-    if (hipEventSynchronize(r.stop) != hipSuccess)
-      return fail(ATTN_E_HIP, "hipEventSynchronize failed");
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
-      return fail(ATTN_E_HIP, "hipEventElapsedTime failed");
+    e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return fail_hip(e, "hipEventElapsedTime");
     if (ms_per_kind) ms_per_kind[r.kind] += ms;
     if (launches_per_kind) launches_per_kind[r.kind] += 1;
   }

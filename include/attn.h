@@ -425,9 +425,15 @@ attn_status attn_prefill_paged_cascade_hnd(attn_dtype dtype, const void* q,
 
 /* ------------------------------------------------------------------------ */
 /* Status text (static strings) and the detail of the calling thread's last
- * failing call (valid until that thread's next call into the library). */
+ * failing call (valid until that thread's next call into the library), after
+ * the error table of "FlashInfer Attention Kernel技术解析" section 3.1 (each
+ * failure named with its cause).  attn_last_hip_error() is the HIP runtime's
+ * own text (hipGetErrorString and hipGetErrorName) for the error behind the
+ * calling thread's last call when it returned ATTN_E_HIP, and "" when that
+ * call returned anything else; attn_last_error() adds which launch failed. */
 const char* attn_status_string(attn_status s);
 const char* attn_last_error(void);
+const char* attn_last_hip_error(void);
 
 /* ------------------------------------------------------------------------ */
 /* Optional kernel timing for benchmarks.  Between attn_timing_begin() and

@@ -352,3 +352,31 @@ def test_binding_fails_loudly_without_library(tmp_path):
 
 def test_timing_api_without_gpu(lib):
     assert lib.attn_timing_begin(0) == E_SHAPE
+
+
+def test_last_hip_error_is_empty_after_argument_errors(lib):
+    assert _decode(lib, B=-1) == E_SHAPE
+    assert lib.attn_last_error() and lib.attn_last_hip_error() == b""
+
+
+def test_hip_failure_is_reported_with_the_runtime_text(lib):
+    """Without a GPU, a launch the argument checks accept fails in the HIP
+    runtime: ATTN_E_HIP, and attn_last_hip_error() carries the runtime's
+    text.  (Skipped where a GPU is visible: the pointers here are not real.)"""
+    if torch.cuda.is_available():
+        pytest.skip("needs a host without a GPU (the call would launch)")
+    assert _decode(lib) == E_HIP
+    assert b"decode" in lib.attn_last_error()
+    assert lib.attn_last_hip_error() != b""
+    assert _decode(lib, B=-1) == E_SHAPE       # cleared by the next call
+    assert lib.attn_last_hip_error() == b""
+
+
+def test_binding_maps_statuses_to_exceptions(lib):
+    import attention_qk_online_amd as A
+    for status in (E_NULL, E_SHAPE, E_DTYPE, E_UNSUP, E_VALUE, E_WS):
+        with pytest.raises(ValueError):
+            A._check(status)
+    with pytest.raises(A.AttnError) as ei:
+        A._check(E_HIP)
+    assert not isinstance(ei.value, ValueError)

@@ -157,8 +157,11 @@ def test_workspace_contents_do_not_matter(gpu):
                                seed=410, extra_pages=5)
     c2 = workloads.make_decode(B=5, Hq=16, Hkv=4, D=128, page_size=16, kv_lens=[300, 2048, 17, 5, 900],
                                dtype=torch.bfloat16, seed=411, extra_pages=3)
-    ws = torch.full((1 << 22,), 0xFF, dtype=torch.uint8, device=gpu)
-    for case, split in ((c1, 2), (c2, 0), (c1, 8), (c2, 1)):
+    calls = ((c1, 2), (c2, 0), (c1, 8), (c2, 1))
+    need = max(A.decode_paged_workspace_size(torch.bfloat16, c.B, c.Hq, c.Hkv, c.D, 16, c.max_kv_len, s)
+               for c, s in calls)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=gpu)
+    for case, split in calls:
         kp, vp = case.pools(gpu)
         args = (case.q.to(gpu), kp, vp, case.page_table.to(gpu), case.kv_lens.to(gpu))
         kw = dict(scale=case.scale, max_kv_len=case.max_kv_len, split_pages=split)
@@ -246,7 +249,7 @@ def _repage16(case, kp, vp):
     return kp16, vp16, (t[:, j // m] * m + j % m).to(torch.int32)
 
 
-@pytest.mark.parametrize("P", [32, 64, 256])
+@pytest.mark.parametrize("P", [32, 64, 128, 256])
 @pytest.mark.parametrize("dtype,D,Hq,Hkv", [(torch.bfloat16, 128, 32, 8), (torch.float16, 64, 8, 8),
                                             (torch.bfloat16, 256, 16, 2)])
 def test_larger_pages(gpu, P, dtype, D, Hq, Hkv):
@@ -301,3 +304,40 @@ def test_larger_pages_variants(gpu):
     ro, rl = oracle.ref_decode_paged_fp8(case.q, kb, vb, ks, vs, case.page_table, case.kv_lens,
                                          case.scale)
     assert_parity(out, lse, ro, rl, torch.bfloat16, "page 64 E4M3")
+
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+@pytest.mark.parametrize("split", [0, 2])
+def test_larger_pages_bad_page(gpu, layout, split):
+    """64-token pages: a table entry outside the pool poisons only its request
+    (NaN out and lse); the others match the oracle."""
+    import attention_qk_online_amd as A
+    case = workloads.make_decode(B=4, Hq=8, Hkv=2, D=128, page_size=64, kv_lens=[100, 300, 70, 1],
+                                 dtype=torch.bfloat16, seed=975, extra_pages=2)
+    ro, rl = _oracle(case)
+    table = case.page_table.clone()
+    table[1, 2] = case.num_pages + 5           # tokens 128..191 of request 1
+    kp, vp = case.pools(gpu, layout=layout)
+    out, lse = A.decode_paged(case.q.to(gpu), kp, vp, table.to(gpu), case.kv_lens.to(gpu),
+                              scale=case.scale, max_kv_len=case.max_kv_len, split_pages=split,
+                              kv_layout=layout)
+    torch.cuda.synchronize()
+    good = torch.tensor([0, 2, 3])
+    assert_parity(out, lse, ro, rl, torch.bfloat16, f"good requests ({layout}, split {split})",
+                  rows=good)
+    assert torch.isnan(out[1].float()).all() and torch.isnan(lse[1]).all()
+
+
+def test_undersized_workspace_is_refused(gpu):
+    """The binding raises on a caller workspace smaller than the size query
+    instead of allocating behind the caller's back."""
+    import attention_qk_online_amd as A
+    case = workloads.make_decode(B=2, Hq=8, Hkv=2, D=128, page_size=16, kv_lens=[300, 40],
+                                 dtype=torch.bfloat16, seed=976)
+    kp, vp = case.pools(gpu)
+    need = A.decode_paged_workspace_size(torch.bfloat16, case.B, case.Hq, case.Hkv, case.D, 16,
+                                         case.max_kv_len, 0)
+    small = torch.empty(need - 1, dtype=torch.uint8, device=gpu)
+    with pytest.raises(ValueError, match="workspace"):
+        A.decode_paged(case.q.to(gpu), kp, vp, case.page_table.to(gpu), case.kv_lens.to(gpu),
+                       scale=case.scale, max_kv_len=case.max_kv_len, workspace=small)

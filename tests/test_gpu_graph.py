@@ -1,10 +1,13 @@
 """The entry points under HIP graph capture: the library only enqueues kernels on
 the caller's stream (no allocation, no synchronisation, no memset), so a captured
-decode / prefill replays to the eager result bit for bit."""
+decode / prefill replays to the eager result bit for bit, and the replayed
+results match the oracle."""
 import pytest
 import torch
 
+import oracle
 import workloads
+from helpers import assert_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -61,6 +64,17 @@ def test_decode_and_prefill_replay_in_a_graph(gpu):
         torch.cuda.synchronize()
         for got, ref in zip((d_out, d_lse, o_out, o_lse, p_out, p_lse), refs):
             assert torch.equal(got, ref), f"replay {rep}"
+
+    # The replayed results against the oracle (not only against the eager run).
+    kc, vc = dec.pools("cpu")
+    ro, rl = oracle.ref_decode_paged(dec.q, kc, vc, dec.page_table, dec.kv_lens, dec.scale)
+    assert_parity(d_out, d_lse, ro, rl, torch.bfloat16, "graph replay: bf16 decode")
+    kc, vc = one.pools("cpu")
+    ro, rl = oracle.ref_decode_paged(one.q, kc, vc, one.page_table, one.kv_lens, one.scale)
+    assert_parity(o_out, o_lse, ro, rl, torch.float32, "graph replay: fp32 decode")
+    ro, rl = oracle.ref_prefill_varlen(pre.q, pre.k, pre.v, pre.cu_seqlens_q, pre.cu_seqlens_k,
+                                       True, pre.scale)
+    assert_parity(p_out, p_lse, ro, rl, torch.bfloat16, "graph replay: causal prefill")
 
 
 def test_more_entry_points_replay_in_a_graph(gpu):
@@ -126,3 +140,16 @@ def test_more_entry_points_replay_in_a_graph(gpu):
         torch.cuda.synchronize()
         for got, ref in zip(outs, refs):
             assert torch.equal(got, ref), f"replay {rep}"
+
+    # The replayed results against the oracle.
+    ro, rl = oracle.ref_decode_paged_fp8(dec.q, kb, vb, ks, vs, dec.page_table, dec.kv_lens, dec.scale,
+                                         window_left=37)
+    assert_parity(f_out, f_lse, ro, rl, torch.bfloat16, "graph replay: E4M3 decode, window 37")
+    ro, rl = oracle.ref_prefill_paged(pg.q, pg.cu_seqlens_q, pg.pool_k, pg.pool_v, pg.page_table,
+                                      pg.kv_lens, False, pg.scale, window_left=70, window_right=20)
+    assert_parity(w_out, w_lse, ro, rl, torch.bfloat16, "graph replay: HND paged prefill, band")
+    ro, rl = oracle.ref_prefill_paged(pg.q, pg.cu_seqlens_q, pg.pool_k, pg.pool_v, pg.page_table,
+                                      pg.kv_lens, True, pg.scale)
+    assert_parity(c_out, c_lse, ro, rl, torch.bfloat16, "graph replay: cascade")
+    ro, rl = oracle.merge_states([(m_a.cpu(), l_a.cpu()), (m_b.cpu(), l_b.cpu())])
+    assert_parity(m_out, m_lse, ro, rl, torch.bfloat16, "graph replay: state merge")

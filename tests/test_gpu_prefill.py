@@ -141,38 +141,57 @@ def test_paged_equals_contiguous_bitwise(gpu):
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
-def test_ragged_config_sampled(gpu):
-    """Ragged causal prefill at full size: B 8, L in [1024, 4096], Hq 64, Hkv 8, D 128."""
+def test_ragged_config_all_rows(gpu):
+    """Ragged causal prefill at full size (B 8, L in [1024, 4096], Hq 64, Hkv 8,
+    D 128): every row of out and lse against the oracle."""
     case = workloads.make_config(3)
     out, lse = _varlen(case, gpu)
-    rows = _sample_rows(case.cu_seqlens_q, 96, 3)
-    ro, rl = _ref(case, rows=rows)
-    assert_parity(out, lse, ro, rl, torch.bfloat16, case.name + " (sampled rows)", rows=rows)
+    ro, rl = _ref(case)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, case.name + " (all rows)")
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
 
 
-def test_long_config_sampled(gpu):
-    """Single 32768-token causal prefill (Hq 64, Hkv 8, D 128), plus the 1K/4K/16K prefixes."""
+def test_long_config_short_prefixes_all_rows(gpu):
+    """The 1K and 4K prefixes of the 32768-token causal prefill (Hq 64, Hkv 8,
+    D 128): every row against the oracle."""
     case = workloads.make_config(4)
-    for L in (1024, 4096, 16384, 32768):
-        sub = case.prefix(L) if L < 32768 else case
+    for L in (1024, 4096):
+        sub = case.prefix(L)
         out, lse = _varlen(sub, gpu)
-        rows = _sample_rows(sub.cu_seqlens_q, 24, L)
-        ro, rl = _ref(sub, rows=rows)
-        assert_parity(out, lse, ro, rl, torch.bfloat16, f"{sub.name} (sampled rows)", rows=rows)
-        assert torch.isfinite(out.float()).all()
+        ro, rl = _ref(sub)
+        assert_parity(out, lse, ro, rl, torch.bfloat16, f"{sub.name} (all rows)")
         del out, lse
 
 
-def test_chunked_paged_config_sampled(gpu):
+def test_long_config_16k_all_rows(gpu):
+    """The 16K prefix of the 32768-token causal prefill: every row."""
+    sub = workloads.make_config(4).prefix(16384)
+    out, lse = _varlen(sub, gpu)
+    ro, rl = _ref(sub)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, f"{sub.name} (all rows)")
+    assert torch.isfinite(out.float()).all()
+
+
+def test_long_config_32k_sampled(gpu):
+    """The whole 32768-token causal prefill: the first and last rows, the rows
+    around the first query tiles' edges and random rows against the oracle
+    (every row would take the float64 oracle minutes); all rows finite."""
+    case = workloads.make_config(4)
+    out, lse = _varlen(case, gpu)
+    rows = _sample_rows(case.cu_seqlens_q, 48, 32768)
+    ro, rl = _ref(case, rows=rows)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, f"{case.name} (sampled rows)", rows=rows)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+def test_chunked_paged_config_all_rows(gpu):
     """Chunked prefill on a paged cache: 16 requests x 512-token chunks over 8192 cached
-    tokens, the first 4096 on shared pages; Hq = Hkv = 16, D 256, page 16."""
+    tokens, the first 4096 on shared pages; Hq = Hkv = 16, D 256, page 16: every row."""
     case = workloads.make_config(5)
     out, lse = _paged(case, gpu)
-    rows = _sample_rows(case.cu_seqlens_q, 48, 5)
     ro, rl = oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, case.pool_k, case.pool_v,
-                                      case.page_table, case.kv_lens, True, case.scale, rows=rows)
-    assert_parity(out, lse, ro, rl, torch.bfloat16, case.name + " (sampled rows)", rows=rows)
+                                      case.page_table, case.kv_lens, True, case.scale)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, case.name + " (all rows)")
     assert torch.isfinite(out.float()).all()
 
 
@@ -278,7 +297,7 @@ def _repage16(case, kp, vp):
             (t[:, j // m] * m + j % m).to(torch.int32))
 
 
-@pytest.mark.parametrize("P", [32, 64, 256])
+@pytest.mark.parametrize("P", [32, 64, 128, 256])
 @pytest.mark.parametrize("D", [128, 256])
 def test_paged_larger_pages(gpu, P, D):
     """Pages of 32 to 256 tokens: parity with the oracle (causal, and with a
@@ -313,3 +332,62 @@ def test_paged_larger_pages(gpu, P, D):
     ro, rl = oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, case.pool_k, case.pool_v,
                                       case.page_table, case.kv_lens, True, case.scale)
     assert_parity(out, lse, ro, rl, torch.bfloat16, f"page {P} D{D} cascade")
+
+
+@pytest.mark.parametrize("P", [32, 64, 128, 256])
+@pytest.mark.parametrize("D", [128, 256])
+def test_paged_larger_pages_ragged(gpu, P, D):
+    """Pages of 32 to 256 tokens with per-request lengths that are multiples of
+    neither 16 nor the page size (partial last pages and partial 16-token
+    blocks, chunks of 1 to 130 queries): parity with the oracle in both page
+    layouts, with and without a sliding window, and through the shared-prefix
+    cascade in both layouts."""
+    import attention_qk_online_amd as A
+    case = workloads.make_paged_prefill(B=4, Hq=4, Hkv=2, D=D, page_size=P, chunk=[90, 17, 1, 130],
+                                        cached=[601, 333, 259, 700], shared_prefix=256,
+                                        dtype=torch.bfloat16, seed=1000 + P + D, spare_pages=2)
+    assert all(int(L) % 16 for L in case.kv_lens)
+    q, cq, lens = case.q.to(gpu), case.cu_seqlens_q.to(gpu), case.kv_lens.to(gpu)
+    t = case.page_table.to(gpu)
+    for layout in ("NHD", "HND"):
+        kp, vp = case.pools(gpu, layout=layout)
+        for window in (-1, 100):
+            out, lse = A.prefill_paged(q, cq, kp, vp, t, lens, case.max_seqlen_q, case.max_kv_len,
+                                       causal=True, scale=case.scale, kv_layout=layout,
+                                       window_left=window)
+            torch.cuda.synchronize()
+            ro, rl = oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, case.pool_k, case.pool_v,
+                                              case.page_table, case.kv_lens, True, case.scale,
+                                              window_left=window)
+            assert_parity(out, lse, ro, rl, torch.bfloat16, f"ragged page {P} D{D} {layout} w{window}")
+        out, lse = A.prefill_paged_cascade(q, cq, kp, vp, t, lens, case.max_seqlen_q, case.max_kv_len,
+                                           256, causal=True, scale=case.scale, kv_layout=layout)
+        torch.cuda.synchronize()
+        ro, rl = oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, case.pool_k, case.pool_v,
+                                          case.page_table, case.kv_lens, True, case.scale)
+        assert_parity(out, lse, ro, rl, torch.bfloat16, f"ragged page {P} D{D} {layout} cascade")
+        del kp, vp
+
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_paged_bad_page_larger_pages(gpu, layout):
+    """64-token pages: a table entry outside the pool (a page every row of that
+    request sees) makes that request's rows NaN; the other requests match the
+    oracle."""
+    import attention_qk_online_amd as A
+    case = workloads.make_paged_prefill(B=3, Hq=4, Hkv=2, D=128, page_size=64, chunk=[40, 33, 70],
+                                        cached=[100, 150, 90], shared_prefix=0,
+                                        dtype=torch.bfloat16, seed=330, spare_pages=1)
+    table = case.page_table.clone()
+    table[1, 1] = case.num_pages + 5           # tokens 64..127 of request 1
+    kp, vp = case.pools(gpu, layout=layout)
+    out, lse = A.prefill_paged(case.q.to(gpu), case.cu_seqlens_q.to(gpu), kp, vp, table.to(gpu),
+                               case.kv_lens.to(gpu), case.max_seqlen_q, case.max_kv_len, causal=True,
+                               scale=case.scale, kv_layout=layout)
+    torch.cuda.synchronize()
+    ro, rl = oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, case.pool_k, case.pool_v,
+                                      case.page_table, case.kv_lens, True, case.scale)
+    c = [int(x) for x in case.cu_seqlens_q]
+    good = torch.cat([torch.arange(c[0], c[1]), torch.arange(c[2], c[3])])
+    assert_parity(out, lse, ro, rl, torch.bfloat16, f"good requests ({layout})", rows=good)
+    assert torch.isnan(out[c[1]:c[2]].float()).all() and torch.isnan(lse[c[1]:c[2]]).all()

@@ -376,48 +376,57 @@ def make_paged_prefill(*, B, Hq, Hkv, D, page_size, chunk, cached, shared_prefix
                        dtype=torch.bfloat16, seed=0, causal=True, scale=None,
                        name="paged_prefill", spare_pages=0) -> PagedPrefillCase:
     """Every request appends a ``chunk``-token query to ``cached`` tokens, so
-    kv_len = cached + chunk.  The first ``shared_prefix`` tokens (a multiple of
-    the page size) sit on pages shared by all requests.
+    kv_len = cached + chunk; ``chunk`` and ``cached`` are one int for every
+    request or a list of B ints.  The first ``shared_prefix`` tokens (a
+    multiple of the page size, at most every request's cached length) sit on
+    pages shared by all requests.
 
     Draw order: page permutation -> Q -> K (shared prefix, then each request's
     private tokens) -> V (same order).
     """
     assert shared_prefix % page_size == 0
     g = _gen(seed)
-    kv_len = cached + chunk
-    n_log = (kv_len + page_size - 1) // page_size
+    chunks = [int(chunk)] * B if isinstance(chunk, int) else [int(c) for c in chunk]
+    cacheds = [int(cached)] * B if isinstance(cached, int) else [int(c) for c in cached]
+    assert len(chunks) == B and len(cacheds) == B and all(c >= shared_prefix for c in cacheds)
+    kv_lens = [c + q for c, q in zip(cacheds, chunks)]
     n_shared = shared_prefix // page_size
-    n_priv = n_log - n_shared
-    num_pages = n_shared + B * n_priv + spare_pages
+    n_log = [(L + page_size - 1) // page_size for L in kv_lens]
+    n_priv = [n - n_shared for n in n_log]
+    num_pages = n_shared + sum(n_priv) + spare_pages
     perm = torch.randperm(num_pages, generator=g)
-    table = torch.empty((B, n_log), dtype=torch.int32)
+    table = torch.full((B, max(n_log) if B else 1), int(perm[-1]) if spare_pages else 0,
+                       dtype=torch.int32)
+    s = n_shared
     for b in range(B):
         table[b, :n_shared] = perm[:n_shared].to(torch.int32)
-        s = n_shared + b * n_priv
-        table[b, n_shared:] = perm[s:s + n_priv].to(torch.int32)
-    q = _randn(g, (B * chunk, Hq, D), dtype)
-    priv_len = kv_len - shared_prefix
+        table[b, n_shared:n_log[b]] = perm[s:s + n_priv[b]].to(torch.int32)
+        s += n_priv[b]
+    q = _randn(g, (sum(chunks), Hq, D), dtype)
+    priv_lens = [L - shared_prefix for L in kv_lens]
     pools = []
     for _ in range(2):  # K then V
         shared = _randn(g, (shared_prefix, Hkv, D), dtype)
-        priv = _randn(g, (B, priv_len, Hkv, D), dtype)
+        priv = _randn(g, (sum(priv_lens), Hkv, D), dtype)
         pool = torch.full((num_pages, page_size, Hkv, D), float("nan"), dtype=dtype)
         flat = pool.view(num_pages * page_size, Hkv, D)
         t = torch.arange(shared_prefix)
         if shared_prefix:
             flat.index_copy_(0, perm[t // page_size].long() * page_size + t % page_size, shared)
+        o = 0
         for b in range(B):
-            tl = torch.arange(shared_prefix, kv_len)
+            tl = torch.arange(shared_prefix, kv_lens[b])
             pid = table[b, (tl // page_size)].long()
-            flat.index_copy_(0, pid * page_size + tl % page_size, priv[b])
+            flat.index_copy_(0, pid * page_size + tl % page_size, priv[o:o + priv_lens[b]])
+            o += priv_lens[b]
         pools.append(pool)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     return PagedPrefillCase(name=name, seed=seed, B=B, Hq=Hq, Hkv=Hkv, D=D, page_size=page_size,
                             num_pages=num_pages, dtype=dtype, causal=bool(causal),
                             scale=float(scale), q=q,
-                            cu_seqlens_q=_cu([chunk] * B),
-                            kv_lens=torch.full((B,), kv_len, dtype=torch.int32),
+                            cu_seqlens_q=_cu(chunks),
+                            kv_lens=torch.tensor(kv_lens, dtype=torch.int32),
                             page_table=table, pool_k=pools[0], pool_v=pools[1],
                             shared_pages=n_shared)
 
