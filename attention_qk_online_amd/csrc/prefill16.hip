@@ -419,6 +419,32 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
       qk(KNXT, snext);
       weights(scur, pb, -m);
       pv(VCUR, pb);
+      // Issue order: eight K fragment reads ahead of the S^T MFMAs, each S^T
+      // MFMA followed by the next K read and two vector ops of the softmax,
+      // the first V^T reads behind the last eight S^T MFMAs, then each O^T
+      // MFMA with the transposing reads of a later fragment.  (Left to the
+      // compiler, the reads ran one or two MFMAs ahead and the waves waited
+      // on LDS before almost every MFMA.)
+      constexpr int KA = 8;
+      __builtin_amdgcn_sched_group_barrier(0x100, KA, 0);             // K reads
+#pragma unroll
+      for (int i = 0; i < KB * QK - KA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // S^T MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);            // next K read
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);            // softmax
+      }
+#pragma unroll
+      for (int i = 0; i < KA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);            // first V reads
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < DB * PS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // O^T MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);            // V reads ahead
+        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+      }
     } else if (kt < w_kt) {
       if (kt < w_lead || kt >= w_fast) mask(kt, scur);
       update_max(scur);
