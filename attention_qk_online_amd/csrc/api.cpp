@@ -66,15 +66,17 @@ hipError_t timed(int kind, hipStream_t s, F&& fn) {
 }
 
 // ------------------------------------------------------------ decode plan ---
-// Pages per split when the caller passes 0: aim for about kUnitsTarget work
-// items over the whole batch (B * Hkv * splits of the longest request), with
-// splits of at least kMinSplitPages pages so partial states stay a small
-// fraction of the KV bytes.
+// fp32 path.  Pages per split when the caller passes 0: aim for about
+// kUnitsTarget work items over the whole batch (B * Hkv * splits of the
+// longest request), with splits of at least kMinSplitPages pages -- two per
+// wave of the split kernel's eight, one batch of loads -- so a short request
+// is one work item (no combine) and partial states stay a small fraction of
+// the KV bytes.
 constexpr int kUnitsTarget = 2048;
-constexpr int kMinSplitPages = 8;
+constexpr int kMinSplitPages = 16;
 // The decode kernel keeps one wave's page ids in a single VGPR: 64 per wave,
-// 4 waves per workgroup.
-constexpr int kMaxSplitPages = 256;
+// 8 waves per workgroup.
+constexpr int kMaxSplitPages = 512;
 
 int auto_split_pages(int B, int Hkv, int max_pages) {
   if (max_pages <= 0) return kMinSplitPages;

@@ -31,7 +31,7 @@ namespace attn {
 namespace {
 
 constexpr int kPage = 16;   // tokens per page handled by this kernel
-constexpr int kNW = 4;      // waves per workgroup (fp32 split kernel)
+constexpr int kNW = 8;      // waves per workgroup (fp32 split kernel)
 constexpr int kMaxGroupWaves = 8;  // KV heads per workgroup (bf16 balanced kernel)
 #ifndef ATTN_DECODE_BATCH
 #define ATTN_DECODE_BATCH 2
