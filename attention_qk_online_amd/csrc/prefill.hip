@@ -561,10 +561,41 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
     inv = __builtin_nanf("");
     lse_v = inv;
   }
+  if (p.merge_lse == nullptr) {
+    // Stage this wave's 32 x D tile through LDS (the K ring is free: every
+    // wave is past its last step) and store whole rows, 16 lanes x 16 bytes
+    // per row: written straight from the O^T layout, each store instruction
+    // would scatter 8-byte pieces over 32 rows.  Chunk q of row r sits at
+    // chunk q ^ (r mod 16) so both passes spread over the banks.
+    char* stage = (wave < 2 ? k_ring0 : k_ring1) + (wave & 1) * 32 * C::ROWB;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        typename H::v4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = (elem)(o[db][a4 * 4 + j] * inv);
+        const int q = db * 4 + a4;
+        *reinterpret_cast<typename H::v4*>(stage + l32 * C::ROWB + ((q ^ (l32 & 15)) << 4) + hl * 8) = v;
+      }
+    }
+    const int c16 = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = i * 4 + (lane >> 4);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * C::ROWB + ((c16 ^ (r & 15)) << 4));
+      const int row = r0 + wave * 32 + r;
+      if (row < Lq)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<elem*>(p.out) +
+                                  ((size_t)(q_start + row) * p.Hq + head) * D + c16 * 8) = x;
+    }
+    if (hl == 0 && row_ok) p.lse[(size_t)(q_start + my_row) * p.Hq + head] = lse_v;
+    return;
+  }
   if (!row_ok) return;
   const size_t orow = (size_t)(q_start + my_row) * p.Hq + head;
   elem* og = reinterpret_cast<elem*>(p.out) + orow * D;
-  if (p.merge_lse != nullptr) {
+  {
     // Merge with another state over disjoint keys: with x = log2 of each
     // normaliser and mx their max, the weights are 2^(x - mx).  Here the
     // accumulator is unnormalised, so its weight per unit is 2^(m - mx).
@@ -600,17 +631,6 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = (elem)(o[db][a4 * 4 + j] * wo + (float)w[j] * wp);
         *reinterpret_cast<typename H::v4*>(og + d0) = v;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        typename H::v4 v;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = (elem)(o[db][a4 * 4 + j] * inv);
-        *reinterpret_cast<typename H::v4*>(og + db * 32 + a4 * 8 + hl * 4) = v;
       }
     }
   }

@@ -519,10 +519,37 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
     inv = __builtin_nanf("");
     lse_v = inv;
   }
+  if (p.merge_lse == nullptr) {
+    // Stage this wave's 16 x D tile through LDS (the K ring is free: every
+    // wave is past its last step) and store whole rows, 32 lanes x 16 bytes
+    // per row, instead of 8-byte pieces scattered over 16 rows per store.
+    // Chunk q of row r sits at chunk q ^ (r mod 16).
+    char* stage = (wave < 4 ? k_ring0 : k_ring1) + (wave & 3) * RW * ROWB;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      typename H::v4 v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = (elem)(o[db][r] * inv);
+      const int q = 2 * db + (grp >> 1);
+      *reinterpret_cast<typename H::v4*>(stage + j16 * ROWB + ((q ^ j16) << 4) + (grp & 1) * 8) = v;
+    }
+    const int c32 = lane & 31;
+#pragma unroll
+    for (int i = 0; i < RW / 2; ++i) {
+      const int r = i * 2 + (lane >> 5);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * ROWB + ((c32 ^ (r & 15)) << 4));
+      const int row = r0 + wave * RW + r;
+      if (row < Lq)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<elem*>(p.out) +
+                                  ((size_t)(q_start + row) * p.Hq + head) * D + c32 * 8) = x;
+    }
+    if (grp == 0 && row_ok) p.lse[(size_t)(q_start + my_row) * p.Hq + head] = lse_v;
+    return;
+  }
   if (!row_ok) return;
   const size_t orow = (size_t)(q_start + my_row) * p.Hq + head;
   elem* og = reinterpret_cast<elem*>(p.out) + orow * D + 4 * grp;
-  if (p.merge_lse != nullptr) {
+  {
     // Merge with another state over disjoint keys (see prefill.hip).
     const float lp = p.merge_lse[orow] * kLog2e;
     const float ls = ltot > 0.f ? m + log2_fast(ltot) : kNegInf;
@@ -550,14 +577,6 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
       if (wp != 0.f) w = *reinterpret_cast<const typename H::v4*>(pg + 16 * db);
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = (elem)(o[db][r] * wo + (float)w[r] * wp);
-      *reinterpret_cast<typename H::v4*>(og + 16 * db) = v;
-    }
-  } else {
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      typename H::v4 v;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (elem)(o[db][r] * inv);
       *reinterpret_cast<typename H::v4*>(og + 16 * db) = v;
     }
   }
