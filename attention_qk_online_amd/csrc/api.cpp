@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <cstdint>
+#include <initializer_list>
 #include <algorithm>
 #include <atomic>
 #include <cmath>
@@ -99,34 +101,58 @@ struct DecodePlan {
 // length to the library: partial states stay well below the KV bytes.
 constexpr int kMinRun = 8;
 
-size_t aligned_bytes(size_t floats) { return (floats * sizeof(float) + 255) & ~(size_t)255; }
+// Size arithmetic that saturates at SIZE_MAX instead of wrapping (a size
+// query then reports SIZE_MAX and the call ATTN_E_SHAPE).
+size_t mul_sat(size_t a, std::initializer_list<long long> xs) {
+  size_t r = a;
+  for (long long x : xs)
+    if (r == SIZE_MAX || x < 0 || __builtin_mul_overflow(r, (size_t)x, &r)) return SIZE_MAX;
+  return r;
+}
+size_t add_sat(size_t a, size_t b) {
+  size_t r;
+  return __builtin_add_overflow(a, b, &r) ? SIZE_MAX : r;
+}
+size_t round256(size_t bytes) { return bytes > SIZE_MAX - 255 ? SIZE_MAX : (bytes + 255) & ~(size_t)255; }
+size_t aligned_bytes(size_t floats) {
+  return floats > SIZE_MAX / sizeof(float) ? SIZE_MAX : round256(floats * sizeof(float));
+}
+
+// True when the product of the non-negative factors is at most `limit`.
+bool product_at_most(std::initializer_list<long long> xs, long long limit) {
+  long long r = 1;
+  for (long long x : xs)
+    if (x < 0 || __builtin_mul_overflow(r, x, &r) || r > limit) return false;
+  return true;
+}
 
 DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int D, int page_size, int max_kv_len,
                        int split_pages) {
   DecodePlan pl{};
-  const int max_pages = page_size > 0 ? (max_kv_len + page_size - 1) / page_size : 0;
+  // Page and block counts of an int length fit an int.
+  const int max_pages = page_size > 0 ? (int)(((long long)max_kv_len + page_size - 1) / page_size) : 0;
   if (dtype == ATTN_BF16 || dtype == ATTN_F16) {
     // The balanced schedule counts 16-token blocks, whatever the page size.
-    const int max_blocks = (max_kv_len + 15) / 16;
+    const long long max_blocks = ((long long)max_kv_len + 15) / 16;
     // A (request, KV head) pair of at most max_blocks units spans at most
     // ceil(max_blocks / run) + 1 runs, and every run has >= min_run units.
     pl.split_pages = split_pages;
     pl.min_run = split_pages > 0 ? split_pages : kMinRun;
-    pl.max_segs = (max_blocks + pl.min_run - 1) / pl.min_run + 1;
-    const size_t slots = (size_t)B * Hkv * pl.max_segs * (Hq / (Hkv > 0 ? Hkv : 1));
-    pl.part_o_elems = slots * D;
+    pl.max_segs = (int)((max_blocks + pl.min_run - 1) / pl.min_run + 1);
+    const size_t slots = mul_sat(1, {B, Hkv, pl.max_segs, Hq / (Hkv > 0 ? Hkv : 1)});
+    pl.part_o_elems = mul_sat(slots, {D});
     pl.part_lse_elems = slots;
-    pl.bytes = aligned_bytes(pl.part_o_elems) + aligned_bytes(pl.part_lse_elems);
+    pl.bytes = add_sat(aligned_bytes(pl.part_o_elems), aligned_bytes(pl.part_lse_elems));
     return pl;
   }
   pl.split_pages = split_pages > 0 ? split_pages : auto_split_pages(B, Hkv, max_pages);
   if (pl.split_pages > kMaxSplitPages) pl.split_pages = kMaxSplitPages;
-  pl.n_splits = max_pages > 0 ? (max_pages + pl.split_pages - 1) / pl.split_pages : 1;
+  pl.n_splits = max_pages > 0 ? (int)(((long long)max_pages + pl.split_pages - 1) / pl.split_pages) : 1;
   if (pl.n_splits < 1) pl.n_splits = 1;
   if (pl.n_splits == 1) return pl;
-  pl.part_o_elems = (size_t)B * pl.n_splits * Hq * D;
-  pl.part_lse_elems = (size_t)B * pl.n_splits * Hq;
-  pl.bytes = aligned_bytes(pl.part_o_elems) + aligned_bytes(pl.part_lse_elems);
+  pl.part_lse_elems = mul_sat(1, {B, pl.n_splits, Hq});
+  pl.part_o_elems = mul_sat(pl.part_lse_elems, {D});
+  pl.bytes = add_sat(aligned_bytes(pl.part_o_elems), aligned_bytes(pl.part_lse_elems));
   return pl;
 }
 
@@ -163,6 +189,7 @@ const char* attn_status_string(attn_status s) {
     case ATTN_E_VALUE: return "invalid value (non-finite scale)";
     case ATTN_E_WORKSPACE: return "workspace missing or too small";
     case ATTN_E_HIP: return "HIP runtime error";
+    default: break;
   }
   return "unknown status";
 }
@@ -227,6 +254,16 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int wi
   if ((long)max_kv_len > (long)max_pages_per_req * page_size)
     return fail(ATTN_E_SHAPE, "max_kv_len=%d exceeds max_pages_per_req*page_size=%ld", max_kv_len,
                 (long)max_pages_per_req * page_size);
+  if (max_kv_len > ATTN_MAX_TOKENS)
+    return fail(ATTN_E_UNSUPPORTED, "max_kv_len=%d exceeds ATTN_MAX_TOKENS=%d", max_kv_len,
+                ATTN_MAX_TOKENS);
+  // The balanced schedule counts (request, head group, 16-token block) units
+  // of the whole batch in an int.
+  if (dtype != ATTN_F32 &&
+      !product_at_most({B, ((long long)max_kv_len + 15) / 16 + 1, ((long long)Hkv + 7) / 8},
+                       ATTN_MAX_TOKENS))
+    return fail(ATTN_E_UNSUPPORTED, "decode: B=%d x (ceil(max_kv_len/16)+1) x ceil(Hkv/8) "
+                "exceeds ATTN_MAX_TOKENS=%d", B, ATTN_MAX_TOKENS);
   if (!std::isfinite(scale)) return fail(ATTN_E_VALUE, "scale is not finite");
   const int G = Hq / Hkv;
   if (!attn::decode_supported((int)dtype, D, G, page_size))
@@ -243,6 +280,8 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int wi
   if (num_pages == 0 && max_kv_len > 0)
     return fail(ATTN_E_SHAPE, "num_pages is 0 but max_kv_len=%d", max_kv_len);
   const DecodePlan pl = plan_decode((int)dtype, B, Hq, Hkv, D, page_size, max_kv_len, split_pages);
+  if (pl.bytes == SIZE_MAX)
+    return fail(ATTN_E_SHAPE, "decode: the workspace size does not fit in size_t");
   if (noalloc && pl.bytes > 0) {
     // Partial states in the static per-device array instead of a workspace.
     if (pl.bytes > (size_t)ATTN_DECODE_NOALLOC_SCRATCH_BYTES)
@@ -278,7 +317,7 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int wi
   // Balanced bf16 grid: one wave per KV head of a group of up to 8 heads,
   // kDecodeGroupsPerCU workgroups per compute unit.
   p.hw = Hkv < 8 ? Hkv : 8;
-  p.nhg = (Hkv + p.hw - 1) / p.hw;
+  p.nhg = (int)(((long long)Hkv + p.hw - 1) / p.hw);
   p.n_groups = attn::kDecodeGroupsPerCU * device_cus();
   p.scale_log2 = fp8_kv ? scale * k_scale * kLog2e : scale * kLog2e;
   p.v_scale = fp8_kv ? v_scale : 1.f;
@@ -425,18 +464,30 @@ static attn_status check_prefill_common(attn_dtype dtype, int B, int Hq, int Hkv
     return fail(ATTN_E_SHAPE, "negative or zero size (B=%d Hq=%d Hkv=%d D=%d total_q=%d "
                 "max_seqlen_q=%d)", B, Hq, Hkv, D, total_q, max_seqlen_q);
   if (Hq % Hkv != 0) return fail(ATTN_E_SHAPE, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (total_q > ATTN_MAX_TOKENS || max_seqlen_q > ATTN_MAX_TOKENS)
+    return fail(ATTN_E_UNSUPPORTED, "total_q=%d or max_seqlen_q=%d exceeds ATTN_MAX_TOKENS=%d",
+                total_q, max_seqlen_q, ATTN_MAX_TOKENS);
   if (causal != 0 && causal != 1) return fail(ATTN_E_VALUE, "causal must be 0 or 1");
   if (!std::isfinite(scale)) return fail(ATTN_E_VALUE, "scale is not finite");
   if (!attn::prefill_supported((int)dtype, D))
     return fail(ATTN_E_UNSUPPORTED, "prefill: dtype=%d D=%d not built (bf16/f16, D in {128,256})",
                 dtype, D);
   // One workgroup per (query head, sequence, query tile), indexed by an int.
-  const long long items =
-      (long long)Hq * B * ((max_seqlen_q + attn::kPrefillBM - 1) / attn::kPrefillBM);
-  if (items > INT_MAX - 8)
-    return fail(ATTN_E_SHAPE, "Hq x B x ceil(max_seqlen_q / %d) = %lld work items exceeds %d",
-                attn::kPrefillBM, items, INT_MAX - 8);
+  const long long tiles = ((long long)max_seqlen_q + attn::kPrefillBM - 1) / attn::kPrefillBM;
+  if (!product_at_most({Hq, B, tiles}, INT_MAX - 8))
+    return fail(ATTN_E_SHAPE, "Hq=%d x B=%d x ceil(max_seqlen_q / %d)=%lld work items exceeds %d",
+                Hq, B, attn::kPrefillBM, tiles, INT_MAX - 8);
   return ATTN_OK;
+}
+
+// Query i of a sequence (Lq <= max_q queries, Lk <= max_k keys) sees keys
+// i + (Lk - Lq) - left .. i + (Lk - Lq) + right.  Since i + (Lk - Lq) lies in
+// [Lk - Lq, Lk - 1], a left side of at least max_k and a right side of at
+// least max_q bound nothing: they become -1, which also keeps the kernels'
+// index sums (at most a length plus a window, each below 2^30) inside an int.
+static void window_clamp(int left, int right, int max_q, int max_k, attn::PrefillParams& p) {
+  p.window_left = left >= max_k ? -1 : left;
+  p.window_right = right >= max_q ? -1 : right;
 }
 
 static attn_status prefill_varlen_impl(attn_dtype dtype, const void* q, const void* k,
@@ -455,6 +506,9 @@ static attn_status prefill_varlen_impl(attn_dtype dtype, const void* q, const vo
     return fail(ATTN_E_VALUE, "window_right=%d (-1 = no bound)", window_right);
   if (total_k < 0 || max_seqlen_k < 0)
     return fail(ATTN_E_SHAPE, "negative total_k=%d or max_seqlen_k=%d", total_k, max_seqlen_k);
+  if (total_k > ATTN_MAX_TOKENS || max_seqlen_k > ATTN_MAX_TOKENS)
+    return fail(ATTN_E_UNSUPPORTED, "total_k=%d or max_seqlen_k=%d exceeds ATTN_MAX_TOKENS=%d",
+                total_k, max_seqlen_k, ATTN_MAX_TOKENS);
   if (B == 0 || max_seqlen_q == 0 || total_q == 0) return ATTN_OK;
   if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !out || !lse)
     return fail(ATTN_E_NULL, "a required pointer is NULL");
@@ -467,11 +521,7 @@ static attn_status prefill_varlen_impl(attn_dtype dtype, const void* q, const vo
   p.max_seqlen_q = max_seqlen_q; p.max_seqlen_k = max_seqlen_k; p.causal = causal;
   p.q_tiles = (max_seqlen_q + attn::kPrefillBM - 1) / attn::kPrefillBM;
   p.scale_log2 = scale * kLog2e;
-  // A window at least as wide as every query-key span bounds nothing; -1
-  // keeps the kernel's index arithmetic small.
-  const long span = (long)max_seqlen_q + max_seqlen_k;
-  p.window_left = window_left >= span ? -1 : window_left;
-  p.window_right = window_right >= span ? -1 : window_right;
+  window_clamp(window_left, window_right, max_seqlen_q, max_seqlen_k, p);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = timed(ATTN_KERNEL_PREFILL, s, [&] { return attn::launch_prefill(p, (int)dtype, D, false, s); });
   if (e != hipSuccess) return fail_hip(e, "prefill launch");
@@ -519,6 +569,9 @@ static attn_status paged_prefill_params(attn_dtype dtype, const void* q,
   if (page_size < 16 || page_size > 256 || (page_size & (page_size - 1)) != 0)
     return fail(ATTN_E_UNSUPPORTED, "prefill_paged: page_size=%d not built (16, 32, ..., 256)",
                 page_size);
+  if (max_kv_len > ATTN_MAX_TOKENS)
+    return fail(ATTN_E_UNSUPPORTED, "max_kv_len=%d exceeds ATTN_MAX_TOKENS=%d", max_kv_len,
+                ATTN_MAX_TOKENS);
   if ((long)num_pages * (kv_hnd ? Hkv : 1) * (page_size / 16) > (long)INT_MAX)
     return fail(ATTN_E_UNSUPPORTED, "prefill_paged: num_pages=%d too large for 16-token block ids",
                 num_pages);
@@ -574,9 +627,7 @@ static attn_status prefill_paged_impl(attn_dtype dtype, int kv_hnd, int window_l
   if (window_right < -1)
     return fail(ATTN_E_VALUE, "window_right=%d (-1 = no bound)", window_right);
   if (empty) return ATTN_OK;
-  const long span = (long)max_seqlen_q + max_kv_len;   // as in the ragged call
-  p.window_left = window_left >= span ? -1 : window_left;
-  p.window_right = window_right >= span ? -1 : window_right;
+  window_clamp(window_left, window_right, max_seqlen_q, max_kv_len, p);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e =
       timed(ATTN_KERNEL_PREFILL_PAGED, s, [&] { return attn::launch_prefill(p, (int)dtype, D, true, s); });
@@ -626,12 +677,11 @@ attn_status attn_prefill_paged_window(attn_dtype dtype, int kv_layout, const voi
 }
 
 static size_t elem_bytes(attn_dtype dtype) { return dtype == ATTN_F32 ? 4 : 2; }
-static size_t round256(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
 
 size_t attn_prefill_paged_cascade_workspace_size(attn_dtype dtype, int total_q, int Hq, int D) {
   if (!dtype_ok(dtype) || total_q < 0 || Hq <= 0 || D <= 0) return 0;
-  const size_t rows = (size_t)total_q * Hq;
-  return round256(rows * D * elem_bytes(dtype)) + round256(rows * sizeof(float));
+  const size_t rows = mul_sat(1, {total_q, Hq});
+  return add_sat(round256(mul_sat(rows, {D, (long long)elem_bytes(dtype)})), aligned_bytes(rows));
 }
 
 static attn_status cascade_impl(attn_dtype dtype, int kv_hnd, const void* q,
@@ -667,11 +717,10 @@ static attn_status cascade_impl(attn_dtype dtype, int kv_hnd, const void* q,
     return ATTN_OK;
   }
   // The shared-prefix pass runs every query row as one sequence.
-  const long long items =
-      (long long)Hq * ((total_q + attn::kPrefillBM - 1) / attn::kPrefillBM);
-  if (items > INT_MAX - 8)
-    return fail(ATTN_E_SHAPE, "Hq x ceil(total_q / %d) = %lld work items exceeds %d",
-                attn::kPrefillBM, items, INT_MAX - 8);
+  const long long tiles = ((long long)total_q + attn::kPrefillBM - 1) / attn::kPrefillBM;
+  if (!product_at_most({Hq, tiles}, INT_MAX - 8))
+    return fail(ATTN_E_SHAPE, "Hq=%d x ceil(total_q / %d)=%lld work items exceeds %d", Hq,
+                attn::kPrefillBM, tiles, INT_MAX - 8);
   const size_t need = attn_prefill_paged_cascade_workspace_size(dtype, total_q, Hq, D);
   if (!workspace || workspace_bytes < need)
     return fail(ATTN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -681,7 +730,7 @@ static attn_status cascade_impl(attn_dtype dtype, int kv_hnd, const void* q,
   void* pre_o = workspace;
   float* pre_lse = reinterpret_cast<float*>(
       reinterpret_cast<char*>(workspace) +
-      round256((size_t)total_q * Hq * D * elem_bytes(dtype)));
+      round256(mul_sat(1, {total_q, Hq, D, (long long)elem_bytes(dtype)})));
 
   attn::PrefillParams pre = p;
   pre.B = 1;
@@ -760,7 +809,9 @@ attn_status attn_merge_states(attn_dtype dtype, const void* o_a, const float* ls
 attn_status attn_timing_begin(int capacity) {
   g_last_error[0] = 0;
   g_last_hip_error[0] = 0;
-  if (capacity <= 0) return fail(ATTN_E_SHAPE, "capacity must be positive");
+  if (capacity <= 0 || capacity > ATTN_TIMING_MAX_LAUNCHES)
+    return fail(ATTN_E_SHAPE, "capacity=%d outside 1 .. ATTN_TIMING_MAX_LAUNCHES=%d", capacity,
+                ATTN_TIMING_MAX_LAUNCHES);
   while ((int)g_timing.recs.size() < capacity) {
     TimingRecord r{};
     hipError_t e = hipEventCreate(&r.start);

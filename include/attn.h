@@ -52,10 +52,19 @@
  *    rows of a sequence longer than max_seqlen_q (or whose kv_len exceeds
  *    max_pages_per_req * page_size), are NaN; of such a sequence only its
  *    first ceil(max_seqlen_q / 128) * 128 rows are written.
+ *  - Size limits: every token count and length argument (total_q, total_k,
+ *    max_seqlen_q, max_seqlen_k, max_kv_len) is at most ATTN_MAX_TOKENS
+ *    (2^30), and a 16-bit decode batch keeps B * (ceil(max_kv_len / 16) + 1)
+ *    * ceil(Hkv / 8) at most ATTN_MAX_TOKENS; larger values return
+ *    ATTN_E_UNSUPPORTED.  Within these limits every index sum on the host and
+ *    in the kernels fits a 32-bit int.  A workspace size that does not fit a
+ *    size_t is returned as SIZE_MAX by the size queries and rejected with
+ *    ATTN_E_SHAPE by the calls.
  */
 #ifndef ATTN_H
 #define ATTN_H
 
+#include <limits.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -71,10 +80,25 @@ typedef enum {
   ATTN_E_UNSUPPORTED = 4, /* valid request that this build has no kernel for     */
   ATTN_E_VALUE = 5,       /* a non-finite scale                                   */
   ATTN_E_WORKSPACE = 6,   /* workspace missing or smaller than the size query     */
-  ATTN_E_HIP = 7          /* the HIP runtime rejected a launch                    */
+  ATTN_E_HIP = 7,         /* the HIP runtime rejected a launch                    */
+  /* range markers, never returned: any int passed to attn_status_string is
+   * a value of the type */
+  ATTN_STATUS_RANGE_MIN_ = INT_MIN,
+  ATTN_STATUS_RANGE_MAX_ = INT_MAX
 } attn_status;
 
-typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_F16 = 2 } attn_dtype;
+/* The two range markers are not element types: they make every int a value
+ * of the enumeration, so that an out-of-range dtype from a caller is a
+ * defined value that the entry points reject with ATTN_E_DTYPE. */
+typedef enum {
+  ATTN_F32 = 0,
+  ATTN_BF16 = 1,
+  ATTN_F16 = 2,
+  ATTN_DTYPE_RANGE_MIN_ = INT_MIN,
+  ATTN_DTYPE_RANGE_MAX_ = INT_MAX
+} attn_dtype;
+
+#define ATTN_MAX_TOKENS (1 << 30)
 
 /* ------------------------------------------------------------------------ */
 /* Batched decode over a paged KV cache.
@@ -441,7 +465,9 @@ const char* attn_last_hip_error(void);
  * pair of hipEvents recorded on its launch stream.  attn_timing_end() waits
  * for those events and returns, per kernel kind, the summed milliseconds and
  * the number of launches.  Process-wide, not thread-safe; it creates HIP
- * events (no device memory).  At most `capacity` launches are recorded. */
+ * events (no device memory).  At most `capacity` launches are recorded;
+ * capacity must be 1 .. ATTN_TIMING_MAX_LAUNCHES (else ATTN_E_SHAPE). */
+#define ATTN_TIMING_MAX_LAUNCHES (1 << 20)
 typedef enum {
   ATTN_KERNEL_DECODE_SPLIT = 0,
   ATTN_KERNEL_DECODE_COMBINE = 1,
@@ -450,7 +476,10 @@ typedef enum {
   ATTN_KERNEL_MERGE = 4,
   ATTN_KERNEL_CASCADE_PREFIX = 5,
   ATTN_KERNEL_CASCADE_SUFFIX = 6,
-  ATTN_KERNEL_KINDS = 7
+  ATTN_KERNEL_KINDS = 7,
+  /* range markers (not kinds), as for attn_dtype */
+  ATTN_KERNEL_RANGE_MIN_ = INT_MIN,
+  ATTN_KERNEL_RANGE_MAX_ = INT_MAX
 } attn_kernel_kind;
 
 attn_status attn_timing_begin(int capacity);
