@@ -298,6 +298,8 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int wi
                 workspace ? workspace_bytes : (size_t)0);
   if (((uintptr_t)q | (uintptr_t)k_pages | (uintptr_t)v_pages | (uintptr_t)out) % 16 != 0)
     return fail(ATTN_E_UNSUPPORTED, "q, k_pages, v_pages and out must be 16-byte aligned");
+  if (pl.bytes > 0 && (uintptr_t)workspace % 16 != 0)
+    return fail(ATTN_E_UNSUPPORTED, "workspace must be 16-byte aligned");
 
   attn::DecodeParams p{};
   p.q = q; p.k_pages = k_pages; p.v_pages = v_pages;
@@ -305,7 +307,7 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int wi
   p.out = out; p.lse = lse;
   if (pl.bytes > 0) {
     p.part_o = reinterpret_cast<float*>(workspace);
-    size_t o_bytes = (pl.part_o_elems * sizeof(float) + 255) & ~(size_t)255;
+    const size_t o_bytes = aligned_bytes(pl.part_o_elems);
     p.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + o_bytes);
   }
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.num_pages = num_pages; p.max_pages = max_pages_per_req;

@@ -49,6 +49,12 @@ BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096
 METRIC = "decode KV GB/s (% HBM peak); causal prefill TFLOPS (% bf16 MFMA peak)"
 
 
+def per_launch(k, kind):
+    """Mean ms per launch of `kind` from timing_end(), None when it never ran."""
+    ms, n = k[kind]
+    return round(ms / n, 5) if n else None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -291,7 +297,7 @@ def main():
             "value": round(f_bytes / (f_mean * 1e-3) / 1e9, 1), "kv_bytes": f_bytes,
             "call_ms": round(f_mean, 5), "call_ms_stats": stats(f_ms),
             "split_kernel_ms": round(f_split, 5),
-            "combine_kernel_ms": round(kf["decode_combine"][0] / kf["decode_combine"][1], 5),
+            "combine_kernel_ms": per_launch(kf, "decode_combine"),
             "speedup_vs_bf16_call": round(ms_decode / f_mean, 4),
             "roofline": roofline_hbm(f_bytes, f_split, "decode_fp8")}
         log("bench: fp8 decode", res["decode_fp8"])
@@ -327,7 +333,7 @@ def main():
             "value": round(kv_bytes / (r_mean * 1e-3) / 1e9, 1), "rope_theta": 10000.0,
             "call_ms": round(r_mean, 5), "call_ms_stats": stats(r_ms),
             "split_kernel_ms": round(r_split, 5),
-            "combine_kernel_ms": round(kr["decode_combine"][0] / kr["decode_combine"][1], 5),
+            "combine_kernel_ms": per_launch(kr, "decode_combine"),
             "slowdown_vs_plain_call": round(r_mean / ms_decode, 4),
             "roofline": roofline_hbm(kv_bytes, r_split, "decode_rope")}
         log("bench: rope decode", res["decode_rope"])
@@ -421,7 +427,7 @@ def main():
                 "kv_bytes": nb, "value": round(nb / (mean * 1e-3) / 1e9, 1), "unit": "GB/s",
                 "call_ms": round(mean, 5), "call_ms_stats": stats(ms),
                 "split_kernel_ms": round(kk["decode_split"], 5),
-                "combine_kernel_ms": round(kk.get("decode_combine", 0.0), 5),
+                "combine_kernel_ms": round(kk["decode_combine"], 5) if "decode_combine" in kk else None,
                 "roofline": {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None}}
             del s_kp, s_vp

@@ -75,7 +75,11 @@ def _decode(lib, **kw):
     (dict(ws=None), E_WS),                    # bf16 always needs its run partials
     (dict(ws_bytes=8, split=2), E_WS),
     (dict(q=8), E_UNSUP),                     # misaligned
+    (dict(ws=24), E_UNSUP),                   # workspace not 16-byte aligned
     (dict(num_pages=0), E_SHAPE),
+    # above ATTN_MAX_TOKENS (2^30), and a batch whose unit count exceeds it
+    (dict(max_kv_len=(1 << 30) + 16, max_pages=(1 << 26) + 1), E_UNSUP),
+    (dict(B=1 << 20, max_kv_len=1 << 14, max_pages=1 << 10), E_UNSUP),
 ])
 def test_decode_rejects(lib, kw, status):
     assert _decode(lib, **kw) == status
@@ -136,12 +140,15 @@ def test_workspace_size(lib):
     o, lse = 4 * 5 * 8 * 128 * 4, 4 * 5 * 8 * 4
     assert n == ((o + 255) // 256 + (lse + 255) // 256) * 256
     # bf16 balanced runs: B*Hkv*max_segs*G*(D+1) floats, max_segs = ceil(max_pages/run)+1
+    def bf16_bytes(B, Hkv, segs, G, D):
+        slots = B * Hkv * segs * G
+        return ((slots * D * 4 + 255) // 256 + (slots * 4 + 255) // 256) * 256
     n = lib.attn_decode_paged_workspace_size(1, 4, 8, 2, 128, 16, 160, 2)   # run 2 -> 6 segs
-    slots = 4 * 2 * 6 * 4
-    assert n == ((slots * 128 * 4 + 255) // 256 + (slots * 4 + 255) // 256) * 256
+    assert n == bf16_bytes(4, 2, 6, 4, 128)
     n = lib.attn_decode_paged_workspace_size(1, 4, 8, 2, 128, 16, 160, 0)   # run >= 8 -> 3 segs
-    slots = 4 * 2 * 3 * 4
-    assert n == ((slots * 128 * 4 + 255) // 256 + (slots * 4 + 255) // 256) * 256
+    assert n == bf16_bytes(4, 2, 3, 4, 128)
+    n = lib.attn_decode_paged_workspace_size(1, 4, 8, 2, 128, 16, 2000, 1)  # run 1 -> 126 segs
+    assert n == bf16_bytes(4, 2, 126, 4, 128)
     assert lib.attn_decode_paged_workspace_size(1, -1, 8, 2, 128, 16, 160, 2) == 0
     assert lib.attn_decode_paged_workspace_size(9, 4, 8, 2, 128, 16, 160, 2) == 0
     # f16 uses the bf16 plan
@@ -380,3 +387,11 @@ def test_binding_maps_statuses_to_exceptions(lib):
     with pytest.raises(A.AttnError) as ei:
         A._check(E_HIP)
     assert not isinstance(ei.value, ValueError)
+
+
+def test_timing_capacity_limit(lib):
+    text = open(HEADER).read()
+    m = re.search(r"#define ATTN_TIMING_MAX_LAUNCHES \(1 << (\d+)\)", text)
+    assert m
+    assert lib.attn_timing_begin((1 << int(m.group(1))) + 1) == E_SHAPE
+    assert lib.attn_last_error()

@@ -341,3 +341,20 @@ def test_undersized_workspace_is_refused(gpu):
     with pytest.raises(ValueError, match="workspace"):
         A.decode_paged(case.q.to(gpu), kp, vp, case.page_table.to(gpu), case.kv_lens.to(gpu),
                        scale=case.scale, max_kv_len=case.max_kv_len, workspace=small)
+
+
+
+@pytest.mark.parametrize("dtype,D,Hq,Hkv", [(torch.bfloat16, 128, 32, 8), (torch.bfloat16, 64, 8, 8),
+                                            (torch.float16, 256, 16, 2), (torch.bfloat16, 128, 16, 2)])
+def test_many_segments_per_pair(gpu, dtype, D, Hq, Hkv):
+    """Long requests among short ones (max_kv_len 8064): their (request, KV
+    head) pairs span tens of runs of the balanced cut.  With four requests the
+    merge folds them with one wave per head, in chunks of 64 lse values; with
+    a single request it runs segment-parallel (16 waves per workgroup).
+    G = 1, 2, 4, 8."""
+    for lens in ([8064, 100, 0, 17], [8064], [5000, 8000, 1, 4097]):
+        case = workloads.make_decode(B=len(lens), Hq=Hq, Hkv=Hkv, D=D, page_size=16, kv_lens=lens,
+                                     dtype=dtype, seed=1200 + D + Hq + len(lens), extra_pages=3)
+        out, lse = _run(case, gpu)
+        ro, rl = _oracle(case)
+        assert_parity(out, lse, ro, rl, dtype, f"{dtype} D{D} Hq{Hq} Hkv{Hkv} lens {lens}")
