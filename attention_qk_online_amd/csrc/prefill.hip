@@ -276,7 +276,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
     }
     return pid;
   };
-  auto dma = [&](int kt, char* dst, bool is_v, int pid) {
+  auto dma = [&](int kt, char* dst, bool is_v, int pid, auto full_tag) {
     const int k0 = kt * C::BN;
     const char* g = is_v ? vg : kg;
     const char* base;
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
     }
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, nrec, kBufferWord3);
-    if (kt < t_full) {
+    if (decltype(full_tag)::value || kt < t_full) {   // full_tag: known to be a whole tile
 #pragma unroll
       for (int i = 0; i < C::DMA; ++i) {
         const int r0i = (wave * C::DMA + i) * RPI;     // first tile row of instruction i
@@ -444,12 +444,14 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
                   f32x16 (&snext)[C::KB]) {
     constexpr int SLOT = decltype(slot_tag)::value;
     constexpr bool FAST = decltype(fast_tag)::value != 0;
+    // 2: a steady-state step whose two DMAs are whole tiles (no clamped rows)
+    constexpr int FULL = decltype(fast_tag)::value == 2 ? 1 : 0;
     char* const KDST = kslot(Idx<SLOT>{});
     char* const KNXT = kslot(Idx<SLOT + 1>{});
     char* const VCUR = vslot(Idx<SLOT>{});
     char* const VDST = vslot(Idx<SLOT + C::R - 1>{});
-    if (kt + C::R - 1 < n_kt) dma(kt + C::R - 1, VDST, true, pid_v);
-    if (kt + C::R < n_kt) dma(kt + C::R, KDST, false, pid_k);
+    if (kt + C::R - 1 < n_kt) dma(kt + C::R - 1, VDST, true, pid_v, Idx<FULL>{});
+    if (kt + C::R < n_kt) dma(kt + C::R, KDST, false, pid_k, Idx<FULL>{});
     v8 pb[C::PS];
     if constexpr (FAST) {
       // One block in which the S^T(kt+1) MFMAs hide the exponentials of tile kt.
@@ -527,8 +529,8 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
       const int pid = load_pid(t);
       char* kd = t == 0 ? kslot(Idx<0>{}) : kslot(Idx<1>{});
       char* vd = t == 0 ? vslot(Idx<0>{}) : vslot(Idx<1>{});
-      dma(t, kd, false, pid);
-      if (t + 1 < C::R) dma(t, vd, true, pid);
+      dma(t, kd, false, pid, Idx<0>{});
+      if (t + 1 < C::R) dma(t, vd, true, pid, Idx<0>{});
       else pid_v = pid;
     }
   }
@@ -541,6 +543,12 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
   for (; kt < n_lead; kt += C::R) {
     step(Idx<0>{}, Idx<0>{}, kt, sa, sb);
     if (kt + 1 < n_kt) step(Idx<1>{}, Idx<0>{}, kt + 1, sb, sa);
+  }
+  // Steady-state steps whose DMAs (tiles kt + C::R - 1 and kt + C::R) are whole
+  // tiles skip the clamped-row addressing of the last, partial tile.
+  for (; kt < n_fast && kt + C::R + 1 < t_full; kt += C::R) {
+    step(Idx<0>{}, Idx<2>{}, kt, sa, sb);
+    step(Idx<1>{}, Idx<2>{}, kt + 1, sb, sa);
   }
   for (; kt < n_fast; kt += C::R) {
     step(Idx<0>{}, Idx<1>{}, kt, sa, sb);
