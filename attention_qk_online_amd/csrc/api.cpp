@@ -275,7 +275,9 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int wi
                 "(num_pages * %s page_size/16 must stay below 2^31)", num_pages,
                 kv_hnd ? "Hkv *" : "");
   if (B == 0) return ATTN_OK;
-  if (!q || !k_pages || !v_pages || !page_table || !kv_lens || !out || !lse)
+  // With max_kv_len 0 no page is read (a longer kv_len is inconsistent and
+  // only poisons its request), so the cache and its table may be empty.
+  if (!q || !kv_lens || !out || !lse || (max_kv_len > 0 && (!k_pages || !v_pages || !page_table)))
     return fail(ATTN_E_NULL, "a required pointer is NULL");
   if (num_pages == 0 && max_kv_len > 0)
     return fail(ATTN_E_SHAPE, "num_pages is 0 but max_kv_len=%d", max_kv_len);
@@ -512,7 +514,8 @@ static attn_status prefill_varlen_impl(attn_dtype dtype, const void* q, const vo
     return fail(ATTN_E_UNSUPPORTED, "total_k=%d or max_seqlen_k=%d exceeds ATTN_MAX_TOKENS=%d",
                 total_k, max_seqlen_k, ATTN_MAX_TOKENS);
   if (B == 0 || max_seqlen_q == 0 || total_q == 0) return ATTN_OK;
-  if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !out || !lse)
+  // With total_k 0 every sequence has no keys: k and v are never read.
+  if (!q || !cu_seqlens_q || !cu_seqlens_k || !out || !lse || (total_k > 0 && (!k || !v)))
     return fail(ATTN_E_NULL, "a required pointer is NULL");
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16 != 0)
     return fail(ATTN_E_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
@@ -582,7 +585,9 @@ static attn_status paged_prefill_params(attn_dtype dtype, const void* q,
                 (long)max_pages_per_req * page_size);
   empty = B == 0 || max_seqlen_q == 0 || total_q == 0;
   if (empty) return ATTN_OK;
-  if (!q || !k_pages || !v_pages || !cu_seqlens_q || !page_table || !kv_lens || !out || !lse)
+  // With max_kv_len 0 no page is read (see the decode check).
+  if (!q || !cu_seqlens_q || !kv_lens || !out || !lse ||
+      (max_kv_len > 0 && (!k_pages || !v_pages || !page_table)))
     return fail(ATTN_E_NULL, "a required pointer is NULL");
   if (num_pages == 0 && max_kv_len > 0)
     return fail(ATTN_E_SHAPE, "num_pages is 0 but max_kv_len=%d", max_kv_len);

@@ -160,8 +160,13 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
       Lk = p.kv_len_fixed;
       table = page_table;
     } else {
+      // kv_len above the table's capacity or above the host bound max_kv_len
+      // (max_seqlen_k) marks the request bad and reads nothing.
       Lk = p.kv_lens[b] - p.kv_offset;
-      if (Lk < 0 || Lk > p.max_tokens - p.kv_offset) { bad = true; Lk = 0; }
+      if (Lk < 0 || Lk > p.max_tokens - p.kv_offset || Lk > p.max_seqlen_k - p.kv_offset) {
+        bad = true;
+        Lk = 0;
+      }
       if (p.kv_offset > 0 && p.causal && Lk < Lq) bad = true;
       table = page_table + (size_t)b * p.table_stride + (LP ? 0 : p.kv_offset / kPage);
       if constexpr (LP) blk_off = p.kv_offset / kPage;
@@ -170,6 +175,7 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
     k_start = min(max(p.cu_k[b], 0), p.total_k);
     const int k_end = min(max(p.cu_k[b + 1], k_start), p.total_k);
     Lk = k_end - k_start;
+    if (Lk > p.max_seqlen_k) { bad = true; Lk = 0; }   // above the host bound max_seqlen_k
   }
   int off = Lk - Lq;                             // bottom-right causal offset
   // Right bound: query i sees keys j <= i + off + rb (causal: rb = 0).

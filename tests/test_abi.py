@@ -197,6 +197,8 @@ def _prefill(lib, **kw):
     (dict(Tk=-1), E_SHAPE),
     (dict(cq=None), E_NULL),
     (dict(out=None), E_NULL),
+    (dict(k=None), E_NULL),                   # keys to read (Tk > 0): k and v are required
+    (dict(v=None), E_NULL),
     (dict(k=24), E_UNSUP),
     (dict(B=1 << 14, Hq=1 << 10, Hkv=1 << 10, mq=1 << 15), E_SHAPE),   # > INT_MAX work items
 ])

@@ -358,3 +358,22 @@ def test_many_segments_per_pair(gpu, dtype, D, Hq, Hkv):
         out, lse = _run(case, gpu)
         ro, rl = _oracle(case)
         assert_parity(out, lse, ro, rl, dtype, f"{dtype} D{D} Hq{Hq} Hkv{Hkv} lens {lens}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_empty_cache(gpu, dtype):
+    """max_kv_len 0 with an empty pool and page table (NULL pointers at the
+    boundary): kv_len 0 gives out 0 and lse -inf; a kv_len above the bound
+    gives NaN and reads nothing."""
+    import attention_qk_online_amd as A
+    D = 128
+    q = torch.randn(3, 8, D, device=gpu).to(dtype)
+    pool = torch.empty((0, 16, 2, D), dtype=dtype, device=gpu)
+    table = torch.empty((3, 0), dtype=torch.int32, device=gpu)
+    lens = torch.tensor([0, 5, 0], dtype=torch.int32, device=gpu)
+    out, lse = A.decode_paged(q, pool, pool, table, lens, scale=0.1, max_kv_len=0)
+    torch.cuda.synchronize()
+    out, lse = out.float().cpu(), lse.cpu()
+    for b in (0, 2):
+        assert torch.equal(out[b], torch.zeros(8, D)) and torch.isneginf(lse[b]).all()
+    assert torch.isnan(out[1]).all() and torch.isnan(lse[1]).all()

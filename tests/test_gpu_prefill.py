@@ -391,3 +391,76 @@ def test_paged_bad_page_larger_pages(gpu, layout):
     good = torch.cat([torch.arange(c[0], c[1]), torch.arange(c[2], c[3])])
     assert_parity(out, lse, ro, rl, torch.bfloat16, f"good requests ({layout})", rows=good)
     assert torch.isnan(out[c[1]:c[2]].float()).all() and torch.isnan(lse[c[1]:c[2]]).all()
+
+
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("causal", [True, False])
+def test_no_keys_at_all(gpu, D, causal):
+    """A ragged batch whose sequences all have zero keys (total_k 0: k and v are
+    empty tensors, NULL pointers at the boundary): every row gets out 0 and
+    lse -inf."""
+    import attention_qk_online_amd as A
+    case = workloads.make_prefill(B=3, Hq=8, Hkv=2, D=D, lens_q=[300, 1, 129], lens_k=[0, 0, 0],
+                                  dtype=torch.bfloat16, seed=330, causal=causal)
+    assert case.k.numel() == 0
+    out, lse = A.prefill_varlen(case.q.to(gpu), case.k.to(gpu), case.v.to(gpu),
+                                case.cu_seqlens_q.to(gpu), case.cu_seqlens_k.to(gpu), 300, 1,
+                                causal=causal, scale=case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.float().cpu(), torch.zeros(out.shape))
+    assert torch.isneginf(lse.cpu()).all()
+
+
+def test_keys_above_max_seqlen_k_are_nan(gpu):
+    """A sequence with more keys than the host bound max_seqlen_k: its rows are NaN;
+    the other sequence is unaffected."""
+    import attention_qk_online_amd as A
+    case = workloads.make_prefill(B=2, Hq=4, Hkv=2, D=128, lens_q=[100, 60], lens_k=[200, 500],
+                                  dtype=torch.bfloat16, seed=331, causal=True)
+    out, lse = A.prefill_varlen(case.q.to(gpu), case.k.to(gpu), case.v.to(gpu),
+                                case.cu_seqlens_q.to(gpu), case.cu_seqlens_k.to(gpu), 100, 300,
+                                causal=True, scale=case.scale)
+    torch.cuda.synchronize()
+    ro, rl = _ref(case)
+    assert_parity(out[:100], lse[:100], ro[:100], rl[:100], torch.bfloat16, "good sequence")
+    assert torch.isnan(out[100:].float()).all() and torch.isnan(lse[100:]).all()
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_paged_kv_len_above_max_kv_len_is_nan(gpu, D):
+    """A request whose kv_len exceeds the host bound max_kv_len (but fits its
+    page-table row): its rows are NaN and nothing of it is read; the other
+    request is unaffected."""
+    import attention_qk_online_amd as A
+    case = workloads.make_paged_prefill(B=2, Hq=4, Hkv=2, D=D, page_size=16, chunk=[40, 30],
+                                        cached=[100, 300], dtype=torch.bfloat16, seed=332)
+    kp, vp = case.pools(gpu)
+    out, lse = A.prefill_paged(case.q.to(gpu), case.cu_seqlens_q.to(gpu), kp, vp,
+                               case.page_table.to(gpu), case.kv_lens.to(gpu), 40, 140,
+                               causal=True, scale=case.scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, case.pool_k, case.pool_v,
+                                      case.page_table, case.kv_lens, True, case.scale)
+    n0 = int(case.cu_seqlens_q[1])
+    assert_parity(out[:n0], lse[:n0], ro[:n0], rl[:n0], torch.bfloat16, "good request")
+    assert torch.isnan(out[n0:].float()).all() and torch.isnan(lse[n0:]).all()
+
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_paged_empty_cache(gpu, layout):
+    """max_kv_len 0 with an empty pool and page table (NULL pointers at the
+    boundary): rows with no key get out 0 and lse -inf; a request claiming keys
+    (kv_len above max_kv_len) gets NaN and reads nothing."""
+    import attention_qk_online_amd as A
+    q = torch.randn(50, 8, 128, device=gpu).to(torch.bfloat16)
+    cu = torch.tensor([0, 20, 50], dtype=torch.int32, device=gpu)
+    lens = torch.tensor([0, 7], dtype=torch.int32, device=gpu)
+    pool = torch.empty((0, 16, 2, 128) if layout == "NHD" else (0, 2, 16, 128), dtype=torch.bfloat16,
+                       device=gpu)
+    table = torch.empty((2, 0), dtype=torch.int32, device=gpu)
+    out, lse = A.prefill_paged(q, cu, pool, pool, table, lens, 30, 0, causal=False, scale=0.1,
+                               kv_layout=layout)
+    torch.cuda.synchronize()
+    out, lse = out.float().cpu(), lse.cpu()
+    assert torch.equal(out[:20], torch.zeros(20, 8, 128)) and torch.isneginf(lse[:20]).all()
+    assert torch.isnan(out[20:]).all() and torch.isnan(lse[20:]).all()
