@@ -49,9 +49,14 @@
  *    a page id outside [0, num_pages) or a kv_len above max_kv_len or
  *    max_pages_per_req * page_size gets NaN in all its out and lse rows.
  *    Prefill: rows whose visible keys reach an out-of-range page id, and the
- *    rows of a sequence longer than max_seqlen_q (or whose kv_len exceeds
- *    max_pages_per_req * page_size), are NaN; of such a sequence only its
- *    first ceil(max_seqlen_q / 128) * 128 rows are written.
+ *    rows of a sequence longer than max_seqlen_q, with more keys than
+ *    max_seqlen_k (paged: a kv_len above max_kv_len or max_pages_per_req *
+ *    page_size), are NaN; of such a sequence only its first
+ *    ceil(max_seqlen_q / 128) * 128 rows are written, and none of its keys
+ *    is read.
+ *  - Empty caches: when nothing can be read (prefill total_k 0; decode and
+ *    paged prefill max_kv_len 0) the key/value tensors and the page table
+ *    may be NULL.
  *  - Size limits: every token count and length argument (total_q, total_k,
  *    max_seqlen_q, max_seqlen_k, max_kv_len) is at most ATTN_MAX_TOKENS
  *    (2^30), and a 16-bit decode batch keeps B * (ceil(max_kv_len / 16) + 1)
