@@ -52,8 +52,8 @@
  *    rows of a sequence longer than max_seqlen_q, with more keys than
  *    max_seqlen_k (paged: a kv_len above max_kv_len or max_pages_per_req *
  *    page_size), are NaN; of such a sequence only its first
- *    ceil(max_seqlen_q / 128) * 128 rows are written, and none of its keys
- *    is read.
+ *    ceil(max_seqlen_q / 128) * 128 rows are written, and a key count above
+ *    its bound makes the kernel read none of its keys.
  *  - Empty caches: when nothing can be read (prefill total_k 0; decode and
  *    paged prefill max_kv_len 0) the key/value tensors and the page table
  *    may be NULL.
