@@ -464,3 +464,63 @@ def test_paged_empty_cache(gpu, layout):
     out, lse = out.float().cpu(), lse.cpu()
     assert torch.equal(out[:20], torch.zeros(20, 8, 128)) and torch.isneginf(lse[:20]).all()
     assert torch.isnan(out[20:]).all() and torch.isnan(lse[20:]).all()
+
+
+@pytest.mark.parametrize("D,layout", [(128, "NHD"), (256, "HND")])
+def test_paged_pages_past_4gib(gpu, D, layout):
+    """The pages of a chunked prefill placed at the top of a pool of more than
+    4 GiB per tensor (byte offsets above 2^32): same result as the compact
+    pool, bit for bit, and parity with the oracle."""
+    import attention_qk_online_amd as A
+    case = workloads.make_paged_prefill(B=3, Hq=8, Hkv=8, D=D, page_size=16, chunk=[100, 37, 64],
+                                        cached=[300, 500, 129], dtype=torch.bfloat16, seed=340)
+    page_bytes = 16 * 8 * D * 2
+    big = (5 << 30) // page_bytes + 64                # > 5 GiB per pool
+    print(f"pool of {big} pages ({big * page_bytes / 2**30:.1f} GiB each)", flush=True)
+    kp, vp = case.pools(gpu, layout)
+    # old id i -> big - 1 - 3 i: scattered over the top of the big pool
+    remap = torch.arange(case.num_pages, device=gpu) * -3 + (big - 1)
+    shape = (big,) + tuple(kp.shape[1:])
+    kb = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=gpu)
+    vb = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=gpu)
+    kb.index_copy_(0, remap, kp)
+    vb.index_copy_(0, remap, vp)
+    table_big = remap[case.page_table.to(gpu).long()].to(torch.int32)
+    args = (case.q.to(gpu), case.cu_seqlens_q.to(gpu))
+    tail = (case.kv_lens.to(gpu), case.max_seqlen_q, case.max_kv_len)
+    o_small, l_small = A.prefill_paged(*args, kp, vp, case.page_table.to(gpu), *tail, causal=True,
+                                       scale=case.scale, kv_layout=layout)
+    o_big, l_big = A.prefill_paged(*args, kb, vb, table_big, *tail, causal=True, scale=case.scale,
+                                   kv_layout=layout)
+    torch.cuda.synchronize()
+    assert torch.equal(o_small, o_big) and torch.equal(l_small, l_big)
+    del kb, vb
+    ro, rl = oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, case.pool_k, case.pool_v,
+                                      case.page_table, case.kv_lens, True, case.scale)
+    assert_parity(o_big, l_big, ro, rl, torch.bfloat16, f"D{D} {layout} pool of {big} pages")
+
+
+def test_varlen_keys_past_4gib(gpu):
+    """A ragged batch whose second sequence starts more than 4 GiB into k and v
+    (a first sequence of 2^20 keys, Hkv 8, head_dim 256): the second
+    sequence's rows match the oracle on its own keys."""
+    import attention_qk_online_amd as A
+    Hq, Hkv, D, L0 = 8, 8, 256, 1 << 20
+    lens_q, lens_k = [1, 200], [L0, 333]
+    Tk = sum(lens_k)
+    print(f"k, v of {Tk * Hkv * D * 2 / 2**30:.2f} GiB each", flush=True)
+    g = torch.Generator(device=gpu).manual_seed(341)
+    k = torch.randn(Tk, Hkv, D, generator=g, device=gpu).to(torch.bfloat16)
+    v = torch.randn(Tk, Hkv, D, generator=g, device=gpu).to(torch.bfloat16)
+    q = torch.randn(sum(lens_q), Hq, D, generator=g, device=gpu).to(torch.bfloat16)
+    cu_q = torch.tensor([0, 1, 201], dtype=torch.int32, device=gpu)
+    cu_k = torch.tensor([0, L0, Tk], dtype=torch.int32, device=gpu)
+    scale = 1.0 / 16
+    out, lse = A.prefill_varlen(q, k, v, cu_q, cu_k, 200, L0, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    k1, v1 = k[L0:].cpu(), v[L0:].cpu()
+    q1 = q[1:].cpu()
+    del k, v
+    ro, rl = oracle.ref_prefill_varlen(q1, k1, v1, torch.tensor([0, 200], dtype=torch.int32),
+                                       torch.tensor([0, 333], dtype=torch.int32), True, scale)
+    assert_parity(out[1:], lse[1:], ro, rl, torch.bfloat16, "sequence past 4 GiB")
