@@ -377,3 +377,18 @@ def test_empty_cache(gpu, dtype):
     for b in (0, 2):
         assert torch.equal(out[b], torch.zeros(8, D)) and torch.isneginf(lse[b]).all()
     assert torch.isnan(out[1]).all() and torch.isnan(lse[1]).all()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_batch_above_65535_requests(gpu, dtype):
+    """A batch of 70 000 short requests (grid dimensions indexed by request go
+    past 65 535): sampled requests match the oracle."""
+    B = 70000
+    case = workloads.make_decode(B=B, Hq=4, Hkv=2, D=64, page_size=16, len_range=(0, 40),
+                                 dtype=dtype, seed=1600, extra_pages=3, poison=False)
+    out, lse = _run(case, gpu, split_pages=1 if dtype == torch.float32 else 0)
+    picks = sorted(set(list(range(40)) + list(range(B - 40, B)) + list(range(0, B, 997))))
+    kp, vp = case.pools("cpu")
+    ro, rl = oracle.ref_decode_paged(case.q, kp, vp, case.page_table, case.kv_lens, case.scale,
+                                     requests=picks)
+    assert_parity(out, lse, ro, rl, dtype, f"B {B}", rows=picks)
