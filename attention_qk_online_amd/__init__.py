@@ -250,15 +250,16 @@ def _decode(q, k_pages, v_pages, page_table, kv_lens, scale, max_kv_len, split_p
     ws_bytes = int(lib.attn_decode_paged_workspace_size(dt, B, Hq, Hkv, D, page_size, max_kv_len,
                                                         split_pages))
     if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+        # A call that keeps no partial states (one fp32 split) passes no workspace.
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     elif workspace.numel() * workspace.element_size() < ws_bytes:
         raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
                          f"this call needs {ws_bytes} (decode_paged_workspace_size)")
-    pw = _dev(workspace, "workspace")
+    pw = 0 if workspace is None else _dev(workspace, "workspace")
+    ws_size = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (pq, pk, pv, pt, pl, B, Hq, Hkv, D, page_size, num_pages, page_table.shape[1],
             max_kv_len, split_pages, s)
-    tail = (out.data_ptr(), lse.data_ptr(), pw, workspace.numel() * workspace.element_size(),
-            _stream(q.device))
+    tail = (out.data_ptr(), lse.data_ptr(), pw, ws_size, _stream(q.device))
     if rope is not None:
         if fp8_scales is not None:
             raise ValueError("the rotary embedding is not built for the E4M3 cache")
