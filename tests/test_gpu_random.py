@@ -75,6 +75,35 @@ def test_random_decode(gpu, seed):
     assert_parity(out, lse, ro, rl, dtype, desc)
 
 
+@pytest.mark.parametrize("seed", range(40))
+def test_random_decode_fp32(gpu, seed):
+    """fp32 decode (16-token pages, head_dim 64 or 128): splits, windows, HND."""
+    import attention_qk_online_amd as A
+    rng = random.Random(7500 + seed)
+    D = rng.choice([64, 128])
+    Hkv = rng.choice([1, 2, 4, 8])
+    G = rng.choice([1, 2, 4, 8])
+    B = rng.randint(1, 10)
+    layout = rng.choice(["NHD", "HND"])
+    window = rng.choice([-1, -1, rng.randint(0, 600)])
+    split = rng.choice([0, 0, rng.randint(1, 40)])
+    lens = [_length(rng, 16, hi=rng.choice([2000, 6000])) for _ in range(B)]
+    desc = (f"seed {seed}: fp32 D{D} Hq{G * Hkv} Hkv{Hkv} {layout} B{B} window {window} "
+            f"split {split} lens {lens}")
+    print(desc, flush=True)
+    case = workloads.make_decode(B=B, Hq=G * Hkv, Hkv=Hkv, D=D, page_size=16, kv_lens=lens,
+                                 dtype=torch.float32, seed=7500 + seed, extra_pages=2)
+    kg, vg = case.pools(gpu, layout)
+    out, lse = A.decode_paged(case.q.to(gpu), kg, vg, case.page_table.to(gpu), case.kv_lens.to(gpu),
+                              scale=case.scale, max_kv_len=case.max_kv_len, split_pages=split,
+                              kv_layout=layout, window_left=window)
+    torch.cuda.synchronize()
+    kp, vp = case.pools()
+    ro, rl = oracle.ref_decode_paged(case.q, kp, vp, case.page_table, case.kv_lens, case.scale,
+                                     window_left=window)
+    assert_parity(out, lse, ro, rl, torch.float32, desc)
+
+
 @pytest.mark.parametrize("seed", range(100))
 def test_random_prefill_varlen(gpu, seed):
     import attention_qk_online_amd as A
