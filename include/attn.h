@@ -19,9 +19,11 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All tensors are dense, row-major, and live in device memory unless the
- *    argument says "host".  Element types: ATTN_F32 (float), ATTN_BF16
- *    (bfloat16 bits) or ATTN_F16 (IEEE half bits).  `out` has the input
- *    element type; `lse` is float.
+ *    argument says "host".  q, k, v (or the page pools), out and the
+ *    workspaces start at 16-byte aligned addresses (ATTN_E_UNSUPPORTED
+ *    otherwise; every device allocation is).  Element types: ATTN_F32
+ *    (float), ATTN_BF16 (bfloat16 bits) or ATTN_F16 (IEEE half bits).  `out`
+ *    has the input element type; `lse` is float.
  *  - Grouped heads: query head h reads KV head h / (Hq / Hkv); Hq must be a
  *    multiple of Hkv ("FlashAttention-3 ..." section 二: queries carry
  *    num_heads, keys/values num_kv_heads).
@@ -136,8 +138,9 @@ typedef enum {
  *  out         [B, Hq, D]                   dtype
  *  lse         [B, Hq]                      float
  *  workspace   device scratch of at least attn_decode_paged_workspace_size()
- *              bytes (may be NULL when that size is 0); contents on entry
- *              do not matter and are clobbered.
+ *              bytes, 16-byte aligned (else ATTN_E_UNSUPPORTED; may be NULL
+ *              when that size is 0); contents on entry do not matter and are
+ *              clobbered.
  *
  * Supported: dtype BF16 or F16 with D in {64, 128, 256}, or F32 with D in {64, 128};
  * Hq/Hkv in {1, 2, 4, 8}; page_size 16, 32, 64, 128 or 256 (BF16/F16; the
