@@ -710,8 +710,9 @@ def visible_pairs(lens_q, lens_k, causal, left=-1, right=-1):
 def cpu_threads():
     """Threads for the CPU oracle: the CPUs this process may run on (its
     affinity mask), bounded by the cgroup CPU quota and by OMP_NUM_THREADS
-    when either is set -- a GPU machine gives one GPU's job a share of the host
-    (os.cpu_count() reports the whole machine).  Returns (threads, details)."""
+    when either is set -- a container or a scheduler that runs one job per
+    GPU gives each job a share of the host (os.cpu_count() reports the whole
+    machine).  Returns (threads, details)."""
     n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     info = {"os_cpu_count": os.cpu_count(), "affinity_cpus": n}
     try:
