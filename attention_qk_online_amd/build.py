@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libattn.so")
 
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "prefill16.hip", "merge.hip"]
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "prefill256.hip", "merge.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops (v_pk_*_f32) are switched off for all device code.

@@ -115,7 +115,7 @@ hipError_t launch_merge_states(const void* oa, const float* la, const void* ob, 
 // Query rows per workgroup of the prefill kernels (grid sizing on the host).
 constexpr int kPrefillBM = 128;
 bool prefill_supported(int dtype, int D);
-// head_dim 256 on eight 16-row waves (prefill16.hip).
+// head_dim 256 on four pairs of waves, 32 rows a pair (prefill256.hip).
 hipError_t launch_prefill_d256(const PrefillParams& p, int dtype, bool paged, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, bool paged, hipStream_t s);
 

@@ -1,5 +1,5 @@
 // Ragged causal prefill for gfx950 on bf16 / fp16 MFMA with fp32 accumulation,
-// head_dim 128 (head_dim 256: prefill16.hip).
+// head_dim 128 (head_dim 256: prefill256.hip).
 //
 // One workgroup = one (query tile of BM = 128 rows, query head) of one
 // sequence; four waves own 32 query rows each.  Key tiles have BN = 64 keys.

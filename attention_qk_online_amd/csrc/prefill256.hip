@@ -1,35 +1,29 @@
-// Prefill for head_dim 256 on bf16 / fp16 MFMA: eight waves of 16 query rows.
+// Prefill for head_dim 256 on bf16 / fp16 MFMA: four pairs of waves, each
+// pair owning 32 query rows.
 //
-// Same tiling, data movement, work order and step structure as the head_dim
-// 128 kernel (prefill.hip): one workgroup = one (query tile of BM = 128
-// rows, query head); K and V tiles of 64 keys go HBM -> LDS by buffer-load
-// DMA into rings of two slots (128 KiB, one workgroup per CU); one wait and
-// one barrier per tile; tiles wholly above the causal diagonal are never
-// loaded.  What differs: a 32-row wave needs the whole register file at
-// head_dim 256 (O^T alone is 128 VGPRs), so it would run alone on its SIMD.
-// Here each wave owns 16 query rows, on v_mfma_f32_16x16x32_{bf16,f16}:
-//   S^T(16 keys x 16 rows) = K . Q^T      A = K rows from LDS (16 bytes per lane),
-//                                          B = Q^T held in VGPRs (32 registers)
-//   O^T(16 d x 16 rows)  += V^T . P^T      A = V^T fragments from LDS via
-//                                          ds_read_b64_tr_b16, B = P^T
-// so a wave needs about half the registers and two waves share each SIMD:
-// one wave's exponentials run beside the other's matrix work.  The price is
-// twice the LDS operand reads per flop (every K and V fragment now feeds 16
-// query rows instead of 32).  Tiles are 64 keys because the fixed cost of a
-// step (DMA issue, wait, barrier) is large: 32-key tiles measured 10 %
-// slower on long sequences.
+// Tiling, data movement and work order follow the head_dim 128 kernel
+// (prefill.hip): one workgroup = one (query tile of BM = 128 rows, query
+// head); K and V tiles of 64 keys go HBM -> LDS by buffer-load DMA into rings
+// of two slots (128 KiB, one workgroup per CU); tiles wholly above the causal
+// diagonal are never loaded.  At head_dim 256 a wave cannot hold Q, O^T and
+// the scores of 32 rows in the 256 registers that two waves per SIMD allow,
+// and a 16-row wave reads every K and V fragment for only 16 rows.  Here the
+// two waves of a pair share 32 rows and split the work of a tile:
+//   wave h:  S^T_h (keys 32 h .. +31 x 32 rows) = K_h . Q^T on
+//            v_mfma_f32_32x32x16 (Q^T in 64 registers): its half of the
+//            tile's scores;
+//   both:    the running max agreed from the two waves' tile maxima (posted
+//            in LDS one step ahead), P_h = 2^(s c - m) posted in LDS;
+//   wave h:  O^T_h (d 128 h .. +127 x 32 rows) += V^T_h . P^T over its own
+//            32 keys, then, after a barrier, over its partner's.
+// A wave reads half a K tile and half a V tile per step: half the LDS
+// operand bytes per flop of 16-row waves, with the register budget of two
+// waves per SIMD (Q 64, O^T 64, two S^T blocks 32 registers).  Two barriers
+// per tile: P posted, and the ring barrier.  The scores of tile kt + 1 are
+// computed beside the exponentials of tile kt.
 //
-// Key order inside each 32 keys of a tile: the S^T accumulator of key block
-// kb (keys 16 kb .. 16 kb + 15) gives lane (query j = lane % 16, group
-// g = lane / 16) keys 16 kb + 4 g .. + 3.  As the B operand of
-// O^T += V^T P^T that lane supplies k-elements 8 g .. 8 g + 7, read here as
-// keys {4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3}; the V^T fragments are read
-// in the same key order, so P^T needs no data movement.
-//
-// LDS layouts (rows of 512 bytes): K chunks of 16 bytes XOR (row mod 16),
-// so the 16 rows of a K fragment read hit every bank once; V units of 32
-// bytes XOR (row mod 8), so the 8 rows two lane groups of a transposing read
-// touch together land on distinct banks.
+// Key order: as in the head_dim 128 kernel the S^T accumulator is the P^T
+// operand as is; the V^T fragments are read in the same key order.
 //
 // This follows the tiled, fused scheme of "FlashAttention-3 内核在最新大模型
 // 推理中的集成实践" (section 一: tiles in on-chip memory, online softmax
@@ -48,24 +42,24 @@ constexpr int D = 256;
 constexpr int BM = kPrefillBM;        // query rows per workgroup
 constexpr int NW = 8;                 // waves
 constexpr int NT = NW * 64;
-constexpr int RW = BM / NW;           // query rows per wave (16)
+constexpr int PR = 32;                // query rows per pair of waves
 constexpr int BN = 64;                // keys per tile
-constexpr int KB = BN / 16;           // 16-key blocks of S^T
-constexpr int PS = BN / 32;           // 32-key k-steps of O^T
 constexpr int ROWB = D * 2;           // bytes of one K/V row
 constexpr int TILEB = BN * ROWB;      // 32 KiB
 constexpr int CH = D / 8;             // 16-byte chunks per row
 constexpr int DMA = TILEB / 1024 / NW;  // 1 KiB DMA instructions per wave per tile
 constexpr int WROWS = BN / NW;        // tile rows written by one wave
-constexpr int QK = D / 32;            // k-steps of S^T
-constexpr int DB = D / 16;            // 16-row blocks of O^T
+constexpr int QK = D / 16;            // 16-element k-steps of S^T
+constexpr int DBH = D / 2 / 32;       // 32-wide d blocks of a wave's half of O^T
+constexpr int PS = BN / 16;           // 16-key k-steps of O^T
 constexpr int R = 2;                  // ring slots per operand
+constexpr int PB = 64 * 32;           // bytes of one wave's P (32 per lane)
 constexpr int kPage = 16;
 constexpr float kRescaleSlack = 8.f;
 constexpr int kBufferWord3 = 0x00020000;
-static_assert(RW == 16 && DMA == 4 && WROWS == 8, "geometry");
+static_assert(BM == 4 * PR && DMA == 4 && WROWS == 8 && DBH == 4 && PS == 4, "geometry");
 static_assert(WROWS <= kPage && kPage % WROWS == 0, "a wave's rows stay inside one page");
-static_assert(R == 2 && 2 * R * TILEB <= 160 * 1024, "LDS per CU");
+static_assert(2 * R * TILEB + NW * PB + 2 * NW * PR * 4 <= 160 * 1024, "LDS per CU");
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -74,7 +68,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Logical 16-byte chunk stored at physical chunk q of K row r / V row r.
 __device__ __forceinline__ int k_chunk(int r, int q) { return q ^ (r & 15); }
-__device__ __forceinline__ int v_chunk(int r, int q) { return (((q >> 1) ^ (r & 7)) << 1) | (q & 1); }
+__device__ __forceinline__ int v_chunk(int r, int q) { return (((q >> 2) ^ (r & 3)) << 2) | (q & 3); }
 
 template <int N>
 struct Idx { static constexpr int value = N; };
@@ -82,32 +76,20 @@ struct Idx { static constexpr int value = N; };
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kWaitLgkm0 = 0xc07f;
 
-// Sum / max over the four 16-lane groups (lanes j, j+16, j+32, j+48).
-__device__ __forceinline__ float max_groups(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
-                                            false, false);
-  x = fmaxf(__builtin_bit_cast(float, (int)a[0]), __builtin_bit_cast(float, (int)a[1]));
-  return max_halves(x);
-}
-__device__ __forceinline__ float sum_groups(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
-                                            false, false);
-  x = __builtin_bit_cast(float, (int)a[0]) + __builtin_bit_cast(float, (int)a[1]);
-  return sum_halves(x);
-}
-
 template <typename E, bool PAGED, bool LP>
-__global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
+__global__ __launch_bounds__(NT, 1) void prefill256_kernel(PrefillParams p,
                                                          const int32_t* __restrict__ page_table) {
   using H = Half16<E>;
   using elem = typename H::elem;
   using v8 = typename H::v8;
   using v2 = typename H::v2;
-  auto mfma = [](v8 a, v8 b, f32x4 c) { return H::mfma16x16x32(a, b, c); };
+  auto mfma32 = [](v8 a, v8 b, f32x16 c) { return H::mfma32x32x16(a, b, c); };
   __shared__ __attribute__((aligned(1024))) char k_ring0[TILEB];
   __shared__ __attribute__((aligned(1024))) char k_ring1[TILEB];
   __shared__ __attribute__((aligned(1024))) char v_ring0[TILEB];
   __shared__ __attribute__((aligned(1024))) char v_ring1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char p_buf[NW * PB];   // each wave's P^T, lane-linear
+  __shared__ float m_buf[2][NW][PR];                               // tile maxima (by tile parity)
   auto kslot = [&](auto i) -> char* {
     if constexpr (decltype(i)::value % R == 0) return k_ring0;
     else return k_ring1;
@@ -120,7 +102,8 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int j16 = lane & 15, grp = lane >> 4;
+  const int pair = wave >> 1, half = wave & 1, partner = wave ^ 1;
+  const int l32 = lane & 31, hl = lane >> 5;
 
   // Work order: as the head_dim 128 kernel (XCD c runs the c-th eighth of the
   // (KV head, sequence, tile heaviest first, query head) list).
@@ -140,7 +123,6 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
     kvh = r / p.B;
     head = kvh * G + hg;
   }
-
   // Sequence extents, clamped so every access stays inside the tensors.
   const bool fixed = PAGED && p.kv_len_fixed >= 0;
   const int q_start = fixed ? 0 : min(max(p.cu_q[b], 0), p.total_q);
@@ -206,24 +188,24 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
   const bool flip = c < 0.f;
   c = flip ? -c : (c == 0.f ? 1e-30f : c);
 
-  // ---- Q^T fragments (B operand): lane (row j16 of this wave, group grp)
-  // holds q[32 ks + 8 grp .. + 8] for k-step ks.
-  const int my_row = r0 + wave * RW + j16;
+  // ---- Q^T fragments (B operand): lane (row l32 of the pair, half hl) holds
+  // q[16 ks + 8 hl .. + 8] for k-step ks.
+  const int my_row = r0 + pair * PR + l32;
   const bool row_ok = my_row < Lq;
   v8 qf[QK];
   {
     const elem* qr = reinterpret_cast<const elem*>(p.q) +
-                     ((size_t)(q_start + (row_ok ? my_row : 0)) * p.Hq + head) * D + grp * 8;
+                     ((size_t)(q_start + (row_ok ? my_row : 0)) * p.Hq + head) * D + hl * 8;
 #pragma unroll
     for (int s = 0; s < QK; ++s) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qr + s * 32);
+      u32x4 v = *reinterpret_cast<const u32x4*>(qr + s * 16);
       if (flip) v ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
       qf[s] = row_ok ? __builtin_bit_cast(v8, v) : v8{};
     }
   }
 
-  // ---- DMA geometry (as prefill.hip): instruction i of this wave fills the
-  // 1 KiB at tile byte (wave * DMA + i) * 1024, RPI whole rows.
+  // ---- DMA geometry: instruction i of this wave fills the 1 KiB at tile
+  // byte (wave * DMA + i) * 1024, RPI whole rows.
   constexpr int RPI = 64 / CH;
   const char* kg = reinterpret_cast<const char*>(p.k);
   const char* vg = reinterpret_cast<const char*>(p.v);
@@ -298,27 +280,34 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
   };
 
   // ---- per-lane LDS read offsets
-  // K fragment (key block kb, k-step ks): row 16 kb + j16, logical chunk
-  // 4 ks + grp.  The swizzle touches chunk bits 0-3, so k-steps 4.. are 256
-  // bytes further on and key block 1 is 16 rows further on.
-  int kro[4];
+  // K fragment (k-step ks) of this wave's 32 keys: row l32 of the half,
+  // logical chunk 2 ks + hl; k-steps 8.. are 256 bytes further on.
+  const int kbase = half * 32 * ROWB;
+  int kro[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) kro[q] = j16 * ROWB + (k_chunk(j16, 4 * q + grp) << 4);
-  // V^T fragment (d block db, keys 4 grp ..): a transposing read in which lane
-  // (j16, grp) addresses row 4 grp + j16 / 4, elements 16 db + 4 (j16 % 4) .. + 3.
-  // The swizzle touches 32-byte unit bits 0-2, so d blocks 8.. are 256 bytes on.
-  const int tr_row = 4 * grp + (j16 >> 2);
-  int vro[8];
+  for (int ks = 0; ks < 8; ++ks) kro[ks] = kbase + l32 * ROWB + (k_chunk(l32, 2 * ks + hl) << 4);
+  // V^T fragment (d block db of this wave's half, key step ps): transposing
+  // reads of rows 16 ps + tr_row (+ 8), d = 128 half + 32 db + tr_col.
+  const int grp = lane >> 4, gj = lane & 15;
+  const int tr_row = 4 * (grp >> 1) + (gj >> 2);
+  const int tr_col = 16 * (grp & 1) + 4 * (gj & 3);
+  int vro[DBH];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) vro[u] = tr_row * ROWB + ((u ^ (tr_row & 7)) << 5) + 8 * (j16 & 3);
+  for (int db = 0; db < DBH; ++db) {
+    const int d = db * 32 + tr_col;
+    vro[db] = half * 256 + tr_row * ROWB + (v_chunk(tr_row, d >> 3) << 4) + (d & 7) * 2;
+  }
+  // P^T pieces: 16-byte piece k of lane L at k * 1024 + L * 16 (conflict-free).
+  char* const p_mine = p_buf + wave * PB + lane * 16;
+  const char* const p_pair = p_buf + pair * 2 * PB + lane * 16;
 
-  f32x4 o[DB];
+  f32x16 o[DBH];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) o[i] = f32x4{};
+  for (int i = 0; i < DBH; ++i) o[i] = f32x16{};
   float m = kNegInf, lsum = 0.f;
 
-  const int w_first = r0 + wave * RW;
-  const int w_last = min(w_first + RW - 1, Lq - 1);
+  const int w_first = r0 + pair * PR;
+  const int w_last = min(w_first + PR - 1, Lq - 1);
   const bool wave_rows = w_first < Lq;
   const int pos = my_row + off;
   int w_kt = 0, w_fast = 0, w_lead = 0;
@@ -332,153 +321,140 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
     w_fast = min(lim, w_kt);
   }
 
-  auto kfrag = [&](const char* kbuf, int kb, int ks) {
-    return *reinterpret_cast<const v8*>(kbuf + kb * 16 * ROWB + (ks >> 2) * 256 + kro[ks & 3]);
-  };
-  auto qk = [&](const char* kbuf, f32x4 (&s)[KB]) {
+  auto qk = [&](const char* kbuf) {
+    f32x16 s = {};
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      s[kb] = f32x4{};
-#pragma unroll
-      for (int ks = 0; ks < QK; ++ks) s[kb] = mfma(kfrag(kbuf, kb, ks), qf[ks], s[kb]);
-    }
+    for (int ks = 0; ks < QK; ++ks)
+      s = mfma32(*reinterpret_cast<const v8*>(kbuf + (ks >> 3) * 256 + kro[ks & 7]), qf[ks], s);
+    return s;
   };
 
-  auto mask = [&](int kt, f32x4 (&s)[KB]) {
-    const int k0 = kt * BN;
+  // Scores of this wave's keys past the end, right of the lane's diagonal or
+  // left of its window -> -inf.
+  auto mask = [&](int kt, f32x16& s) {
+    const int k0 = kt * BN + half * 32;
     const int lim = up ? min(pos + rb, Lk - 1) : Lk - 1;
     const int lo = win >= 0 ? pos - win : 0;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + 16 * kb + 4 * grp + r;
-        s[kb][r] = (key > lim || key < lo) ? kNegInf : s[kb][r];
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+      s[r] = (key > lim || key < lo) ? kNegInf : s[r];
+    }
   };
 
-  auto update_max = [&](f32x4 (&s)[KB]) {
-    float mr = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mr = fmaxf(mr, s[kb][r]);
-    const float mt = max_groups(mr) * c;
+  // Running max agreed by the pair: the larger of the two tile maxima; raised
+  // (O, l rescaled) only past the slack.  Both waves see the same values.
+  auto agree_max = [&](float mine, float theirs) {
+    const float mt = fmaxf(mine, theirs) * c;
     const bool raise = mt > m + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
       const float alpha = raise ? exp2_fast(m - mt) : 1.f;
       m = raise ? mt : m;
       lsum *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DBH; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[db][r] *= alpha;
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
   };
 
-  // P^T = 2^(s c - m) in the B-operand order {kb 0 keys, kb 1 keys}; the row
-  // sum adds the rounded weights.
-  auto weights = [&](f32x4 (&s)[KB], v8 (&pb)[PS], float nm) {
+  // P^T of this wave's 32 keys (two 16-key k-steps): kept for this wave's
+  // O^T and posted to LDS for the partner; the row sum adds the rounded weights.
+  auto weights = [&](const f32x16& s, float nm, v8 (&pw)[2]) {
     const v2 one = {(elem)1.f, (elem)1.f};
     float psum = 0.f;
 #pragma unroll
-    for (int ps = 0; ps < PS; ++ps) {
+    for (int ps = 0; ps < 2; ++ps) {
       v8 w;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        w[e] = (elem)exp2_fast(__builtin_fmaf(s[2 * ps + (e >> 2)][e & 3], c, nm));
+      for (int e = 0; e < 8; ++e) w[e] = (elem)exp2_fast(__builtin_fmaf(s[ps * 8 + e], c, nm));
 #pragma unroll
       for (int e = 0; e < 8; e += 2) psum = H::dot2(v2{w[e], w[e + 1]}, one, psum);
-      pb[ps] = w;
+      *reinterpret_cast<v8*>(p_mine + ps * 1024) = w;
+      pw[ps] = w;
     }
     lsum += psum;
   };
 
-  auto vfrag = [&](const char* vbuf, int db, int ps) {
-    const int ro = ps * 32 * ROWB + (db >> 3) * 256 + vro[db & 7];
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_char*)vbuf + ro));
-    const v4i16 hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_char*)vbuf + ro + 16 * ROWB));
-    return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-  auto pv = [&](const char* vbuf, v8 (&pb)[PS]) {
+  // O^T += V^T . P^T over one wave's 32 keys: key half kh of the tile (this
+  // wave's own, or its partner's), P^T given.
+  auto pv_half = [&](const char* vbuf, int kh, const v8 (&pw)[2]) {
+    const char* vb = vbuf + kh * 32 * ROWB;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DBH; ++db)
 #pragma unroll
-      for (int ps = 0; ps < PS; ++ps) o[db] = mfma(vfrag(vbuf, db, ps), pb[ps], o[db]);
+      for (int ps = 0; ps < 2; ++ps) {
+        const int ro = ps * 16 * ROWB + vro[db];
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_char*)vb + ro));
+        const v4i16 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((lds_char*)vb + ro + 8 * ROWB));
+        o[db] = mfma32(__builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)),
+                       pw[ps], o[db]);
+      }
   };
 
-  f32x4 sa[KB], sb[KB];
-  int pid_v = 0, pid_k = 0;
-  auto step = [&](auto slot_tag, auto fast_tag, int kt, f32x4 (&scur)[KB], f32x4 (&snext)[KB]) {
-    constexpr int SLOT = decltype(slot_tag)::value;
-    constexpr bool FAST = decltype(fast_tag)::value != 0;
-    // 2: a steady-state step whose two DMAs are whole tiles (no clamped rows)
-    constexpr int FULL = decltype(fast_tag)::value == 2 ? 1 : 0;
-    char* const KDST = kslot(Idx<SLOT>{});
-    char* const KNXT = kslot(Idx<SLOT + 1>{});
-    char* const VCUR = vslot(Idx<SLOT>{});
-    char* const VDST = vslot(Idx<SLOT + R - 1>{});
-    if (kt + R - 1 < n_kt) dma(kt + R - 1, VDST, true, pid_v, Idx<FULL>{});
-    if (kt + R < n_kt) dma(kt + R, KDST, false, pid_k, Idx<FULL>{});
-    v8 pb[PS];
-    if constexpr (FAST) {
-      update_max(scur);
-      qk(KNXT, snext);
-      weights(scur, pb, -m);
-      pv(VCUR, pb);
-      // Issue order: eight K fragment reads ahead of the S^T MFMAs, each S^T
-      // MFMA followed by the next K read and two vector ops of the softmax,
-      // the first V^T reads behind the last eight S^T MFMAs, then each O^T
-      // MFMA with the transposing reads of a later fragment.  (Left to the
-      // compiler, the reads ran one or two MFMAs ahead and the waves waited
-      // on LDS before almost every MFMA.)
-      constexpr int KA = 8;
-      __builtin_amdgcn_sched_group_barrier(0x100, KA, 0);             // K reads
-#pragma unroll
-      for (int i = 0; i < KB * QK - KA; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // S^T MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);            // next K read
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);            // softmax
-      }
-#pragma unroll
-      for (int i = 0; i < KA; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);            // first V reads
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < DB * PS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // O^T MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);            // V reads ahead
-        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
-      }
-    } else if (kt < w_kt) {
-      if (kt < w_lead || kt >= w_fast) mask(kt, scur);
-      update_max(scur);
-      if (kt + 1 < w_kt) qk(KNXT, snext);
-      weights(scur, pb, m == kNegInf ? 0.f : -m);
-      pv(VCUR, pb);
-    }
-    if constexpr (PAGED) {
-      pid_v = pid_k;
-      if (kt + R + 1 < n_kt) pid_k = load_pid(kt + R + 1);
-    }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  auto barrier = [&]() {
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     asm volatile("s_barrier" ::: "memory");
   };
 
+  // One tile step.  On entry S^T(kt) of this wave is in registers and both
+  // waves' tile maxima are in m_buf[kt % 2]; K(kt + 1) and V(kt) are in LDS.
+  // The step starts the DMA of V(kt + 1) and K(kt + 2) (slots last read in
+  // step kt - 1), agrees the running max and posts this wave's P(kt), computes
+  // S^T(kt + 1) beside those exponentials and posts its maxima, accumulates
+  // O^T over its own P(kt) and, after a barrier, over its partner's.  FAST:
+  // tiles kt and kt + 1 unmasked and needed by every row.  (Issue-order hints
+  // as in the head_dim 128 kernel measured 1.5 % slower here than the
+  // compiler's own order.)
+  int pid_v = 0, pid_k = 0;     // pages of V(kt + 1) and K(kt + 2) for the next DMA
+  float mine = kNegInf;         // this wave's tile max of S^T(kt)
+  auto step = [&](auto slot_tag, auto fast_tag, int kt, f32x16& scur, f32x16& snext) {
+    constexpr int SLOT = decltype(slot_tag)::value;
+    constexpr bool FAST = decltype(fast_tag)::value != 0;
+    constexpr int FULL = decltype(fast_tag)::value == 2 ? 1 : 0;
+    if (kt + 1 < n_kt) dma(kt + 1, vslot(Idx<SLOT + 1>{}), true, pid_v, Idx<FULL>{});
+    if (kt + 2 < n_kt) dma(kt + 2, kslot(Idx<SLOT>{}), false, pid_k, Idx<FULL>{});
+    const bool need = FAST || kt < w_kt;
+    const bool need_n = FAST || kt + 1 < w_kt;
+    v8 pw[2];
+    if (need) {
+      agree_max(mine, m_buf[kt & 1][partner][l32]);
+      weights(scur, FAST ? -m : (m == kNegInf ? 0.f : -m), pw);
+    }
+    mine = kNegInf;
+    if (need_n) {
+      snext = qk(kslot(Idx<SLOT + 1>{}));
+      if (!FAST && (kt + 1 < w_lead || kt + 1 >= w_fast)) mask(kt + 1, snext);
+      float mr = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mr = fmaxf(mr, snext[r]);
+      mine = max_halves(mr);
+    }
+    if (hl == 0) m_buf[(kt + 1) & 1][wave][l32] = mine;
+    if (need) pv_half(vslot(Idx<SLOT>{}), half, pw);     // this wave's own keys first
+    barrier();
+    if (need) {
+      v8 pp[2];
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps) pp[ps] = *reinterpret_cast<const v8*>(p_pair + (half ^ 1) * PB + ps * 1024);
+      pv_half(vslot(Idx<SLOT>{}), half ^ 1, pp);
+    }
+    if constexpr (PAGED) {
+      pid_v = pid_k;
+      if (kt + 3 < n_kt) pid_k = load_pid(kt + 3);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    barrier();
+  };
+
+  // Tiles that every row of the workgroup sees whole and unmasked; a FAST
+  // step also computes the scores of the next tile, so it needs two of them.
   int n_fast = t_full;
   if (up) n_fast = min(n_fast, max(0, r0 + off + rb + 1) / BN);
-  {
-    const int wkend0 = up ? max(0, min(Lk, min(r0 + RW - 1, Lq - 1) + off + rb + 1)) : Lk;
-    const int w_kt0 = min(n_kt, (wkend0 + BN - 1) / BN);
-    n_fast = max(0, min(n_fast, w_kt0 - 1));
-    n_fast -= n_fast % R;
-  }
-  // Leading tiles that some row's window cuts (from the last row, whose
-  // window starts latest) run the masked step too; a multiple of R.
+  n_fast = max(0, min(n_fast, n_kt) - 1);
+  n_fast -= n_fast % R;
+  // Leading tiles that some row's window cuts run the masked step; a multiple of R.
   int n_lead = 0;
   if (win >= 0) {
     n_lead = min(n_kt, max(0, r_last + off - win + BN - 1) / BN);
@@ -486,30 +462,35 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
   }
   n_fast = max(n_fast, n_lead);
 
-  // prologue: K(0 .. R-1) and V(0 .. R-2) in LDS, S^T(0) in registers
-#pragma unroll
-  for (int t = 0; t < R; ++t) {
-    if (t < n_kt) {
-      const int pid = load_pid(t);
-      char* kd = t == 0 ? kslot(Idx<0>{}) : kslot(Idx<1>{});
-      char* vd = t == 0 ? vslot(Idx<0>{}) : vslot(Idx<1>{});
-      dma(t, kd, false, pid, Idx<0>{});
-      if (t + 1 < R) dma(t, vd, true, pid, Idx<0>{});
-      else pid_v = pid;
-    }
+  // prologue: K(0), V(0) in slot 0 and K(1) in slot 1; S^T(0) and its maxima.
+  if (n_kt > 0) {
+    const int pid = load_pid(0);
+    dma(0, k_ring0, false, pid, Idx<0>{});
+    dma(0, v_ring0, true, pid, Idx<0>{});
   }
-  if (R < n_kt) pid_k = load_pid(R);
+  if (1 < n_kt) {
+    pid_v = load_pid(1);
+    dma(1, k_ring1, false, pid_v, Idx<0>{});
+  }
+  if (2 < n_kt) pid_k = load_pid(2);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
-  if (n_kt > 0) qk(k_ring0, sa);
+  f32x16 sa = {}, sb = {};
+  if (n_kt > 0 && 0 < w_kt) {
+    sa = qk(k_ring0);
+    if (0 < w_lead || 0 >= w_fast) mask(0, sa);
+    float mr = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mr = fmaxf(mr, sa[r]);
+    mine = max_halves(mr);
+  }
+  if (hl == 0) m_buf[0][wave][l32] = mine;
   __syncthreads();
   int kt = 0;
   for (; kt < n_lead; kt += R) {
     step(Idx<0>{}, Idx<0>{}, kt, sa, sb);
     if (kt + 1 < n_kt) step(Idx<1>{}, Idx<0>{}, kt + 1, sb, sa);
   }
-  // Steady-state steps whose DMAs (tiles kt + R - 1 and kt + R) are whole
-  // tiles skip the clamped-row addressing of the last, partial tile.
   for (; kt < n_fast && kt + R + 1 < t_full; kt += R) {
     step(Idx<0>{}, Idx<2>{}, kt, sa, sb);
     step(Idx<1>{}, Idx<2>{}, kt + 1, sb, sa);
@@ -525,44 +506,49 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
 
   const bool any_bad = __syncthreads_or(bad);
 
-  // ---- epilogue: lane (row j16, group grp) holds O^T[16 db + 4 grp + r][row]
-  const float ltot = sum_groups(lsum);
+  // ---- epilogue: the pair's row sums (each wave summed its own keys)
+  const float lmine = sum_halves(lsum);
+  if (hl == 0) m_buf[0][wave][l32] = lmine;
+  __syncthreads();
+  const float ltot = lmine + m_buf[0][partner][l32];
   float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   float lse_v = ltot > 0.f ? (m + log2_fast(ltot)) * kLn2 : kNegInf;
   if (any_bad) {
     inv = __builtin_nanf("");
     lse_v = inv;
   }
+  // Lane (row l32, hl) holds O^T[128 half + 32 db + 8 (r / 4) + 4 hl + r % 4][row].
   if (p.merge_lse == nullptr) {
-    // Stage this wave's 16 x D tile through LDS (the K ring is free: every
-    // wave is past its last step) and store whole rows, 32 lanes x 16 bytes
-    // per row, instead of 8-byte pieces scattered over 16 rows per store.
-    // Chunk q of row r sits at chunk q ^ (r mod 16).
-    char* stage = (wave < 4 ? k_ring0 : k_ring1) + (wave & 3) * RW * ROWB;
+    // Stage this wave's 32 rows x 128 d through LDS (the K ring is free: every
+    // wave is past its last step) and store whole 256-byte row halves, 16
+    // lanes x 16 bytes per row.  Chunk q of row r sits at chunk q ^ (r mod 16).
+    char* stage = (wave < 4 ? k_ring0 : k_ring1) + (wave & 3) * PR * 256;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      typename H::v4 v;
+    for (int db = 0; db < DBH; ++db)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (elem)(o[db][r] * inv);
-      const int q = 2 * db + (grp >> 1);
-      *reinterpret_cast<typename H::v4*>(stage + j16 * ROWB + ((q ^ j16) << 4) + (grp & 1) * 8) = v;
-    }
-    const int c32 = lane & 31;
+      for (int rq = 0; rq < 4; ++rq) {
+        typename H::v4 v;
 #pragma unroll
-    for (int i = 0; i < RW / 2; ++i) {
-      const int r = i * 2 + (lane >> 5);
-      const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * ROWB + ((c32 ^ (r & 15)) << 4));
-      const int row = r0 + wave * RW + r;
+        for (int r = 0; r < 4; ++r) v[r] = (elem)(o[db][4 * rq + r] * inv);
+        const int q = 4 * db + rq;
+        *reinterpret_cast<typename H::v4*>(stage + l32 * 256 + ((q ^ (l32 & 15)) << 4) + hl * 8) = v;
+      }
+    const int c16 = lane & 15;
+#pragma unroll
+    for (int i = 0; i < PR / 4; ++i) {
+      const int r = i * 4 + (lane >> 4);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * 256 + ((c16 ^ (r & 15)) << 4));
+      const int row = w_first + r;
       if (row < Lq)
         *reinterpret_cast<u32x4*>(reinterpret_cast<elem*>(p.out) +
-                                  ((size_t)(q_start + row) * p.Hq + head) * D + c32 * 8) = x;
+                                  ((size_t)(q_start + row) * p.Hq + head) * D + half * 128 + c16 * 8) = x;
     }
-    if (grp == 0 && row_ok) p.lse[(size_t)(q_start + my_row) * p.Hq + head] = lse_v;
+    if (half == 0 && hl == 0 && row_ok) p.lse[(size_t)(q_start + my_row) * p.Hq + head] = lse_v;
     return;
   }
   if (!row_ok) return;
   const size_t orow = (size_t)(q_start + my_row) * p.Hq + head;
-  elem* og = reinterpret_cast<elem*>(p.out) + orow * D + 4 * grp;
+  elem* og = reinterpret_cast<elem*>(p.out) + orow * D + half * 128 + 4 * hl;
   {
     // Merge with another state over disjoint keys (see prefill.hip).
     const float lp = p.merge_lse[orow] * kLog2e;
@@ -583,18 +569,21 @@ __global__ __launch_bounds__(NT, 1) void prefill16_kernel(PrefillParams p,
       wp *= rd;
       lse_v = (mx + log2_fast(den)) * kLn2;
     }
-    const elem* pg = reinterpret_cast<const elem*>(p.merge_o) + orow * D + 4 * grp;
+    const elem* pg = reinterpret_cast<const elem*>(p.merge_o) + orow * D + half * 128 + 4 * hl;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      typename H::v4 v;
-      typename H::v4 w{};
-      if (wp != 0.f) w = *reinterpret_cast<const typename H::v4*>(pg + 16 * db);
+    for (int db = 0; db < DBH; ++db)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = (elem)(o[db][r] * wo + (float)w[r] * wp);
-      *reinterpret_cast<typename H::v4*>(og + 16 * db) = v;
-    }
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d = 32 * db + 8 * rq;
+        typename H::v4 v;
+        typename H::v4 w{};
+        if (wp != 0.f) w = *reinterpret_cast<const typename H::v4*>(pg + d);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (elem)(o[db][4 * rq + r] * wo + (float)w[r] * wp);
+        *reinterpret_cast<typename H::v4*>(og + d) = v;
+      }
   }
-  if (grp == 0) p.lse[orow] = lse_v;
+  if (half == 0 && hl == 0) p.lse[orow] = lse_v;
 }
 
 template <typename E, bool PAGED>
@@ -602,9 +591,9 @@ hipError_t launch16_t(const PrefillParams& p, hipStream_t s) {
   const int total = p.Hq * p.B * p.q_tiles;
   dim3 grid(8 * ((total + 7) / 8));
   if (PAGED && p.page_shift > 0)
-    hipLaunchKernelGGL((prefill16_kernel<E, PAGED, PAGED>), grid, dim3(NT), 0, s, p, p.page_table);
+    hipLaunchKernelGGL((prefill256_kernel<E, PAGED, PAGED>), grid, dim3(NT), 0, s, p, p.page_table);
   else
-    hipLaunchKernelGGL((prefill16_kernel<E, PAGED, false>), grid, dim3(NT), 0, s, p, p.page_table);
+    hipLaunchKernelGGL((prefill256_kernel<E, PAGED, false>), grid, dim3(NT), 0, s, p, p.page_table);
   return hipGetLastError();
 }
 

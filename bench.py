@@ -646,7 +646,7 @@ KERNEL_SOURCES = {
     "decode_fp8": ["decode.hip"],
     "decode_rope": ["decode.hip"],
     "prefill": ["prefill.hip"],
-    "prefill_paged": ["prefill16.hip"],     # the chunked workload has head_dim 256
+    "prefill_paged": ["prefill256.hip"],     # the chunked workload has head_dim 256
 }
 
 

@@ -24,7 +24,7 @@ INCLUDE = os.path.join(ROOT, "include")
 DRIVER = os.path.join(ROOT, "tests", "sanitize", "abi_fuzz.c")
 OUT = os.path.join(ROOT, "_build", "sanitize")
 LLVM = "/opt/rocm/llvm/bin"
-KERNELS = ["decode.hip", "prefill.hip", "prefill16.hip", "merge.hip"]
+KERNELS = ["decode.hip", "prefill.hip", "prefill256.hip", "merge.hip"]
 HEADERS = [os.path.join(CSRC, h) for h in ("common.h", "launch.h")] + [os.path.join(INCLUDE, "attn.h")]
 # Host code only: each -fsanitize= applies to the host compilation.
 SAN = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=all"]
