@@ -104,6 +104,29 @@ def test_large_logits(gpu):
     assert_parity(out, lse, ro, rl, torch.bfloat16, "large logits")
 
 
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("causal", [True, False])
+def test_running_max_raised_across_tiles_and_key_halves(gpu, D, causal):
+    """Keys scaled so that each row's maximum score jumps between 64-key tiles
+    and between the two 32-key halves of a tile (head_dim 256 splits a
+    tile's scores between two waves that must agree on the running max):
+    the running max is raised many times, by different amounts per half."""
+    case = workloads.make_prefill(B=2, Hq=4, Hkv=2, D=D, lens_q=[333, 200], lens_k=[333, 520],
+                                  dtype=torch.bfloat16, seed=245, causal=causal)
+    j = torch.arange(case.k.shape[0])
+    pos = j - torch.repeat_interleave(case.cu_seqlens_k[:-1].long(), torch.diff(case.cu_seqlens_k.long()))
+    f = 1.0 + 3.0 * ((pos % 64) >= 32).float() + 0.75 * (pos // 64).float()
+    # every third tile puts its larger keys in the first half instead
+    f = torch.where((pos // 64) % 3 == 1, 1.0 + 5.0 * ((pos % 64) < 32).float(), f)
+    case.k = (case.k.float() * f[:, None, None]).to(case.k.dtype)
+    case.scale = 4.0 / D ** 0.5
+    out, lse = _varlen(case, gpu)
+    ro, rl = _ref(case)
+    assert torch.isfinite(out.float()).all()
+    assert rl.abs().max() > 100
+    assert_parity(out, lse, ro, rl, torch.bfloat16, f"raised max D{D} causal {causal}")
+
+
 def test_deterministic(gpu):
     case = workloads.make_prefill(B=3, Hq=8, Hkv=1, D=128, len_range=(100, 700), dtype=torch.bfloat16,
                                   seed=250, causal=True)
