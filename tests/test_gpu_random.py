@@ -178,3 +178,76 @@ def test_random_prefill_paged(gpu, seed):
                                       case.kv_lens, causal, case.scale, window_left=wl,
                                       window_right=wr)
     assert_parity(out, lse, ro, rl, dtype, desc)
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_random_prefill_d256(gpu, seed):
+    """head_dim 256 only (pairs of waves share 32 rows and split each tile's
+    keys): varlen or paged, every page size and layout, windows, cascade,
+    fp16, query and key lengths around the 32-key halves and 64-key tiles."""
+    import attention_qk_online_amd as A
+    rng = random.Random(9500 + seed)
+    dtype = rng.choice([torch.bfloat16, torch.float16])
+    Hkv = rng.choice([1, 2, 4])
+    G = rng.choice([1, 2, 4])
+    causal = rng.random() < 0.7
+    paged = rng.random() < 0.5
+    B = rng.randint(1, 4)
+
+    def near_tile():
+        return max(1, rng.choice([32, 64, 96, 128, 192]) * rng.randint(1, 4) + rng.choice([-1, 0, 1]))
+
+    if not paged:
+        lens_k = [near_tile() if rng.random() < 0.5 else rng.randint(1, 700) for _ in range(B)]
+        lens_q = [k if rng.random() < 0.5 else near_tile() for k in lens_k]
+        wl = rng.choice([-1, -1, rng.randint(0, 300)])
+        wr = rng.choice([-1, -1, rng.randint(0, 300)])
+        desc = (f"seed {seed}: varlen {dtype} Hq{G * Hkv} Hkv{Hkv} causal {causal} window ({wl}, {wr}) "
+                f"lens_q {lens_q} lens_k {lens_k}")
+        print(desc, flush=True)
+        case = workloads.make_prefill(B=B, Hq=G * Hkv, Hkv=Hkv, D=256, lens_q=lens_q, lens_k=lens_k,
+                                      dtype=dtype, seed=9500 + seed, causal=causal)
+        out, lse = A.prefill_varlen(case.q.to(gpu), case.k.to(gpu), case.v.to(gpu),
+                                    case.cu_seqlens_q.to(gpu), case.cu_seqlens_k.to(gpu),
+                                    max_seqlen_q=max(1, case.max_seqlen_q),
+                                    max_seqlen_k=max(1, case.max_seqlen_k), causal=causal,
+                                    scale=case.scale, window_left=wl, window_right=wr)
+        torch.cuda.synchronize()
+        ro, rl = oracle.ref_prefill_varlen(case.q, case.k, case.v, case.cu_seqlens_q,
+                                           case.cu_seqlens_k, causal, case.scale,
+                                           window_left=wl, window_right=wr)
+        assert_parity(out, lse, ro, rl, dtype, desc)
+        return
+    P = rng.choice([16, 32, 64, 128, 256])
+    layout = rng.choice(["NHD", "HND"])
+    cascade = rng.random() < 0.3
+    shared = P * rng.randint(1, 3) if cascade else 0
+    chunks = [near_tile() if rng.random() < 0.5 else rng.randint(1, 300) for _ in range(B)]
+    cached = [shared + (near_tile() if rng.random() < 0.5 else rng.randint(0, 400)) for _ in range(B)]
+    if cascade and causal:
+        cached = [max(c, shared) for c in cached]
+    wl = -1 if cascade else rng.choice([-1, -1, rng.randint(0, 300)])
+    wr = -1 if cascade else rng.choice([-1, -1, rng.randint(0, 300)])
+    desc = (f"seed {seed}: paged {dtype} Hq{G * Hkv} Hkv{Hkv} P{P} {layout} causal {causal} "
+            f"cascade {shared} window ({wl}, {wr}) chunks {chunks} cached {cached}")
+    print(desc, flush=True)
+    case = workloads.make_paged_prefill(B=B, Hq=G * Hkv, Hkv=Hkv, D=256, page_size=P, chunk=chunks,
+                                        cached=cached, shared_prefix=shared, dtype=dtype,
+                                        seed=9500 + seed, causal=causal, spare_pages=1)
+    kg, vg = case.pools(gpu, layout)
+    args = (case.q.to(gpu), case.cu_seqlens_q.to(gpu), kg, vg, case.page_table.to(gpu),
+            case.kv_lens.to(gpu))
+    if cascade:
+        out, lse = A.prefill_paged_cascade(*args, max_seqlen_q=case.max_seqlen_q,
+                                           max_kv_len=case.max_kv_len, shared_prefix_len=shared,
+                                           causal=causal, scale=case.scale, kv_layout=layout)
+    else:
+        out, lse = A.prefill_paged(*args, max_seqlen_q=case.max_seqlen_q,
+                                   max_kv_len=case.max_kv_len, causal=causal, scale=case.scale,
+                                   kv_layout=layout, window_left=wl, window_right=wr)
+    torch.cuda.synchronize()
+    kp, vp = case.pools()
+    ro, rl = oracle.ref_prefill_paged(case.q, case.cu_seqlens_q, kp, vp, case.page_table,
+                                      case.kv_lens, causal, case.scale, window_left=wl,
+                                      window_right=wr)
+    assert_parity(out, lse, ro, rl, dtype, desc)
