@@ -841,13 +841,19 @@ __global__ __launch_bounds__(kMaxGroupWaves * 64, D == 256 ? 1 : 2) void decode_
 // hundreds of runs) the S partial states of a head are combined through LDS.
 // Lanes own d.  Pairs held by a single run were written by that run; empty
 // requests get out 0 and lse -inf and inconsistent ones NaN.
-template <typename E, int D, int G, int S>
-__global__ __launch_bounds__(G * S * 64) void decode_merge_kernel(DecodeParams p) {
-  constexpr int DL = D / 64 > 0 ? D / 64 : 1;
+// HPW query heads per workgroup: G (S waves each), or 1, the head then
+// taken from blockIdx.z / DS; DS slices of d, the slice blockIdx.z % DS.
+template <typename E, int D, int G, int S, int DS, int HPW>
+__global__ __launch_bounds__(HPW * S * 64) void decode_merge_kernel(DecodeParams p) {
+  static_assert(HPW == G || HPW == 1, "all heads of the group, or one");
+  constexpr int DW = D / DS;                        // d of this workgroup
+  constexpr int DL = DW / 64 > 0 ? DW / 64 : 1;
   const int kvh = blockIdx.x, b = blockIdx.y;
+  const int d0 = (blockIdx.z % DS) * DW;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = wv / S, sl = wv % S;
+  const int g = HPW == G ? wv / S : (int)blockIdx.z / DS, sl = wv % S;
+  const bool lse_writer = blockIdx.z % DS == 0;
   int U = 0, pre = 0;
   for (int c = 0; c < p.B; c += 64) {
     const int bb = c + lane;
@@ -863,18 +869,18 @@ __global__ __launch_bounds__(G * S * 64) void decode_merge_kernel(DecodeParams p
   const int nseg = np > 0 ? (start_pair + np - 1) / W - start_pair / W + 1 : 0;
   if (nseg == 1) return;                 // the same for every wave of the workgroup
   const int h = kvh * G + g;
-  E* og = reinterpret_cast<E*>(p.out) + ((size_t)b * p.Hq + h) * D;
+  E* og = reinterpret_cast<E*>(p.out) + ((size_t)b * p.Hq + h) * D + d0;
   if (bad || nseg == 0) {
     if (sl == 0) {
       const float val = bad ? __builtin_nanf("") : 0.f;
-      for (int d = lane; d < D; d += 64) store_out(og + d, val);
-      if (lane == 0) p.lse[(size_t)b * p.Hq + h] = bad ? val : kNegInf;
+      for (int d = lane; d < DW; d += 64) store_out(og + d, val);
+      if (lane == 0 && lse_writer) p.lse[(size_t)b * p.Hq + h] = bad ? val : kNegInf;
     }
     return;
   }
   const size_t slot0 = ((size_t)b * p.Hkv + kvh) * p.max_segs;
   const float* pl = p.part_lse + slot0 * G + g;           // stride G between segments
-  const float* po = p.part_o + (slot0 * G + g) * D;       // stride G*D between segments
+  const float* po = p.part_o + (slot0 * G + g) * D + d0;  // stride G*D between segments
   // This wave's slice of the segments.
   const int per = (nseg + S - 1) / S;
   const int s0 = min(nseg, sl * per), s1 = min(nseg, s0 + per);
@@ -896,7 +902,7 @@ __global__ __launch_bounds__(G * S * 64) void decode_merge_kernel(DecodeParams p
       for (int t = 0; t < MB; ++t)
 #pragma unroll
         for (int i = 0; i < DL; ++i)
-          v[t][i] = (j + t < nj && lane + 64 * i < D) ? po[(size_t)(j0 + j + t) * G * D + lane + 64 * i] : 0.f;
+          v[t][i] = (j + t < nj && lane + 64 * i < DW) ? po[(size_t)(j0 + j + t) * G * D + lane + 64 * i] : 0.f;
     };
     load_o(0);
     nan_seen |= __builtin_amdgcn_ballot_w64(ls != ls) != 0;
@@ -924,6 +930,7 @@ __global__ __launch_bounds__(G * S * 64) void decode_merge_kernel(DecodeParams p
       }
     }
   }
+  const int gs = HPW == G ? g : 0;        // this head's first wave slot in the workgroup
   if constexpr (S == 1) {
     const float mu = mx == kNegInf ? 0.f : mx;
     const float inv = ws > 0.f ? 1.f / ws : 0.f;
@@ -931,18 +938,18 @@ __global__ __launch_bounds__(G * S * 64) void decode_merge_kernel(DecodeParams p
     if (nan_seen) lse_nat = __builtin_nanf("");
 #pragma unroll
     for (int i = 0; i < DL; ++i)
-      if (lane + 64 * i < D) store_out(og + lane + 64 * i, nan_seen ? lse_nat : acc[i] * inv);
-    if (lane == 0) p.lse[(size_t)b * p.Hq + h] = lse_nat;
+      if (lane + 64 * i < DW) store_out(og + lane + 64 * i, nan_seen ? lse_nat : acc[i] * inv);
+    if (lane == 0 && lse_writer) p.lse[(size_t)b * p.Hq + h] = lse_nat;
     return;
   }
   // Combine the S slices of each head: weights e^(mx_s - M) over the slices'
   // maxima M; an empty slice (mx -inf, ws 0, acc 0) adds nothing.
-  __shared__ float sh_acc[16][D];
+  __shared__ float sh_acc[16][DW];
   __shared__ float sh_mx[16], sh_ws[16];
   __shared__ int sh_nan[16];
 #pragma unroll
   for (int i = 0; i < DL; ++i)
-    if (lane + 64 * i < D) sh_acc[wv][lane + 64 * i] = acc[i];
+    if (lane + 64 * i < DW) sh_acc[wv][lane + 64 * i] = acc[i];
   if (lane == 0) {
     sh_mx[wv] = mx;
     sh_ws[wv] = ws;
@@ -954,26 +961,26 @@ __global__ __launch_bounds__(G * S * 64) void decode_merge_kernel(DecodeParams p
   bool any_nan = false;
 #pragma unroll
   for (int k = 0; k < S; ++k) {
-    M = fmaxf(M, sh_mx[g * S + k]);
-    any_nan |= sh_nan[g * S + k] != 0;
+    M = fmaxf(M, sh_mx[gs * S + k]);
+    any_nan |= sh_nan[gs * S + k] != 0;
   }
   const float mu = M == kNegInf ? 0.f : M;
   float wtot = 0.f, tot[DL] = {};
 #pragma unroll
   for (int k = 0; k < S; ++k) {
-    const float f = exp2_fast((sh_mx[g * S + k] - mu) * kLog2e);
-    wtot += f * sh_ws[g * S + k];
+    const float f = exp2_fast((sh_mx[gs * S + k] - mu) * kLog2e);
+    wtot += f * sh_ws[gs * S + k];
 #pragma unroll
     for (int i = 0; i < DL; ++i)
-      if (lane + 64 * i < D) tot[i] += f * sh_acc[g * S + k][lane + 64 * i];
+      if (lane + 64 * i < DW) tot[i] += f * sh_acc[gs * S + k][lane + 64 * i];
   }
   const float inv = wtot > 0.f ? 1.f / wtot : 0.f;
   float lse_nat = wtot > 0.f ? mu + log2_fast(wtot) * kLn2 : kNegInf;
   if (any_nan) lse_nat = __builtin_nanf("");
 #pragma unroll
   for (int i = 0; i < DL; ++i)
-    if (lane + 64 * i < D) store_out(og + lane + 64 * i, any_nan ? lse_nat : tot[i] * inv);
-  if (lane == 0) p.lse[(size_t)b * p.Hq + h] = lse_nat;
+    if (lane + 64 * i < DW) store_out(og + lane + 64 * i, any_nan ? lse_nat : tot[i] * inv);
+  if (lane == 0 && lse_writer) p.lse[(size_t)b * p.Hq + h] = lse_nat;
 }
 
 // One thread per (head, d); requests with a single split were finished above.
@@ -1073,11 +1080,16 @@ template <typename E, int D, int G>
 void launch_merge_gs(const DecodeParams& p, hipStream_t s) {
   // Segment-parallel merge (16 waves) when a pair is expected to span more
   // than 64 runs, i.e. fewer than one (request, head group) per 64 workgroups.
-  dim3 grid(p.Hkv, p.B);
-  if ((long)p.B * p.nhg * 64 < p.n_groups)
-    hipLaunchKernelGGL((decode_merge_kernel<E, D, G, 16 / G>), grid, dim3(1024), 0, s, p);
-  else
-    hipLaunchKernelGGL((decode_merge_kernel<E, D, G, 1>), grid, dim3(G * 64), 0, s, p);
+  // That case gives each query head and each 64 d of it a workgroup of 16
+  // waves, so a pair's hundreds of partial states are read by G * D / 64
+  // CUs, 16 segments or fewer per wave (one memory round trip).
+  if ((long)p.B * p.nhg * 64 < p.n_groups) {
+    constexpr int DS = D / 64 > 0 ? D / 64 : 1;
+    hipLaunchKernelGGL((decode_merge_kernel<E, D, G, 16, DS, 1>), dim3(p.Hkv, p.B, G * DS), dim3(1024),
+                       0, s, p);
+  } else {
+    hipLaunchKernelGGL((decode_merge_kernel<E, D, G, 1, 1, G>), dim3(p.Hkv, p.B), dim3(G * 64), 0, s, p);
+  }
 }
 
 template <typename E, int D>
