@@ -404,9 +404,9 @@ __global__ __launch_bounds__(NT, 1) void prefill256_kernel(PrefillParams p,
   // step kt - 1), agrees the running max and posts this wave's P(kt), computes
   // S^T(kt + 1) beside those exponentials and posts its maxima, accumulates
   // O^T over its own P(kt) and, after a barrier, over its partner's.  FAST:
-  // tiles kt and kt + 1 unmasked and needed by every row.  (Issue-order hints
-  // as in the head_dim 128 kernel measured 1.5 % slower here than the
-  // compiler's own order.)
+  // tiles kt and kt + 1 unmasked and needed by every row.  (No issue-order
+  // hints: those of the head_dim 128 kernel measured 1.5 % slower here, and
+  // hints for the K reads alone were within 1 % of the compiler's order.)
   int pid_v = 0, pid_k = 0;     // pages of V(kt + 1) and K(kt + 2) for the next DMA
   float mine = kNegInf;         // this wave's tile max of S^T(kt)
   auto step = [&](auto slot_tag, auto fast_tag, int kt, f32x16& scur, f32x16& snext) {
