@@ -153,3 +153,69 @@ def test_more_entry_points_replay_in_a_graph(gpu):
     assert_parity(c_out, c_lse, ro, rl, torch.bfloat16, "graph replay: cascade")
     ro, rl = oracle.merge_states([(m_a.cpu(), l_a.cpu()), (m_b.cpu(), l_b.cpu())])
     assert_parity(m_out, m_lse, ro, rl, torch.bfloat16, "graph replay: state merge")
+
+
+def test_head_dim_256_and_long_request_merge_replay_in_a_graph(gpu):
+    """head_dim 256: ragged prefill and paged-prefill cascade (pairs of waves
+    exchanging P through LDS), and a one-request decode whose merge splits
+    heads and d over workgroups, captured together; every replay equals the
+    eager run bit for bit and the oracle."""
+    import attention_qk_online_amd as A
+    pre = workloads.make_prefill(B=2, Hq=4, Hkv=2, D=256, lens_q=[300, 97], dtype=torch.bfloat16,
+                                 seed=505, causal=True)
+    pg = workloads.make_paged_prefill(B=2, Hq=4, Hkv=4, D=256, page_size=16, chunk=[70, 33],
+                                      cached=[160, 100], shared_prefix=64, dtype=torch.bfloat16, seed=506)
+    dec = workloads.make_decode(B=1, Hq=32, Hkv=8, D=128, page_size=16, kv_lens=[6000],
+                                dtype=torch.bfloat16, seed=507, extra_pages=2)
+    p_in = (pre.q.to(gpu), pre.k.to(gpu), pre.v.to(gpu), pre.cu_seqlens_q.to(gpu), pre.cu_seqlens_k.to(gpu))
+    kp, vp = pg.pools(gpu)
+    g_in = (pg.q.to(gpu), pg.cu_seqlens_q.to(gpu), kp, vp, pg.page_table.to(gpu), pg.kv_lens.to(gpu))
+    d_kp, d_vp = dec.pools(gpu)
+    d_in = (dec.q.to(gpu), d_kp, d_vp, dec.page_table.to(gpu), dec.kv_lens.to(gpu))
+    p_out, p_lse = torch.empty_like(p_in[0]), torch.empty(p_in[0].shape[:2], device=gpu)
+    c_out, c_lse = torch.empty_like(g_in[0]), torch.empty(g_in[0].shape[:2], device=gpu)
+    d_out, d_lse = torch.empty_like(d_in[0]), torch.empty(dec.B, dec.Hq, device=gpu)
+    ws_c = torch.empty(A.prefill_paged_cascade_workspace_size(torch.bfloat16, g_in[0].shape[0], pg.Hq,
+                                                              pg.D), dtype=torch.uint8, device=gpu)
+    ws_d = torch.empty(A.decode_paged_workspace_size(torch.bfloat16, dec.B, dec.Hq, dec.Hkv, dec.D, 16,
+                                                     dec.max_kv_len, 0), dtype=torch.uint8, device=gpu)
+
+    def run():
+        A.prefill_varlen(*p_in, pre.max_seqlen_q, pre.max_seqlen_k, causal=True, scale=pre.scale,
+                         out=p_out, lse=p_lse)
+        A.prefill_paged_cascade(*g_in, pg.max_seqlen_q, pg.max_kv_len, 64, causal=True,
+                                scale=pg.scale, out=c_out, lse=c_lse, workspace=ws_c)
+        A.decode_paged(*d_in, scale=dec.scale, max_kv_len=dec.max_kv_len, out=d_out, lse=d_lse,
+                       workspace=ws_d)
+
+    run()
+    torch.cuda.synchronize()
+    outs = (p_out, p_lse, c_out, c_lse, d_out, d_lse)
+    refs = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(4):
+        for t in outs:
+            t.fill_(float("nan"))
+        A.prefill_varlen(*p_in, pre.max_seqlen_q, pre.max_seqlen_k, causal=True, scale=pre.scale)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, ref in zip(outs, refs):
+            assert torch.equal(got, ref), f"replay {rep}"
+
+    ro, rl = oracle.ref_prefill_varlen(pre.q, pre.k, pre.v, pre.cu_seqlens_q, pre.cu_seqlens_k, True,
+                                       pre.scale)
+    assert_parity(p_out, p_lse, ro, rl, torch.bfloat16, "graph replay: head_dim 256 prefill")
+    ro, rl = oracle.ref_prefill_paged(pg.q, pg.cu_seqlens_q, pg.pool_k, pg.pool_v, pg.page_table,
+                                      pg.kv_lens, True, pg.scale)
+    assert_parity(c_out, c_lse, ro, rl, torch.bfloat16, "graph replay: head_dim 256 cascade")
+    kc, vc = dec.pools("cpu")
+    ro, rl = oracle.ref_decode_paged(dec.q, kc, vc, dec.page_table, dec.kv_lens, dec.scale)
+    assert_parity(d_out, d_lse, ro, rl, torch.bfloat16, "graph replay: one long decode request")
