@@ -392,3 +392,22 @@ def test_batch_above_65535_requests(gpu, dtype):
     ro, rl = oracle.ref_decode_paged(case.q, kp, vp, case.page_table, case.kv_lens, case.scale,
                                      requests=picks)
     assert_parity(out, lse, ro, rl, dtype, f"B {B}", rows=picks)
+
+
+@pytest.mark.parametrize("Hkv,G", [(3, 4), (5, 2), (12, 2), (16, 1), (32, 2)])
+@pytest.mark.parametrize("lens", [[1, 700, 33, 2048], [5000]])
+def test_more_than_eight_kv_heads(gpu, Hkv, G, lens):
+    """A workgroup folds up to eight KV heads of a unit; more heads form
+    several head groups per request (the last one partial when Hkv is not a
+    multiple of 8), and a single long request takes the merge that splits
+    heads and d over workgroups."""
+    import attention_qk_online_amd as A
+    case = workloads.make_decode(B=len(lens), Hq=G * Hkv, Hkv=Hkv, D=128, page_size=16, kv_lens=lens,
+                                 dtype=torch.bfloat16, seed=1900 + Hkv, extra_pages=2)
+    kp, vp = case.pools(gpu)
+    out, lse = A.decode_paged(case.q.to(gpu), kp, vp, case.page_table.to(gpu), case.kv_lens.to(gpu),
+                              scale=case.scale, max_kv_len=case.max_kv_len)
+    torch.cuda.synchronize()
+    kc, vc = case.pools()
+    ro, rl = oracle.ref_decode_paged(case.q, kc, vc, case.page_table, case.kv_lens, case.scale)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, f"Hkv {Hkv} G {G} lens {lens}")

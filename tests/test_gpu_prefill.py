@@ -547,3 +547,14 @@ def test_varlen_keys_past_4gib(gpu):
     ro, rl = oracle.ref_prefill_varlen(q1, k1, v1, torch.tensor([0, 200], dtype=torch.int32),
                                        torch.tensor([0, 333], dtype=torch.int32), True, scale)
     assert_parity(out[1:], lse[1:], ro, rl, torch.bfloat16, "sequence past 4 GiB")
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_more_than_eight_kv_heads(gpu, D):
+    """Twelve KV heads, two query heads each (the work order walks KV heads,
+    sequences, tiles and the heads of a group)."""
+    case = workloads.make_prefill(B=2, Hq=24, Hkv=12, D=D, lens_q=[150, 260], dtype=torch.bfloat16,
+                                  seed=260, causal=True)
+    out, lse = _varlen(case, gpu)
+    ro, rl = _ref(case)
+    assert_parity(out, lse, ro, rl, torch.bfloat16, f"Hkv 12 D{D}")
