@@ -376,22 +376,37 @@ __device__ __forceinline__ int pages_of(const DecodeParams& p, int b) {
 }
 
 __device__ __forceinline__ int wave_incl_scan(int x) {
+  // Within each row of 16 lanes: DPP row_shr 1, 2, 4, 8 (a lane whose source
+  // falls outside the row adds 0); then the totals of the rows before.
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);
   const int lane = __lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  return x;
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  return x + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
 }
 
-// Units (pages x KV-head groups) of the whole batch.
-__device__ __forceinline__ int total_units(const DecodeParams& p) {
+// Units (pages x KV-head groups) of the whole batch.  For the first 64
+// requests the lane's length (-1 for an inconsistent one) and the inclusive
+// scan of units stay in len0 / incl0, so the run that follows finds its
+// request without reading the lengths again.
+__device__ __forceinline__ int total_units(const DecodeParams& p, int& len0, int& incl0) {
   int tot = 0;
+  len0 = 0;
+  incl0 = 0;
   for (int c = 0; c < p.B; c += 64) {
     const int b = c + __lane_id();
-    const int u = b < p.B ? pages_of(p, b) * p.nhg : 0;
-    tot += __builtin_amdgcn_readlane(wave_incl_scan(u), 63);
+    bool bd = false;
+    const int ln = b < p.B ? request_len(p, b, bd) : 0;
+    const int u = b < p.B ? pages_from_len(p, ln) * p.nhg : 0;
+    const int incl = wave_incl_scan(u);
+    if (c == 0) {
+      len0 = bd ? -1 : ln;
+      incl0 = incl;
+    }
+    tot += __builtin_amdgcn_readlane(incl, 63);
   }
   return tot;
 }
@@ -431,7 +446,7 @@ __device__ __forceinline__ typename H::v8 fp8x8(uint32_t w0, uint32_t w1) {
 // adjacent in the NHD layout).
 template <typename E, int D, int G, int NB, bool F8, bool RP, bool LP>
 __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1, int W, int lane,
-                                           int wave) {
+                                           int wave, int len0, int incl0) {
   static_assert(!(RP && F8), "rotary embedding on the 16-bit cache only");
   using C = MfmaDecodeCfg<D>;
   constexpr int GROWB = F8 ? D : 2 * D;                  // bytes of one K/V row in the cache
@@ -442,16 +457,22 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
   using elem = typename H::elem;
   const int l16 = lane & 15, gq = lane >> 4;
   // Request holding unit u0 (scan of units per request, 64 requests at a
-  // time).  The lengths of the 64 requests from c_base on stay one per lane
-  // (lenv, -1 for an inconsistent one), so later pieces read them without a
-  // memory round trip.
+  // time; the first 64 come from total_units).  The lengths of the 64
+  // requests from c_base on stay one per lane (lenv, -1 for an inconsistent
+  // one), so later pieces read them without a memory round trip.
   int b = 0, start_b = 0, c_base = 0, lenv = 0;
   for (int c = 0, cum = 0; c < p.B; c += 64) {
     const int bb = c + lane;
     bool bd = false;
-    const int ln = bb < p.B ? request_len(p, bb, bd) : 0;
+    int ln;
+    if (c == 0) {
+      bd = len0 < 0;
+      ln = bd ? 0 : len0;
+    } else {
+      ln = bb < p.B ? request_len(p, bb, bd) : 0;
+    }
     const int u = bb < p.B ? pages_from_len(p, ln) * p.nhg : 0;
-    const int incl = wave_incl_scan(u);
+    const int incl = c == 0 ? incl0 : wave_incl_scan(u);
     const int tot = __builtin_amdgcn_readlane(incl, 63);
     if (cum + tot > u0) {
       const uint64_t hit = __builtin_amdgcn_ballot_w64(cum + incl > u0);
@@ -728,7 +749,7 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
           s[rr] = v;
           mx = fmaxf(mx, v);
         }
-        mx = max_halves(fmaxf(mx, shfl_xor_f32(mx, 16)));
+        mx = max_halves(max_rows16(mx));
         const float mn = fmaxf(m, mx);
         const float mu = mn == kNegInf ? 0.f : mn;
         const float alpha = exp2_fast(m - mu);
@@ -789,7 +810,7 @@ __device__ __forceinline__ void decode_run(const DecodeParams& p, int u0, int u1
     }
 
     // Finish the piece: lane (head l16, group gq) holds d = 16 db + 4 gq + rr.
-    const float ltot = sum_halves(lsum + shfl_xor_f32(lsum, 16));
+    const float ltot = sum_halves(sum_rows16(lsum));
     float inv = ltot > 0.f ? (F8 ? p.v_scale : 1.f) / ltot : 0.f;
     float lse_nat = ltot > 0.f ? (m + log2_fast(ltot)) * kLn2 : kNegInf;
     if (bad) { inv = qnan; lse_nat = qnan; }
@@ -828,10 +849,11 @@ __global__ __launch_bounds__(kMaxGroupWaves * 64, D == 256 ? 1 : 2) void decode_
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  const int U = total_units(p);
+  int len0, incl0;
+  const int U = total_units(p, len0, incl0);
   const int W = run_length(p, U);
   for (int run = blockIdx.x; (long)run * W < U; run += gridDim.x) {
-    decode_run<E, D, G, NB, F8, RP, LP>(p, run * W, min(run * W + W, U), W, lane, wave);
+    decode_run<E, D, G, NB, F8, RP, LP>(p, run * W, min(run * W + W, U), W, lane, wave, len0, incl0);
   }
 }
 
@@ -854,6 +876,40 @@ __global__ __launch_bounds__(HPW * S * 64) void decode_merge_kernel(DecodeParams
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = HPW == G ? wv / S : (int)blockIdx.z / DS, sl = wv % S;
   const bool lse_writer = blockIdx.z % DS == 0;
+  const int h = kvh * G + g;
+  const size_t slot0 = ((size_t)b * p.Hkv + kvh) * p.max_segs;
+  const float* pl = p.part_lse + slot0 * G + g;           // stride G between segments
+  const float* po = p.part_o + (slot0 * G + g) * D + d0;  // stride G*D between segments
+  // This wave takes segments sl, sl + S, sl + 2S, ... (local segment js is
+  // segment sl + S js).  Chunks of 64 local segments: lane j holds local
+  // segment j0 + j's lse and weight, and the partial outputs are read MB
+  // local segments at a time.  With S waves per head (a pair spanning many
+  // runs) the first chunk's lse values and first batch of partial outputs
+  // are requested before the segment count is known: every slot below
+  // max_segs exists in the workspace, and values past the count are never
+  // used (selected away, not multiplied by 0), so the lengths and the
+  // partial states arrive in the same memory round trip (single request of
+  // 32768 keys: merge 6.1 -> 5.5 us).  With one wave per head the pairs
+  // span a few runs and most slots past the count were never written: the
+  // same early loads made the merge slower there (5.3 -> 5.9 us, 64
+  // requests), so that path loads after the count.
+  constexpr int MB = D > 128 ? 16 : 32;
+  constexpr int SPEC = S > 1 ? MB : 0;
+  const int n_slot = p.max_segs > sl ? (p.max_segs - sl + S - 1) / S : 0;
+  float v[MB][DL];
+  auto load_o = [&](int js, int lim) {
+#pragma unroll
+    for (int t = 0; t < MB; ++t)
+#pragma unroll
+      for (int i = 0; i < DL; ++i)
+        v[t][i] = (js + t < lim && lane + 64 * i < DW) ? po[(size_t)(sl + S * (js + t)) * G * D + lane + 64 * i] : 0.f;
+  };
+  float ls_first = kNegInf;
+  if constexpr (SPEC > 0) {
+    ls_first = lane < n_slot ? pl[(size_t)(sl + S * lane) * G] : kNegInf;
+    load_o(0, min(SPEC, n_slot));
+  }
+
   int U = 0, pre = 0;
   for (int c = 0; c < p.B; c += 64) {
     const int bb = c + lane;
@@ -868,7 +924,6 @@ __global__ __launch_bounds__(HPW * S * 64) void decode_merge_kernel(DecodeParams
   const int start_pair = pre + (kvh / p.hw) * np;
   const int nseg = np > 0 ? (start_pair + np - 1) / W - start_pair / W + 1 : 0;
   if (nseg == 1) return;                 // the same for every wave of the workgroup
-  const int h = kvh * G + g;
   E* og = reinterpret_cast<E*>(p.out) + ((size_t)b * p.Hq + h) * D + d0;
   if (bad || nseg == 0) {
     if (sl == 0) {
@@ -878,55 +933,32 @@ __global__ __launch_bounds__(HPW * S * 64) void decode_merge_kernel(DecodeParams
     }
     return;
   }
-  const size_t slot0 = ((size_t)b * p.Hkv + kvh) * p.max_segs;
-  const float* pl = p.part_lse + slot0 * G + g;           // stride G between segments
-  const float* po = p.part_o + (slot0 * G + g) * D + d0;  // stride G*D between segments
-  // This wave's slice of the segments.
-  const int per = (nseg + S - 1) / S;
-  const int s0 = min(nseg, sl * per), s1 = min(nseg, s0 + per);
+  const int n_loc = nseg > sl ? (nseg - sl + S - 1) / S : 0;   // local segments of this wave
   float acc[DL] = {};
   float mx = kNegInf, ws = 0.f;
   bool nan_seen = false;
-  // Segments in chunks of 64: lane j holds segment j's lse and weight, then
-  // the partial outputs are read MB segments at a time (one memory round
-  // trip per batch).
-  constexpr int MB = D > 128 ? 16 : 32;
-  for (int j0 = s0; j0 < s1; j0 += 64) {
-    const int nj = min(64, s1 - j0);
-    const float ls = lane < nj ? pl[(size_t)(j0 + lane) * G] : kNegInf;
-    // Partial outputs of segments j0 + j .. j0 + j + MB - 1; the first batch
-    // is requested together with the lse values (one memory round trip less).
-    float v[MB][DL];
-    auto load_o = [&](int j) {
-#pragma unroll
-      for (int t = 0; t < MB; ++t)
-#pragma unroll
-        for (int i = 0; i < DL; ++i)
-          v[t][i] = (j + t < nj && lane + 64 * i < DW) ? po[(size_t)(j0 + j + t) * G * D + lane + 64 * i] : 0.f;
-    };
-    load_o(0);
+  for (int j0 = 0; j0 < n_loc; j0 += 64) {
+    const int nj = min(64, n_loc - j0);
+    const bool early = SPEC > 0 && j0 == 0;       // lse and first batch requested above
+    float ls = ls_first;
+    if (!early) ls = lane < nj ? pl[(size_t)(sl + S * (j0 + lane)) * G] : kNegInf;
+    ls = lane < nj ? ls : kNegInf;
     nan_seen |= __builtin_amdgcn_ballot_w64(ls != ls) != 0;
-    float cm = ls;
-#pragma unroll
-    for (int sh = 32; sh >= 1; sh >>= 1) cm = fmaxf(cm, shfl_xor_f32(cm, sh));
-    const float mnew = fmaxf(mx, cm);
+    const float mnew = fmaxf(mx, wave_max(ls));
     const float mu = mnew == kNegInf ? 0.f : mnew;
     const float resc = exp2_fast((mx - mu) * kLog2e);
-    float w = lane < nj ? exp2_fast((ls - mu) * kLog2e) : 0.f;
-    float wsum = w;
-#pragma unroll
-    for (int sh = 32; sh >= 1; sh >>= 1) wsum += shfl_xor_f32(wsum, sh);
-    ws = ws * resc + wsum;
+    const float w = lane < nj ? exp2_fast((ls - mu) * kLog2e) : 0.f;
+    ws = ws * resc + wave_sum(w);
 #pragma unroll
     for (int i = 0; i < DL; ++i) acc[i] *= resc;
     mx = mnew;
     for (int j = 0; j < nj; j += MB) {
-      if (j > 0) load_o(j);
+      if (!early || j > 0) load_o(j0 + j, n_loc);
 #pragma unroll
       for (int t = 0; t < MB; ++t) {
         const float wt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), min(j + t, 63)));
 #pragma unroll
-        for (int i = 0; i < DL; ++i) acc[i] += (j + t < nj ? wt : 0.f) * v[t][i];
+        for (int i = 0; i < DL; ++i) acc[i] += j + t < nj ? wt * v[t][i] : 0.f;
       }
     }
   }
