@@ -159,6 +159,13 @@ __device__ __forceinline__ float sum_rows16(float x) {
   return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
 }
 
+// Value of lane ^ 16.
+__device__ __forceinline__ float swap_rows16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                            false, false);
+  return __builtin_bit_cast(float, (int)((__lane_id() & 16) ? r[0] : r[1]));
+}
+
 // Maximum / sum over the 64 lanes, in every lane: DPP within rows of 16, then
 // the two lane-swap steps above (no LDS round trip).
 __device__ __forceinline__ float wave_max(float x) {
@@ -169,11 +176,5 @@ __device__ __forceinline__ float wave_max(float x) {
   return max_halves(max_rows16(x));
 }
 __device__ __forceinline__ float wave_sum(float x) { return sum_halves(sum_rows16(row16_sum(x))); }
-
-__device__ __forceinline__ float shfl_xor_f32(float x, int mask) {
-  int lane = __lane_id();
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2,
-                                                                __builtin_bit_cast(int, x)));
-}
 
 }  // namespace attn

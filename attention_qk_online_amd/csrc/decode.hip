@@ -243,19 +243,21 @@ __global__ __launch_bounds__(kNW * 64) void decode_split_kernel(DecodeParams p) 
       if (j == 0 || i + j < n_w) compute(i + j, bufs[j]);
   }
 
-  // Merge the four 16-lane groups of the wave (lane ^ 16, then lane ^ 32).
+  // Merge the four 16-lane groups of the wave (lane ^ 16, then lane ^ 32,
+  // by lane-swap instructions rather than LDS permutes).
+  auto partner = [](float x, int mask) { return mask == 16 ? swap_rows16(x) : swap_halves(x); };
 #pragma unroll
   for (int mask = 16; mask <= 32; mask <<= 1) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float mo = shfl_xor_f32(m[g], mask);
-      float lo = shfl_xor_f32(l[g], mask);
+      float mo = partner(m[g], mask);
+      float lo = partner(l[g], mask);
       float mn = fmaxf(m[g], mo);
       float mu = mn == kNegInf ? 0.f : mn;
       float a = exp2_fast(m[g] - mu), ao = exp2_fast(mo - mu);
       l[g] = l[g] * a + lo * ao;
 #pragma unroll
-      for (int e = 0; e < VPL; ++e) o[g][e] = o[g][e] * a + shfl_xor_f32(o[g][e], mask) * ao;
+      for (int e = 0; e < VPL; ++e) o[g][e] = o[g][e] * a + partner(o[g][e], mask) * ao;
       m[g] = mn;
     }
   }
