@@ -222,6 +222,30 @@ def test_few_long_requests(gpu, dtype, D, Hq, Hkv):
         assert_parity(out, lse, ro, rl, dtype, f"{dtype} D{D} Hq{Hq} Hkv{Hkv} lens {lens}")
 
 
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (256, 16, 2), (64, 8, 8)])
+def test_many_segment_merge_chunks_and_idle_waves(gpu, D, Hq, Hkv):
+    """The 16-wave merge with one-page runs: the long request leaves ~1250
+    partial states per head, so each wave folds two chunks of 64; the short
+    one leaves 3, so 13 of the 16 waves hold none.  The workspace starts as
+    NaN bit patterns (the merge reads its first slots before it knows the
+    segment count): the result equals a fresh-workspace call bit for bit and
+    matches the oracle; the empty request gets out 0 and lse -inf."""
+    import attention_qk_online_amd as A
+    case = workloads.make_decode(B=3, Hq=Hq, Hkv=Hkv, D=D, page_size=16, kv_lens=[20000, 40, 0],
+                                 dtype=torch.bfloat16, seed=960 + D, extra_pages=2)
+    kp, vp = case.pools(gpu)
+    args = (case.q.to(gpu), kp, vp, case.page_table.to(gpu), case.kv_lens.to(gpu))
+    kw = dict(scale=case.scale, max_kv_len=case.max_kv_len, split_pages=1)
+    need = A.decode_paged_workspace_size(torch.bfloat16, case.B, Hq, Hkv, D, 16, case.max_kv_len, 1)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=gpu)
+    out, lse = A.decode_paged(*args, workspace=ws, **kw)
+    o_ref, l_ref = A.decode_paged(*args, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o_ref) and torch.equal(lse, l_ref)
+    ro, rl = _oracle(case)
+    assert_parity(out.cpu(), lse.cpu(), ro, rl, torch.bfloat16, f"D{D} Hq{Hq} Hkv{Hkv} split_pages 1")
+
+
 def test_few_long_requests_bad_page(gpu):
     """A bad page id in one of two long requests poisons only that request."""
     import attention_qk_online_amd as A
