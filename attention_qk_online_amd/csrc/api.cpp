@@ -142,7 +142,9 @@ DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int D, int page_size, 
     const size_t slots = mul_sat(1, {B, Hkv, pl.max_segs, Hq / (Hkv > 0 ? Hkv : 1)});
     pl.part_o_elems = mul_sat(slots, {D});
     pl.part_lse_elems = slots;
-    pl.bytes = add_sat(aligned_bytes(pl.part_o_elems), aligned_bytes(pl.part_lse_elems));
+    // + the first unit of each request and the total (B + 1 int32)
+    pl.bytes = add_sat(add_sat(aligned_bytes(pl.part_o_elems), aligned_bytes(pl.part_lse_elems)),
+                       aligned_bytes((size_t)B + 1));
     return pl;
   }
   pl.split_pages = split_pages > 0 ? split_pages : auto_split_pages(B, Hkv, max_pages);
@@ -311,6 +313,9 @@ static attn_status decode_impl(attn_dtype dtype, bool fp8_kv, int kv_hnd, int wi
     p.part_o = reinterpret_cast<float*>(workspace);
     const size_t o_bytes = aligned_bytes(pl.part_o_elems);
     p.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + o_bytes);
+    if (dtype != ATTN_F32)
+      p.unit_start = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + o_bytes +
+                                                aligned_bytes(pl.part_lse_elems));
   }
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.num_pages = num_pages; p.max_pages = max_pages_per_req;
   p.max_kv_len = max_kv_len; p.split_pages = pl.split_pages; p.n_splits = pl.n_splits;

@@ -393,8 +393,11 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // Units (pages x KV-head groups) of the whole batch.  For the first 64
 // requests the lane's length (-1 for an inconsistent one) and the inclusive
 // scan of units stay in len0 / incl0, so the run that follows finds its
-// request without reading the lengths again.
-__device__ __forceinline__ int total_units(const DecodeParams& p, int& len0, int& incl0) {
+// request without reading the lengths again.  With `publish` (one wave of
+// the grid) the first unit of every request and the total go to
+// p.unit_start for the merge kernel.
+__device__ __forceinline__ int total_units(const DecodeParams& p, int& len0, int& incl0,
+                                           bool publish) {
   int tot = 0;
   len0 = 0;
   incl0 = 0;
@@ -408,8 +411,10 @@ __device__ __forceinline__ int total_units(const DecodeParams& p, int& len0, int
       len0 = bd ? -1 : ln;
       incl0 = incl;
     }
+    if (publish && b < p.B) p.unit_start[b] = tot + incl - u;
     tot += __builtin_amdgcn_readlane(incl, 63);
   }
+  if (publish && __lane_id() == 0) p.unit_start[p.B] = tot;
   return tot;
 }
 
@@ -852,7 +857,7 @@ __global__ __launch_bounds__(kMaxGroupWaves * 64, D == 256 ? 1 : 2) void decode_
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   int len0, incl0;
-  const int U = total_units(p, len0, incl0);
+  const int U = total_units(p, len0, incl0, blockIdx.x == 0 && wave == 0);
   const int W = run_length(p, U);
   for (int run = blockIdx.x; (long)run * W < U; run += gridDim.x) {
     decode_run<E, D, G, NB, F8, RP, LP>(p, run * W, min(run * W + W, U), W, lane, wave, len0, incl0);
@@ -912,13 +917,9 @@ __global__ __launch_bounds__(HPW * S * 64) void decode_merge_kernel(DecodeParams
     load_o(0, min(SPEC, n_slot));
   }
 
-  int U = 0, pre = 0;
-  for (int c = 0; c < p.B; c += 64) {
-    const int bb = c + lane;
-    const int u = bb < p.B ? pages_of(p, bb) * p.nhg : 0;
-    U += __builtin_amdgcn_readlane(wave_incl_scan(u), 63);
-    pre += __builtin_amdgcn_readlane(wave_incl_scan(bb < b ? u : 0), 63);
-  }
+  // The batch's unit count and request b's first unit, as the main kernel
+  // counted them (no scan of the lengths here).
+  const int U = p.unit_start[p.B], pre = p.unit_start[b];
   const int W = run_length(p, U);
   bool bad;
   request_len(p, b, bad);

@@ -18,6 +18,10 @@ struct DecodeParams {
   float* lse;              // [B, Hq]
   float* part_o;           // workspace: partial outputs (layout per kernel below)
   float* part_lse;         // workspace: partial log-sum-exp
+  // workspace (bf16 balanced schedule): [B + 1] first unit of each request
+  // in the batch's unit order, then the total; written by workgroup 0 of the
+  // main kernel, read by the merge kernel.
+  int32_t* unit_start;
   int B, Hq, Hkv, num_pages, max_pages, max_kv_len, split_pages;
   // Pages hold 16 << page_shift tokens (16-bit path; the fp32 path takes 16
   // only).  The kernels work in 16-token blocks: block k of a request is

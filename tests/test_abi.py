@@ -139,10 +139,11 @@ def test_workspace_size(lib):
     n = lib.attn_decode_paged_workspace_size(0, 4, 8, 2, 128, 16, 160, 2)   # 10 pages -> 5 splits
     o, lse = 4 * 5 * 8 * 128 * 4, 4 * 5 * 8 * 4
     assert n == ((o + 255) // 256 + (lse + 255) // 256) * 256
-    # bf16 balanced runs: B*Hkv*max_segs*G*(D+1) floats, max_segs = ceil(max_pages/run)+1
+    # bf16 balanced runs: B*Hkv*max_segs*G*(D+1) floats, max_segs = ceil(max_pages/run)+1,
+    # and B+1 int32 (each request's first unit and the total)
     def bf16_bytes(B, Hkv, segs, G, D):
         slots = B * Hkv * segs * G
-        return ((slots * D * 4 + 255) // 256 + (slots * 4 + 255) // 256) * 256
+        return ((slots * D * 4 + 255) // 256 + (slots * 4 + 255) // 256 + ((B + 1) * 4 + 255) // 256) * 256
     n = lib.attn_decode_paged_workspace_size(1, 4, 8, 2, 128, 16, 160, 2)   # run 2 -> 6 segs
     assert n == bf16_bytes(4, 2, 6, 4, 128)
     n = lib.attn_decode_paged_workspace_size(1, 4, 8, 2, 128, 16, 160, 0)   # run >= 8 -> 3 segs

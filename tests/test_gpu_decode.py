@@ -186,6 +186,35 @@ def test_many_requests(gpu, dtype):
         assert_parity(out, lse, ro, rl, dtype, f"B150 {dtype} split{split}")
 
 
+def test_more_than_512_requests(gpu):
+    """700 requests: the schedule reads the lengths 512 at a time (two
+    batches of eight 64-request chunks), in the unit count, the run's
+    request search and the merge; an inconsistent length in the second
+    batch poisons only its own request."""
+    import attention_qk_online_amd as A
+    g = torch.Generator().manual_seed(430)
+    lens = torch.randint(0, 200, (700,), generator=g).tolist()
+    lens[3] = 0
+    lens[511] = 1
+    lens[512] = 199
+    case = workloads.make_decode(B=700, Hq=8, Hkv=2, D=128, page_size=16, kv_lens=lens,
+                                 dtype=torch.bfloat16, seed=431, extra_pages=4)
+    ro, rl = _oracle(case)
+    kp, vp = case.pools(gpu)
+    for split in (0, 2):
+        out, lse = _run(case, gpu, split, pools=(kp, vp))
+        assert_parity(out, lse, ro, rl, torch.bfloat16, f"B700 split{split}")
+    kv = case.kv_lens.clone()
+    kv[600] = case.max_kv_len + 1
+    out, lse = A.decode_paged(case.q.to(gpu), kp, vp, case.page_table.to(gpu), kv.to(gpu),
+                              scale=case.scale, max_kv_len=case.max_kv_len)
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu()
+    assert torch.isnan(out[600].float()).all() and torch.isnan(lse[600]).all()
+    keep = torch.arange(700) != 600
+    assert_parity(out[keep], lse[keep], ro[keep], rl[keep], torch.bfloat16, "B700, request 600 bad")
+
+
 @pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 8, 8), (256, 16, 2)])
 @pytest.mark.parametrize("split_pages", [0, 2])
 def test_small_paged_fp16(gpu, D, Hq, Hkv, split_pages):
