@@ -215,6 +215,20 @@ def test_more_than_512_requests(gpu):
     assert_parity(out[keep], lse[keep], ro[keep], rl[keep], torch.bfloat16, "B700, request 600 bad")
 
 
+def test_more_than_4096_requests(gpu):
+    """4200 short requests: the unit count hands the run's request search the
+    count at the end of each of the first 64 chunks of 64 requests; runs
+    starting past them search on from chunk 64."""
+    g = torch.Generator().manual_seed(440)
+    lens = torch.randint(0, 48, (4200,), generator=g).tolist()
+    case = workloads.make_decode(B=4200, Hq=4, Hkv=2, D=64, page_size=16, kv_lens=lens,
+                                 dtype=torch.bfloat16, seed=441, extra_pages=2)
+    ro, rl = _oracle(case)
+    for split in (0, 1):
+        out, lse = _run(case, gpu, split)
+        assert_parity(out, lse, ro, rl, torch.bfloat16, f"B4200 split{split}")
+
+
 @pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 8, 8), (256, 16, 2)])
 @pytest.mark.parametrize("split_pages", [0, 2])
 def test_small_paged_fp16(gpu, D, Hq, Hkv, split_pages):
