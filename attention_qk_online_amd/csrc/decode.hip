@@ -865,9 +865,11 @@ __global__ __launch_bounds__(kMaxGroupWaves * 64, D == 256 ? 1 : 2) void decode_
 }
 
 // Merge of the balanced runs: one workgroup per (KV head, request) with S
-// waves per query head of the group, each folding a slice of the pair's
-// segments; with S > 1 (a batch of a few long requests, each split over
-// hundreds of runs) the S partial states of a head are combined through LDS.
+// waves per query head of the group, wave sl folding the pair's segments
+// sl, sl + S, ...; with S > 1 (a batch of a few long requests, each split
+// over hundreds of runs) the S partial states of a head are combined
+// through LDS.  The request's first unit and the batch's unit count come
+// from unit_start, written by the main kernel.
 // Lanes own d.  Pairs held by a single run were written by that run; empty
 // requests get out 0 and lse -inf and inconsistent ones NaN.
 // HPW query heads per workgroup: G (S waves each), or 1, the head then
