@@ -167,7 +167,7 @@ __device__ __forceinline__ float swap_rows16(float x) {
 }
 
 // Maximum / sum over the 64 lanes, in every lane: DPP within rows of 16, then
-// the two lane-swap steps above (no LDS round trip).
+// the two lane-swap steps above (no LDS round trip).  All 64 lanes active.
 __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp_f32<0xB1>(x));
   x = fmaxf(x, dpp_f32<0x4E>(x));

@@ -380,6 +380,7 @@ __device__ __forceinline__ int pages_of(const DecodeParams& p, int b) {
 __device__ __forceinline__ int wave_incl_scan(int x) {
   // Within each row of 16 lanes: DPP row_shr 1, 2, 4, 8 (a lane whose source
   // falls outside the row adds 0); then the totals of the rows before.
+  // Called with all 64 lanes active (DPP reads inactive lanes' stale values).
   x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);
   x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);
   x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
